@@ -1,0 +1,27 @@
+"""fp64 CPU oracle of the selected-token logprob drift contract.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import, call or execute this
+package: only the tests, the smoke check of the entry module and the CPU-baseline leg of
+the benchmark use it. It shares no code, tables or helpers with the HIP library.
+
+It is a plain, slow, textbook implementation in float64 numpy / Python:
+
+* ``logprob``     - active-row rule, logical-input validation, two-pass log-sum-exp,
+                    selected-logit gather and dlogp (page "WS2 Cross-Config Logprob Drift
+                    Contract", section "Measurement Contract"; page "[WS2] Framework for
+                    ablation experiment", LogProb knobs rows 2, 6, 8).
+* ``diagnostics`` - ratio0, clipfrac0, approx_kl0 and mean/p95/p99/max |dlogp| (page "WS2
+                    Cross-Config Logprob Drift Contract", section "Diagnostics" table).
+* ``lmhead``      - hidden x W_vocab followed by the same log-softmax gather (page "[WS2]
+                    Framework for ablation experiment", LogProb knobs rows 9 and 10).
+
+Each function is pinned by tests against closed forms, brute force at 50 decimal digits
+and textbook library routines; none is "parity unpinned".
+"""
+from .logprob import (STATUS, widen, logsumexp_row, selected_logprob, validate_inputs,
+                      active_rows, score_row, score_rows)
+from .diagnostics import diagnostics, nearest_rank
+from .lmhead import lmhead_logprob
+
+__all__ = ["STATUS", "widen", "logsumexp_row", "selected_logprob", "validate_inputs",
+           "active_rows", "score_row", "score_rows", "diagnostics", "nearest_rank", "lmhead_logprob"]

@@ -1,0 +1,55 @@
+"""The oracle's pins catch plausible mistakes: each case plants one mistake in a copy of
+the oracle (on the CPU) and checks that the pin tests then fail."""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PIN_TESTS = ["tests/test_oracle_logprob.py", "tests/test_oracle_diagnostics.py",
+             "tests/test_oracle_lmhead.py"]
+
+MUTATIONS = [
+    ("logprob.py", "lpt = xt - lt", "lpt = lt - xt"),                          # sign
+    ("logprob.py", "return m + math.log(", "return math.log("),                 # dropped term
+    ("logprob.py", "xt = float(train_row[y])", "xt = float(train_row[y - 1])"),  # index
+    ("logprob.py", "lpt - lpr, bool(bad)", "lpr - lpt, bool(bad)"),             # drift sign
+    ("logprob.py", "<< np.uint32(16)", "<< np.uint32(15)"),                      # widening
+    ("logprob.py", "return att & act", "return att | act"),                      # active rule
+    ("logprob.py", 'layout == "right" and (not a2[b, t]) and a2[b, t + 1]',
+     'layout == "right" and a2[b, t] and (not a2[b, t + 1])'),                   # padding side
+    ("logprob.py", "(ids < 0) | (ids >= V)", "(ids < 0) | (ids > V)"),           # OOV bound
+    ("diagnostics.py", "k = (q_num * n + q_den - 1) // q_den", "k = (q_num * n) // q_den"),
+    ("diagnostics.py", "a[nearest_rank(n, 99, 100) - 1]", "a[nearest_rank(n, 95, 100) - 1]"),
+    ("diagnostics.py", "lo_edge = 1.0 - eps_low", "lo_edge = 1.0 - eps_high"),
+    ("diagnostics.py", "math.expm1(v) - v for v", "math.expm1(v) + v for v"),
+    ("diagnostics.py", "math.fsum(abs(v) for v in vals) / n", "math.fsum(vals) / n"),
+    ("diagnostics.py", "math.fsum(math.exp(v) for v in vals) / n",
+     "math.fsum(math.exp(v) for v in vals) / (n + 1)"),
+    ("diagnostics.py", 'out["argmax_row"] = int(r)\n            break',
+     'out["argmax_row"] = int(r)'),                                              # last tie
+    ("lmhead.py", "z[i, int(ids[r])]", "z[i, int(ids[i])]"),
+    ("lmhead.py", "z = h @ weight_f64", "z = (h[:, ::-1] @ weight_f64)"),        # reversed K
+]
+
+
+@pytest.mark.parametrize("fname,old,new", MUTATIONS, ids=[f"{m[0]}:{i}" for i, m in enumerate(MUTATIONS)])
+def test_pins_catch_planted_mistake(tmp_path, fname, old, new):
+    dst = tmp_path / "oracle"
+    shutil.copytree(os.path.join(ROOT, "oracle"), dst,
+                    ignore=shutil.ignore_patterns("__pycache__"))
+    path = dst / fname
+    src = path.read_text()
+    assert src.count(old) == 1, f"mutation anchor not found once: {old!r}"
+    path.write_text(src.replace(old, new))
+    for t in PIN_TESTS:
+        shutil.copy(os.path.join(ROOT, t), tmp_path / os.path.basename(t))
+    shutil.copytree(os.path.join(ROOT, "tests", "golden"), tmp_path / "golden")
+    env = dict(os.environ, PYTHONPATH=f"{tmp_path}{os.pathsep}{ROOT}")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        "--rootdir", str(tmp_path)] +
+                       [str(tmp_path / os.path.basename(t)) for t in PIN_TESTS],
+                       cwd=str(tmp_path), env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"planted mistake survived the pins: {new!r}\n{r.stdout[-2000:]}"
