@@ -1,0 +1,160 @@
+"""Throughput of the paired selected-token logprob + drift path on one MI355X.
+
+One step = drift_selected_logprob (classification, compaction, paired one-pass log-softmax
+gather) + drift_diagnostics (sums, counts, exact nearest-rank select, one host sync) over
+one batch of the Qwen3-8B-shaped scoring workload: bf16 logits, V=151936, B=8, L=2048,
+left padding, 12288 active rows, inputs resident in HBM before timing starts.
+
+Prints ONE JSON line (rank 0). `roofline` is for the dominant kernel (the paired scoring
+kernel): algorithmic bytes = active rows x V x 2 bytes x 2 sides, divided by its average
+duration measured with HIP events recorded by the library around that kernel on the launch
+stream. `cpu_baseline` is the fp64 CPU oracle timed on a bounded sample of the same rows.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "active tokens/sec + logits HBM GB/s (% of peak) for paired logprob+drift"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(case, budget_s):
+    """fp64 oracle on a bounded sample of the workload's active rows (single process)."""
+    import numpy as np
+
+    import oracle
+    from train_rollout_logprob_amd import synth
+
+    att = case.attention if case.attention is not None else np.ones(case.N, np.uint8)
+    rows = np.nonzero((att != 0) & (case.action != 0))[0]
+    done, spent, chunk = 0, 0.0, 16
+    while spent < budget_s and done < len(rows):
+        sel = rows[done: done + chunk]
+        tr = synth.rows_to_host(case.train, sel)
+        ro = synth.rows_to_host(case.rollout, sel)
+        t0 = time.perf_counter()
+        oracle.score_rows(tr, ro, case.dtype, case.ids[sel])
+        spent += time.perf_counter() - t0
+        done += len(sel)
+    return {"value": done / spent, "unit": "active tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} active rows of the same batch (both sides, V={case.V}), "
+                      f"numpy fp64 two-pass log-sum-exp, one process, {spent:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build has "
+              f"no multi-GPU path; the per-row work shards by rows with no exchange.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from train_rollout_logprob_amd import binding as B
+    from train_rollout_logprob_amd import synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    log("[bench] generating the qwen8b-shaped workload")
+    case = synth.make_logits_case("qwen8b", device=dev)
+    ids = torch.as_tensor(case.ids, device=dev)
+    att = torch.as_tensor(case.attention, device=dev)
+    act = torch.as_tensor(case.action, device=dev)
+    N, V = case.N, case.V
+    n_active = case.n_active()
+    ws = B.workspace(B.DRIFT_OP_SELECTED_LOGPROB, N, V, B.DRIFT_BF16, dev)
+    dws = B.workspace(B.DRIFT_OP_DIAGNOSTICS, N, 1, B.DRIFT_F32, dev)
+    outs = tuple(torch.empty(N, dtype=dt, device=dev)
+                 for dt in (torch.float32, torch.float32, torch.float32, torch.uint8))
+    stream = torch.cuda.current_stream()
+    n_ev = args.warmup + args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_ev)]
+    for e0, e1 in evs:          # create the underlying events
+        e0.record()
+        e1.record()
+    torch.cuda.synchronize()
+
+    def step(i):
+        B.selected_logprob(case.train, case.rollout, ids, att, act, "left", case.B, case.L,
+                           ws=ws, out=outs, stream=stream,
+                           events=(evs[i][0].cuda_event, evs[i][1].cuda_event))
+        st, s = B.diagnostics(outs[2], outs[3], case.eps_low, case.eps_high, logprob_ws=ws,
+                              ws=dws, stream=stream)
+        if st != B.DRIFT_OK:
+            raise RuntimeError(f"status {B.STATUS_NAMES[st]}")
+        return s
+
+    log("[bench] warmup")
+    for i in range(args.warmup):
+        stats = step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.warmup, n_ev):
+        stats = step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern_ms = [evs[i][0].elapsed_time(evs[i][1]) for i in range(args.warmup, n_ev)]
+    kern_avg = sum(kern_ms) / len(kern_ms)
+    assert stats["n_active"] == n_active, (stats["n_active"], n_active)
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = n_active * args.steps / elapsed
+    alg_bytes = n_active * V * 2 * 2
+    achieved = alg_bytes / (kern_avg * 1e-3) / 1e9
+    log(f"[bench] step {ms_per_step:.3f} ms, scoring kernel {kern_avg:.3f} ms "
+        f"({achieved:.0f} GB/s), {value / 1e6:.3f} M active tok/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        cpu = cpu_baseline(case, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "active tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "qwen8b-shaped paired scoring: bf16 logits, V=151936, B=8, "
+                               "L=2048 (prompt 512 + response 1536), left padding",
+                   "V": V, "B": case.B, "L": case.L, "n_active": n_active,
+                   "logits_dtype": "bf16", "arith": "fp32 exp2, fp64 sums",
+                   "parallelism": "single GPU"},
+        "logits_gbs": alg_bytes * args.steps / elapsed / 1e9,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "score_rows<bf16>", "kernel_ms": kern_avg,
+                     "bytes_per_launch": alg_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

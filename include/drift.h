@@ -1,0 +1,226 @@
+/*
+ * drift.h - C ABI of the MI355X (gfx950) selected-token logprob drift library.
+ *
+ * What is computed (the pages' measurement contract):
+ *   For every active row r of a teacher-forced batch, the selected-token log-probability
+ *   of both sides, logp = x[y_r] - log(sum_i exp(x_i)), and the drift
+ *   dlogp = train_recomputed_logp - rollout_old_logp
+ *   ("WS2 Cross-Config Logprob Drift Contract", section "Measurement Contract"), then the
+ *   diagnostics ratio0, clipfrac0, approx_kl0 and mean/p95/p99/max |dlogp| over the
+ *   active rows (same page, "Diagnostics" table), and optionally the logits themselves
+ *   from hidden x W_vocab ("[WS2] Framework for ablation experiment", LogProb knobs
+ *   row 9, "LM-head GEMM and materialization boundary").
+ *
+ * Conventions shared by every entry point:
+ *   - All array arguments are DEVICE pointers owned by the caller (e.g. torch tensors);
+ *     the library never allocates device memory and keeps no state between calls.
+ *   - `stream` is a hipStream_t passed as void*; every call is stream-ordered. Only
+ *     drift_diagnostics and drift_get_status synchronize the stream.
+ *   - The caller provides a device workspace of at least drift_workspace_size() bytes,
+ *     256-byte aligned. A workspace must not be shared by calls that can overlap.
+ *   - Return value: DRIFT_OK (0) or a negative DRIFT_E* status. Argument errors are
+ *     detected on the host and returned at once, before any launch. Data-dependent
+ *     errors (mask shape, token ids, non-finite logits) are found on the device and
+ *     recorded in the workspace; drift_get_status() and drift_diagnostics() report them.
+ *     There is exactly one implementation per (operation, dtype); the library never
+ *     falls back to another algorithm ("Kernel Integration Contract": no silent
+ *     fallback).
+ *   - Results are deterministic and each row's results are bitwise independent of the
+ *     batch it is scored in (the "Attention Debug Matrix" page, Metrics: the
+ *     batch-composition control must be exactly zero).
+ */
+#ifndef DRIFT_H
+#define DRIFT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DRIFT_ABI_VERSION 1
+
+/* ---- status codes ---------------------------------------------------------------- */
+#define DRIFT_OK          0
+#define DRIFT_EINVAL     -1  /* null/negative/inconsistent argument, misaligned pointer  */
+#define DRIFT_EDTYPE     -2  /* unsupported logits or id dtype                           */
+#define DRIFT_EWORKSPACE -3  /* workspace missing, too small or misaligned               */
+#define DRIFT_ETOKEN     -4  /* an active row's selected id is outside [0, V)            */
+#define DRIFT_EMASK      -5  /* mask byte not 0/1, action on a padded row, attention not
+                                contiguous on the declared padding side, bad cu_seqlens  */
+#define DRIFT_ENOACTIVE  -6  /* diagnostics over zero active rows                        */
+#define DRIFT_ENONFINITE -7  /* NaN/+inf logit in an active row, selected logit -inf,
+                                |logit| >= 2^127, or a non-finite active dlogp           */
+#define DRIFT_EHIP       -8  /* a HIP runtime call failed                                */
+
+/* ---- element types ---------------------------------------------------------------- */
+#define DRIFT_F32  0
+#define DRIFT_BF16 1
+#define DRIFT_I32  2
+#define DRIFT_I64  3
+
+/* ---- batch layouts (the padding side of "Measurement Contract") ------------------- */
+#define DRIFT_PAD_RIGHT 0  /* each sequence: attended rows, then padding              */
+#define DRIFT_PAD_LEFT  1  /* each sequence: padding, then attended rows              */
+#define DRIFT_PACKED    2  /* sequences packed back to back, delimited by cu_seqlens  */
+
+/* ---- operations (for drift_workspace_size) ---------------------------------------- */
+#define DRIFT_OP_SELECTED_LOGPROB 0
+#define DRIFT_OP_DIAGNOSTICS      1
+#define DRIFT_OP_LMHEAD           2
+
+/*
+ * Arguments of drift_selected_logprob. Logical inputs follow "Measurement Contract"
+ * (same token ids, selected ids, attention and action masks, padding layout, packed
+ * metadata on both sides).
+ *
+ *  logits_dtype    DRIFT_F32 or DRIFT_BF16 (both sides share it).
+ *  ids_dtype       DRIFT_I32 or DRIFT_I64.
+ *  layout          DRIFT_PAD_RIGHT, DRIFT_PAD_LEFT or DRIFT_PACKED.
+ *  num_rows        N, rows of the logits tensors (B*L, or the packed capacity). N < 2^31.
+ *  vocab           V >= 1, logits per row; every column enters the log-sum-exp.
+ *  row_stride      elements between the starts of consecutive rows, >= V.
+ *  train_logits, rollout_logits
+ *                  [N, row_stride] row-major, element-aligned. Rows are pre-shifted:
+ *                  row r scores target_ids[r] (LogProb knobs row 8). Only active rows
+ *                  are read.
+ *  target_ids      [N] selected token ids; values on inactive rows are never checked
+ *                  (e.g. an ignore_index of -100 is fine there).
+ *  attention_mask  [N] bytes 0/1, or NULL = all rows attended (PACKED: all rows before
+ *                  cu_seqlens[num_seqs]). RIGHT: every sequence is 1..1 0..0; LEFT:
+ *                  0..0 1..1; PACKED: if given, exactly the rows before the end.
+ *  action_mask     [N] bytes 0/1, or NULL = every attended row. 0 on prompt rows.
+ *  batch, seq_len  RIGHT/LEFT: B and L with B*L == N. Ignored for PACKED.
+ *  cu_seqlens      PACKED: device int32 [num_seqs+1], starting at 0, non-decreasing,
+ *                  ending <= N; rows at or past the end are packed-buffer padding.
+ *  num_seqs        PACKED: number of sequences.
+ *  prof_events     optional pair of hipEvent_t (as void*), recorded on `stream` right
+ *                  before and after the scoring kernel; NULL entries are skipped.
+ *
+ * A row is active iff attention != 0 and action != 0 (and, PACKED, it is before the end).
+ */
+typedef struct drift_logprob_args {
+  int32_t logits_dtype;
+  int32_t ids_dtype;
+  int32_t layout;
+  int32_t reserved0;           /* must be 0 */
+  int64_t num_rows;
+  int64_t vocab;
+  int64_t row_stride;
+  const void* train_logits;
+  const void* rollout_logits;
+  const void* target_ids;
+  const uint8_t* attention_mask;
+  const uint8_t* action_mask;
+  int64_t batch;
+  int64_t seq_len;
+  const int32_t* cu_seqlens;
+  int64_t num_seqs;
+  void* prof_events[2];
+} drift_logprob_args;
+
+/* Statistics of drift_diagnostics ("Diagnostics" table; every metric over active rows).
+ *  ratio0          mean over active rows of exp(dlogp)
+ *  clipfrac0       (n_clip_low + n_clip_high) / n_active; a ratio is clipped iff
+ *                  exp(d) < 1 - eps_low or exp(d) > 1 + eps_high (evaluated in fp64)
+ *  approx_kl0      mean of exp(d) - 1 - d, evaluated as expm1(d) - d in fp64
+ *  mean_abs_dlogp  mean |d|;   mean_dlogp: mean d
+ *  p95/p99_abs_dlogp  nearest rank: the ceil(q*n)-th smallest |d| (exact)
+ *  max_abs_dlogp   the largest |d|; argmax_row: smallest row index attaining it
+ *  n_nonfinite     active rows whose d is NaN or +-inf (then status ENONFINITE and the
+ *                  means and order statistics are not meaningful)
+ * Means are fp64 sums in a fixed order divided by n; counts and order statistics are
+ * exact. With n_active == 0 the means and order statistics are NaN, argmax_row is -1. */
+typedef struct drift_stats {
+  int64_t n_active;
+  int64_t n_clip_low;
+  int64_t n_clip_high;
+  int64_t n_nonfinite;
+  int64_t argmax_row;
+  double ratio0;
+  double clipfrac0;
+  double approx_kl0;
+  double mean_abs_dlogp;
+  double mean_dlogp;
+  float p95_abs_dlogp;
+  float p99_abs_dlogp;
+  float max_abs_dlogp;
+  int32_t status;
+} drift_stats;
+
+/* Backend descriptor ("Kernel Integration Contract": stable id, semantic operator,
+ * supported architectures/dtypes/layouts, determinism properties, precision and
+ * downcast points, build fingerprint). Static storage; never free. */
+typedef struct drift_backend_desc {
+  int32_t abi_version;
+  const char* backend_id;
+  const char* semantic_ops;
+  const char* archs;
+  const char* dtypes;
+  const char* layouts;
+  const char* determinism;
+  const char* precision;
+  const char* lse_domain;
+  const char* fallback;
+  const char* build_fingerprint;
+} drift_backend_desc;
+
+/* Workspace bytes for `op` over `num_rows` rows of `vocab` columns of element type
+ * `dtype` (DRIFT_OP_LMHEAD: num_rows = T). Returns 0 for invalid arguments. Host only. */
+size_t drift_workspace_size(int op, int64_t num_rows, int64_t vocab, int dtype);
+
+/* Per-row selected-token logprobs of both sides and their drift
+ * ("Measurement Contract"). Outputs, each [N] device arrays:
+ *   train_logp, rollout_logp  x_y - LSE(x), fp32 (the fp64 result rounded once)
+ *   dlogp                     (x^t_y - x^r_y) - (LSE^t - LSE^r) formed in fp64 from the
+ *                             unrounded terms, rounded once to fp32
+ *   active                    1 on active rows, 0 elsewhere
+ * Inactive rows get 0.0; active rows with an out-of-range id get NaN (status ETOKEN).
+ * LSE uses fp32 exp2 terms summed in fp64 with a power-of-two running maximum; the
+ * reduction tree depends only on V, so a row's bits do not depend on the batch.
+ * Asynchronous: returns after launching; data-dependent errors are read later with
+ * drift_get_status(ws) or by passing ws to drift_diagnostics as logprob_ws. */
+int drift_selected_logprob(const drift_logprob_args* args, float* train_logp,
+                           float* rollout_logp, float* dlogp, uint8_t* active, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* Synchronizes `stream` and returns the data-dependent status recorded by the last
+ * drift_selected_logprob or drift_lmhead_logprob call on `ws` (priority EMASK > ETOKEN
+ * > ENONFINITE), and, if first_bad_row is not NULL, the smallest row index of that
+ * error class (-1 when OK). */
+int drift_get_status(const void* ws, void* stream, int64_t* first_bad_row);
+
+/* Diagnostics over the active rows of `dlogp` ("Diagnostics" table). Fills *out_host
+ * (host memory) and synchronizes `stream` once. eps_low, eps_high in [0, 1) give the clip
+ * range [1 - eps_low, 1 + eps_high]. `logprob_ws` (nullable) is the workspace of the
+ * drift_selected_logprob call that produced dlogp: its device status is read in the same
+ * synchronization and takes priority in the return value. Returns DRIFT_OK,
+ * DRIFT_ENOACTIVE, DRIFT_ENONFINITE, or the logprob status. No threshold is applied:
+ * the library reports, it never decides pass/fail. */
+int drift_diagnostics(const float* dlogp, const uint8_t* active, int64_t num_rows,
+                      double eps_low, double eps_high, const void* logprob_ws,
+                      drift_stats* out_host, void* ws, size_t ws_bytes, void* stream);
+
+/* Fused LM-head selected logprob: logits z = hidden x W are formed tile by tile on the
+ * matrix cores and never written to memory; logp[t] = z[t, y_t] - LSE(z[t]).
+ *   hidden      bf16 [T, H] row-major (16-byte aligned rows: H % 8 == 0)
+ *   weight      bf16 [H, V] row-major, vocabulary contiguous (V % 8 == 0)
+ *   target_ids  int32 [T]; active (nullable) uint8 [T]: inactive rows get 0.0
+ *   logp        fp32 [T]
+ * Products accumulate in fp32 over k = 0..H-1 in a fixed order that does not depend on
+ * T or on the row's position, so a row's result is bitwise the same in any batch. */
+int drift_lmhead_logprob(const void* hidden, const void* weight, int64_t T, int64_t H,
+                         int64_t V, const int32_t* target_ids, const uint8_t* active,
+                         float* logp, void* ws, size_t ws_bytes, void* stream);
+
+const drift_backend_desc* drift_backend_descriptor(void);
+
+/* Static description of a status code. */
+const char* drift_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DRIFT_H */

@@ -1,0 +1,108 @@
+"""Shared helpers of the GPU tests: run the library on a synthetic batch, and run the
+oracle on the same inputs copied to the host."""
+import numpy as np
+import torch
+
+import oracle
+from train_rollout_logprob_amd import synth
+
+LOGP_TOL = 2e-5          # per-token |logp_gpu - logp_fp64|
+MEAN_RTOL = 1e-5         # aggregate means, relative
+
+
+def gpu_available():
+    return torch.cuda.is_available()
+
+
+def device_inputs(case, dev="cuda"):
+    ids = torch.as_tensor(case.ids, device=dev)
+    att = torch.as_tensor(case.attention, device=dev) if case.attention is not None else None
+    act = torch.as_tensor(case.action, device=dev) if case.action is not None else None
+    cu = torch.as_tensor(case.cu_seqlens, device=dev) if case.cu_seqlens is not None else None
+    return ids, att, act, cu
+
+
+def run_library(case, dev="cuda", ids_dtype=None, train=None, rollout=None, **kw):
+    from train_rollout_logprob_amd import binding as B
+    ids, att, act, cu = device_inputs(case, dev)
+    if ids_dtype is not None:
+        ids = ids.to(ids_dtype)
+    tr = case.train if train is None else train
+    ro = case.rollout if rollout is None else rollout
+    t, r, d, a, ws = B.selected_logprob(tr, ro, ids, att, act, case.layout, case.B, case.L, cu,
+                                        **kw)
+    st, bad = B.drift_get_status(ws)
+    return {"train_logp": t.cpu().numpy(), "rollout_logp": r.cpu().numpy(),
+            "dlogp": d.cpu().numpy(), "active": a.cpu().numpy(), "status": st,
+            "first_bad": bad, "ws": ws, "d_dev": d, "a_dev": a}
+
+
+def host_logits(t):
+    """Whole logits tensor to host as float32 or bf16 bit patterns."""
+    t = t.cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def run_oracle(case, train=None, rollout=None):
+    tr = host_logits(case.train if train is None else train)
+    ro = host_logits(case.rollout if rollout is None else rollout)
+    return oracle.selected_logprob(tr, ro, case.dtype, case.ids, case.attention, case.action,
+                                   case.V, case.layout, case.B, case.L, case.cu_seqlens)
+
+
+def status_name(code):
+    from train_rollout_logprob_amd import binding as B
+    return B.STATUS_NAMES[code]
+
+
+def assert_logprob_parity(got, want, tol=LOGP_TOL):
+    assert np.array_equal(got["active"], want["active"])
+    act = want["active"] == 1
+    for k in ("train_logp", "rollout_logp", "dlogp"):
+        g = got[k].astype(np.float64)
+        w = want[k]
+        assert np.all(g[~act] == 0.0), k
+        err = np.abs(g[act] - w[act])
+        assert err.size == 0 or float(err.max()) <= tol, (k, float(err.max()))
+
+
+def assert_stats_exact(got, want):
+    """Counts, order statistics and argmax bit-exact; means to MEAN_RTOL relative
+    (mean_dlogp, which sits near 0, to an absolute bound scaled by mean |d|)."""
+    for k in ("n_active", "n_clip_low", "n_clip_high", "n_nonfinite", "argmax_row"):
+        assert got[k] == want[k], (k, got[k], want[k])
+    for k in ("p95_abs_dlogp", "p99_abs_dlogp", "max_abs_dlogp"):
+        g, w = got[k], want[k]
+        assert (np.isnan(g) and np.isnan(w)) or np.float32(g) == np.float32(w), (k, g, w)
+    for k in ("ratio0", "clipfrac0", "approx_kl0", "mean_abs_dlogp"):
+        g, w = got[k], want[k]
+        if np.isnan(w):
+            assert np.isnan(g), k
+        else:
+            assert abs(g - w) <= MEAN_RTOL * abs(w) + 1e-300, (k, g, w)
+    g, w = got["mean_dlogp"], want["mean_dlogp"]
+    if not np.isnan(w):
+        assert abs(g - w) <= MEAN_RTOL * max(abs(w), want["mean_abs_dlogp"]), (g, w)
+
+
+def small_variants():
+    """Scaled-down versions of the scoring workloads: several tiles, ragged tails, every
+    layout and dtype."""
+    return {
+        "tiny": dict(name="tiny"),
+        "qwen8b_small": dict(name="qwen8b", B=3, L=96),
+        "large_small": dict(name="large", B=4, L=64),
+        "packed_small": dict(name="packed", nseq=6, len_lo=64, len_hi=300),
+        "bf16_ragged_V": dict(name="qwen8b", B=2, L=32, V=1001),
+        "f32_ragged_V": dict(name="packed", nseq=3, len_lo=20, len_hi=60, V=4099),
+        "f32_V37": dict(name="tiny", B=2, L=16, V=37, prompt=4),
+        "bf16_V8": dict(name="large", B=2, L=16, V=8, prompt=4),
+    }
+
+
+def make_small(spec, dev="cuda"):
+    spec = dict(spec)
+    name = spec.pop("name")
+    return synth.make_logits_case(name, device=dev, **spec)

@@ -1,0 +1,95 @@
+"""The C-ABI library loads and exports every symbol the header declares; host-side
+argument checks fail closed before any launch (CPU only; no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "drift.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(drift_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    assert names == sorted(["drift_workspace_size", "drift_selected_logprob",
+                            "drift_get_status", "drift_diagnostics", "drift_lmhead_logprob",
+                            "drift_backend_descriptor", "drift_strerror"])
+
+
+def test_library_exports_every_declared_symbol():
+    from train_rollout_logprob_amd import binding as B
+    raw = ctypes.CDLL(B.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(raw, name), name
+    assert set(B.EXPORTS) == set(_declared_functions())
+
+
+def test_struct_layouts_match_header():
+    from train_rollout_logprob_amd import binding as B
+    # drift_logprob_args: 4 x i32, 3 x i64, 5 pointers, 2 x i64, pointer, i64, 2 pointers
+    assert ctypes.sizeof(B.drift_logprob_args) == 16 + 24 + 40 + 16 + 8 + 8 + 16
+    assert ctypes.sizeof(B.drift_stats) == 5 * 8 + 5 * 8 + 3 * 4 + 4
+
+
+def test_descriptor_and_strerror():
+    from train_rollout_logprob_amd import binding as B
+    d = B.drift_backend_descriptor()
+    assert d["abi_version"] == 1 and d["archs"] == "gfx950"
+    assert "batch composition" in d["determinism"]
+    assert d["lse_domain"] == "natural log"
+    assert d["build_fingerprint"].startswith("src:")
+    for code in B.STATUS_NAMES:
+        assert B.drift_strerror(code) != "unknown status"
+    assert B.drift_strerror(12345) == "unknown status"
+
+
+def test_workspace_sizes():
+    from train_rollout_logprob_amd import binding as B
+    f = B.drift_workspace_size
+    assert f(B.DRIFT_OP_SELECTED_LOGPROB, 16384, 151936, B.DRIFT_BF16) >= 256 + 4 * 16384
+    assert f(B.DRIFT_OP_SELECTED_LOGPROB, 0, 1, B.DRIFT_F32) >= 256
+    assert f(B.DRIFT_OP_SELECTED_LOGPROB, 10, 0, B.DRIFT_F32) == 0      # V < 1
+    assert f(B.DRIFT_OP_SELECTED_LOGPROB, -1, 5, B.DRIFT_F32) == 0
+    assert f(B.DRIFT_OP_SELECTED_LOGPROB, 1 << 31, 5, B.DRIFT_F32) == 0
+    assert f(B.DRIFT_OP_SELECTED_LOGPROB, 10, 5, 7) == 0                # bad dtype
+    assert f(B.DRIFT_OP_DIAGNOSTICS, 270000, 1, B.DRIFT_F32) > 0
+    assert f(B.DRIFT_OP_LMHEAD, 16384, 151936, B.DRIFT_F32) == 0        # bf16 only
+    assert f(9, 10, 10, B.DRIFT_F32) == 0
+
+
+def test_host_checks_fail_closed_without_launching():
+    from train_rollout_logprob_amd import binding as B
+    lib = B.lib
+    assert lib.drift_selected_logprob(None, None, None, None, None, None, 0, None) == B.DRIFT_EINVAL
+    a = B.drift_logprob_args()
+    a.logits_dtype = 5
+    assert lib.drift_selected_logprob(ctypes.byref(a), None, None, None, None, None, 0,
+                                      None) == B.DRIFT_EDTYPE
+    a.logits_dtype, a.ids_dtype, a.layout = B.DRIFT_F32, B.DRIFT_I32, B.DRIFT_PAD_RIGHT
+    a.num_rows, a.vocab, a.row_stride = 0, 10, 5                        # stride < V
+    assert lib.drift_selected_logprob(ctypes.byref(a), None, None, None, None, None, 0,
+                                      None) == B.DRIFT_EINVAL
+    a.row_stride, a.batch, a.seq_len = 10, 0, 1
+    assert lib.drift_selected_logprob(ctypes.byref(a), None, None, None, None, None, 0,
+                                      None) == B.DRIFT_EWORKSPACE        # no workspace
+    a.layout = 7
+    assert lib.drift_selected_logprob(ctypes.byref(a), None, None, None, None, None, 0,
+                                      None) == B.DRIFT_EINVAL
+    a.layout, a.num_rows, a.batch, a.seq_len = B.DRIFT_PAD_LEFT, 6, 2, 4  # B*L != N
+    assert lib.drift_selected_logprob(ctypes.byref(a), None, None, None, None, None, 0,
+                                      None) == B.DRIFT_EINVAL
+    st = B.drift_stats()
+    assert lib.drift_diagnostics(None, None, 5, 0.2, 0.2, None, ctypes.byref(st), None, 0,
+                                 None) == B.DRIFT_EINVAL
+    assert lib.drift_diagnostics(None, None, 0, 1.5, 0.2, None, ctypes.byref(st), None, 0,
+                                 None) == B.DRIFT_EINVAL                # eps out of range
+    assert lib.drift_lmhead_logprob(None, None, 4, 4100, 16, None, None, None, None, 0,
+                                    None) == B.DRIFT_EINVAL             # H % 8 != 0
+    assert lib.drift_get_status(None, None, None) == B.DRIFT_EWORKSPACE

@@ -1,0 +1,246 @@
+"""Python binding of the drift library (C ABI of include/drift.h).
+
+This module only marshals arguments into the C ABI declared in ``include/drift.h``; every
+step of the computation runs in the HIP kernels of ``libdrift.so``. Loading fails loudly
+if the library has not been built (there is no CPU fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime that the library shares with PyTorch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdrift.so")
+
+DRIFT_OK = 0
+DRIFT_EINVAL = -1
+DRIFT_EDTYPE = -2
+DRIFT_EWORKSPACE = -3
+DRIFT_ETOKEN = -4
+DRIFT_EMASK = -5
+DRIFT_ENOACTIVE = -6
+DRIFT_ENONFINITE = -7
+DRIFT_EHIP = -8
+STATUS_NAMES = {DRIFT_OK: "OK", DRIFT_EINVAL: "EINVAL", DRIFT_EDTYPE: "EDTYPE",
+                DRIFT_EWORKSPACE: "EWORKSPACE", DRIFT_ETOKEN: "ETOKEN", DRIFT_EMASK: "EMASK",
+                DRIFT_ENOACTIVE: "ENOACTIVE", DRIFT_ENONFINITE: "ENONFINITE",
+                DRIFT_EHIP: "EHIP"}
+
+DRIFT_F32, DRIFT_BF16, DRIFT_I32, DRIFT_I64 = 0, 1, 2, 3
+DRIFT_PAD_RIGHT, DRIFT_PAD_LEFT, DRIFT_PACKED = 0, 1, 2
+LAYOUTS = {"right": DRIFT_PAD_RIGHT, "left": DRIFT_PAD_LEFT, "packed": DRIFT_PACKED}
+DRIFT_OP_SELECTED_LOGPROB, DRIFT_OP_DIAGNOSTICS, DRIFT_OP_LMHEAD = 0, 1, 2
+
+EXPORTS = ("drift_workspace_size", "drift_selected_logprob", "drift_get_status",
+           "drift_diagnostics", "drift_lmhead_logprob", "drift_backend_descriptor",
+           "drift_strerror")
+
+
+class drift_logprob_args(ctypes.Structure):
+    _fields_ = [("logits_dtype", ctypes.c_int32), ("ids_dtype", ctypes.c_int32),
+                ("layout", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("num_rows", ctypes.c_int64), ("vocab", ctypes.c_int64),
+                ("row_stride", ctypes.c_int64), ("train_logits", ctypes.c_void_p),
+                ("rollout_logits", ctypes.c_void_p), ("target_ids", ctypes.c_void_p),
+                ("attention_mask", ctypes.c_void_p), ("action_mask", ctypes.c_void_p),
+                ("batch", ctypes.c_int64), ("seq_len", ctypes.c_int64),
+                ("cu_seqlens", ctypes.c_void_p), ("num_seqs", ctypes.c_int64),
+                ("prof_events", ctypes.c_void_p * 2)]
+
+
+class drift_stats(ctypes.Structure):
+    _fields_ = [("n_active", ctypes.c_int64), ("n_clip_low", ctypes.c_int64),
+                ("n_clip_high", ctypes.c_int64), ("n_nonfinite", ctypes.c_int64),
+                ("argmax_row", ctypes.c_int64), ("ratio0", ctypes.c_double),
+                ("clipfrac0", ctypes.c_double), ("approx_kl0", ctypes.c_double),
+                ("mean_abs_dlogp", ctypes.c_double), ("mean_dlogp", ctypes.c_double),
+                ("p95_abs_dlogp", ctypes.c_float), ("p99_abs_dlogp", ctypes.c_float),
+                ("max_abs_dlogp", ctypes.c_float), ("status", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class drift_backend_desc(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_int32)] + [
+        (n, ctypes.c_char_p) for n in ("backend_id", "semantic_ops", "archs", "dtypes",
+                                        "layouts", "determinism", "precision", "lse_domain",
+                                        "fallback", "build_fingerprint")]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import "
+                          f"__graft_entry__ as g; g.build()'` (no CPU fallback exists)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    lib.drift_workspace_size.argtypes = [ctypes.c_int, i64, i64, ctypes.c_int]
+    lib.drift_workspace_size.restype = sz
+    lib.drift_selected_logprob.argtypes = [ctypes.POINTER(drift_logprob_args), vp, vp, vp, vp,
+                                           vp, sz, vp]
+    lib.drift_selected_logprob.restype = ctypes.c_int
+    lib.drift_get_status.argtypes = [vp, vp, ctypes.POINTER(i64)]
+    lib.drift_get_status.restype = ctypes.c_int
+    lib.drift_diagnostics.argtypes = [vp, vp, i64, ctypes.c_double, ctypes.c_double, vp,
+                                      ctypes.POINTER(drift_stats), vp, sz, vp]
+    lib.drift_diagnostics.restype = ctypes.c_int
+    lib.drift_lmhead_logprob.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]
+    lib.drift_lmhead_logprob.restype = ctypes.c_int
+    lib.drift_backend_descriptor.argtypes = []
+    lib.drift_backend_descriptor.restype = ctypes.POINTER(drift_backend_desc)
+    lib.drift_strerror.argtypes = [ctypes.c_int]
+    lib.drift_strerror.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+# ----------------------------------------------------------------------------- C names
+
+def drift_workspace_size(op: int, num_rows: int, vocab: int, dtype: int) -> int:
+    return int(lib.drift_workspace_size(op, num_rows, vocab, dtype))
+
+
+def drift_selected_logprob(args: drift_logprob_args, train_logp, rollout_logp, dlogp, active,
+                           ws, ws_bytes: int, stream) -> int:
+    return int(lib.drift_selected_logprob(ctypes.byref(args), _ptr(train_logp),
+                                          _ptr(rollout_logp), _ptr(dlogp), _ptr(active),
+                                          _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def drift_get_status(ws, stream=None):
+    bad = ctypes.c_int64(-1)
+    st = int(lib.drift_get_status(_ptr(ws), _stream(stream), ctypes.byref(bad)))
+    return st, int(bad.value)
+
+
+def drift_diagnostics(dlogp, active, num_rows: int, eps_low: float, eps_high: float,
+                      logprob_ws, ws, ws_bytes: int, stream=None):
+    out = drift_stats()
+    st = int(lib.drift_diagnostics(_ptr(dlogp), _ptr(active), num_rows, eps_low, eps_high,
+                                   _ptr(logprob_ws), ctypes.byref(out), _ptr(ws), ws_bytes,
+                                   _stream(stream)))
+    return st, out
+
+
+def drift_lmhead_logprob(hidden, weight, T: int, H: int, V: int, target_ids, active, logp, ws,
+                         ws_bytes: int, stream=None) -> int:
+    return int(lib.drift_lmhead_logprob(_ptr(hidden), _ptr(weight), T, H, V, _ptr(target_ids),
+                                        _ptr(active), _ptr(logp), _ptr(ws), ws_bytes,
+                                        _stream(stream)))
+
+
+def drift_backend_descriptor() -> dict:
+    d = lib.drift_backend_descriptor().contents
+    out = {"abi_version": d.abi_version}
+    for n, _ in drift_backend_desc._fields_[1:]:
+        v = getattr(d, n)
+        out[n] = v.decode() if v is not None else None
+    return out
+
+
+def drift_strerror(status: int) -> str:
+    return lib.drift_strerror(status).decode()
+
+
+# ----------------------------------------------------------------------------- helpers
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+class DriftError(RuntimeError):
+    def __init__(self, status, where=""):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} "
+                         f"({drift_strerror(status)})")
+
+
+def workspace(op: int, num_rows: int, vocab: int, dtype: int, device) -> torch.Tensor:
+    n = drift_workspace_size(op, num_rows, vocab, dtype)
+    if n == 0:
+        raise DriftError(DRIFT_EINVAL, "drift_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def make_args(train, rollout, ids, attention=None, action=None, layout="right", batch=0,
+              seq_len=0, cu_seqlens=None, vocab=None, events=None) -> drift_logprob_args:
+    """Describe torch tensors to the C ABI (no copies, no conversions)."""
+    if train.dtype != rollout.dtype or train.shape != rollout.shape:
+        raise ValueError("train and rollout logits must share dtype and shape")
+    if train.stride(1) != 1 or rollout.stride(0) != train.stride(0):
+        raise ValueError("logits rows must be contiguous with a common row stride")
+    a = drift_logprob_args()
+    a.logits_dtype = {torch.float32: DRIFT_F32, torch.bfloat16: DRIFT_BF16}.get(train.dtype, 99)
+    a.ids_dtype = {torch.int32: DRIFT_I32, torch.int64: DRIFT_I64}.get(ids.dtype, 99)
+    a.layout = LAYOUTS[layout]
+    a.reserved0 = 0
+    a.num_rows = train.shape[0]
+    a.vocab = vocab if vocab is not None else train.shape[1]
+    a.row_stride = train.stride(0)
+    a.train_logits = train.data_ptr()
+    a.rollout_logits = rollout.data_ptr()
+    a.target_ids = ids.data_ptr()
+    a.attention_mask = attention.data_ptr() if attention is not None else None
+    a.action_mask = action.data_ptr() if action is not None else None
+    a.batch = batch
+    a.seq_len = seq_len
+    a.cu_seqlens = cu_seqlens.data_ptr() if cu_seqlens is not None else None
+    a.num_seqs = (cu_seqlens.numel() - 1) if cu_seqlens is not None else 0
+    if events is not None:
+        a.prof_events[0] = events[0]
+        a.prof_events[1] = events[1]
+    return a
+
+
+def selected_logprob(train, rollout, ids, attention=None, action=None, layout="right",
+                     batch=0, seq_len=0, cu_seqlens=None, ws=None, out=None, stream=None,
+                     events=None, check=False):
+    """Allocate outputs (and a workspace unless given) and call drift_selected_logprob.
+    Returns (train_logp, rollout_logp, dlogp, active, ws). With check=True, synchronizes
+    and raises DriftError on a data-dependent status."""
+    N = train.shape[0]
+    dev = train.device
+    args = make_args(train, rollout, ids, attention, action, layout, batch, seq_len,
+                     cu_seqlens, events=events)
+    if ws is None:
+        ws = workspace(DRIFT_OP_SELECTED_LOGPROB, N, args.vocab, args.logits_dtype, dev)
+    if out is None:
+        out = (torch.empty(N, dtype=torch.float32, device=dev),
+               torch.empty(N, dtype=torch.float32, device=dev),
+               torch.empty(N, dtype=torch.float32, device=dev),
+               torch.empty(N, dtype=torch.uint8, device=dev))
+    st = drift_selected_logprob(args, *out, ws, ws.numel(), stream)
+    if st != DRIFT_OK:
+        raise DriftError(st, "drift_selected_logprob")
+    if check:
+        st, _ = drift_get_status(ws, stream)
+        if st != DRIFT_OK:
+            raise DriftError(st, "drift_selected_logprob (device)")
+    return (*out, ws)
+
+
+def diagnostics(dlogp, active, eps_low=0.2, eps_high=0.2, logprob_ws=None, ws=None,
+                stream=None):
+    """Call drift_diagnostics; returns (status, stats dict)."""
+    N = dlogp.shape[0]
+    if ws is None:
+        ws = workspace(DRIFT_OP_DIAGNOSTICS, N, 1, DRIFT_F32, dlogp.device)
+    st, s = drift_diagnostics(dlogp, active, N, eps_low, eps_high, logprob_ws, ws, ws.numel(),
+                              stream)
+    return st, s.as_dict()

@@ -1,0 +1,230 @@
+// C entry points of the drift library: argument checks (fail closed, before any launch),
+// workspace sizing, dispatch to the kernels, status readback and the backend descriptor.
+#include <string.h>
+
+#include "common.h"
+
+#ifndef DRIFT_BUILD_FINGERPRINT
+#define DRIFT_BUILD_FINGERPRINT "unknown"
+#endif
+
+using namespace drift;
+
+namespace {
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int status_from_header(const WsHeader& h, int64_t* first_bad) {
+  static const int kCode[kNumErr] = {DRIFT_EMASK, DRIFT_ETOKEN, DRIFT_ENONFINITE};
+  if (h.magic != kWsMagic) {
+    if (first_bad) *first_bad = -1;
+    return DRIFT_EWORKSPACE;
+  }
+  for (int c = 0; c < kNumErr; ++c) {  // priority: mask, token, non-finite
+    if (h.err_bits & (1u << c)) {
+      if (first_bad) *first_bad = (int64_t)h.first_bad[c];
+      return kCode[c];
+    }
+  }
+  if (first_bad) *first_bad = -1;
+  return DRIFT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t drift_workspace_size(int op, int64_t num_rows, int64_t vocab, int dtype) {
+  if (num_rows < 0 || num_rows > INT32_MAX || vocab < 1) return 0;
+  switch (op) {
+    case DRIFT_OP_SELECTED_LOGPROB:
+      if (dtype != DRIFT_F32 && dtype != DRIFT_BF16) return 0;
+      return LogprobWs::make(num_rows).total;
+    case DRIFT_OP_DIAGNOSTICS:
+      return diag_ws_bytes(num_rows);
+    case DRIFT_OP_LMHEAD:
+      if (dtype != DRIFT_BF16) return 0;
+      return lmhead_ws_bytes(num_rows, vocab);
+    default:
+      return 0;
+  }
+}
+
+int drift_selected_logprob(const drift_logprob_args* a, float* train_logp, float* rollout_logp,
+                           float* dlogp, uint8_t* active, void* ws, size_t ws_bytes,
+                           void* stream) {
+  if (!a) return DRIFT_EINVAL;
+  if (a->logits_dtype != DRIFT_F32 && a->logits_dtype != DRIFT_BF16) return DRIFT_EDTYPE;
+  if (a->ids_dtype != DRIFT_I32 && a->ids_dtype != DRIFT_I64) return DRIFT_EDTYPE;
+  if (a->reserved0 != 0) return DRIFT_EINVAL;
+  const int64_t N = a->num_rows, V = a->vocab;
+  if (N < 0 || N > INT32_MAX || V < 1 || V > INT32_MAX || a->row_stride < V) return DRIFT_EINVAL;
+  const size_t esz = a->logits_dtype == DRIFT_F32 ? 4 : 2;
+  const size_t isz = a->ids_dtype == DRIFT_I32 ? 4 : 8;
+  if (N > 0) {
+    if (!a->train_logits || !a->rollout_logits || !a->target_ids) return DRIFT_EINVAL;
+    if (!train_logp || !rollout_logp || !dlogp || !active) return DRIFT_EINVAL;
+    if (!aligned(a->train_logits, esz) || !aligned(a->rollout_logits, esz) ||
+        !aligned(a->target_ids, isz) || !aligned(train_logp, 4) ||
+        !aligned(rollout_logp, 4) || !aligned(dlogp, 4))
+      return DRIFT_EINVAL;
+  }
+  switch (a->layout) {
+    case DRIFT_PAD_RIGHT:
+    case DRIFT_PAD_LEFT:
+      if (a->batch < 0 || a->seq_len < 1 || a->batch * a->seq_len != N) return DRIFT_EINVAL;
+      break;
+    case DRIFT_PACKED:
+      if (!a->cu_seqlens || a->num_seqs < 0 || a->num_seqs > INT32_MAX - 1 ||
+          !aligned(a->cu_seqlens, 4))
+        return DRIFT_EINVAL;
+      break;
+    default:
+      return DRIFT_EINVAL;
+  }
+  const LogprobWs lay = LogprobWs::make(N);
+  if (!ws || !aligned(ws, 256) || ws_bytes < lay.total) return DRIFT_EWORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+
+  ClassifyParams cp;
+  cp.N = N;
+  cp.V = V;
+  cp.B = a->batch;
+  cp.L = a->layout == DRIFT_PACKED ? 1 : a->seq_len;
+  cp.nseq = a->num_seqs;
+  cp.layout = a->layout;
+  cp.ids_i64 = a->ids_dtype == DRIFT_I64;
+  cp.ids = a->target_ids;
+  cp.att = a->attention_mask;
+  cp.act = a->action_mask;
+  cp.cu = a->cu_seqlens;
+  cp.out_t = train_logp;
+  cp.out_r = rollout_logp;
+  cp.out_d = dlogp;
+  cp.active = active;
+  cp.ws = (char*)ws;
+  if (launch_classify(cp, s) != hipSuccess) return DRIFT_EHIP;
+
+  ScoreParams sp;
+  sp.N = N;
+  sp.V = V;
+  sp.stride = a->row_stride;
+  sp.dtype = a->logits_dtype;
+  sp.ids_i64 = cp.ids_i64;
+  sp.train = a->train_logits;
+  sp.rollout = a->rollout_logits;
+  sp.ids = a->target_ids;
+  sp.out_t = train_logp;
+  sp.out_r = rollout_logp;
+  sp.out_d = dlogp;
+  sp.ws = (char*)ws;
+  if (a->prof_events[0] && hipEventRecord((hipEvent_t)a->prof_events[0], s) != hipSuccess)
+    return DRIFT_EHIP;
+  if (launch_score(sp, s) != hipSuccess) return DRIFT_EHIP;
+  if (a->prof_events[1] && hipEventRecord((hipEvent_t)a->prof_events[1], s) != hipSuccess)
+    return DRIFT_EHIP;
+  return DRIFT_OK;
+}
+
+int drift_get_status(const void* ws, void* stream, int64_t* first_bad_row) {
+  if (!ws) return DRIFT_EWORKSPACE;
+  WsHeader h;
+  hipStream_t s = (hipStream_t)stream;
+  if (hipMemcpyAsync(&h, ws, sizeof(h), hipMemcpyDeviceToHost, s) != hipSuccess)
+    return DRIFT_EHIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return DRIFT_EHIP;
+  return status_from_header(h, first_bad_row);
+}
+
+int drift_diagnostics(const float* dlogp, const uint8_t* active, int64_t num_rows,
+                      double eps_low, double eps_high, const void* logprob_ws,
+                      drift_stats* out_host, void* ws, size_t ws_bytes, void* stream) {
+  if (!out_host || num_rows < 0 || num_rows > INT32_MAX) return DRIFT_EINVAL;
+  if (num_rows > 0 && (!dlogp || !active || !aligned(dlogp, 4))) return DRIFT_EINVAL;
+  if (!(eps_low >= 0.0 && eps_low < 1.0 && eps_high >= 0.0 && eps_high < 1.0))
+    return DRIFT_EINVAL;
+  if (!ws || !aligned(ws, 256) || ws_bytes < diag_ws_bytes(num_rows)) return DRIFT_EWORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  DiagParams dp;
+  dp.N = num_rows;
+  dp.eps_low = eps_low;
+  dp.eps_high = eps_high;
+  dp.d = dlogp;
+  dp.active = active;
+  dp.ws = (char*)ws;
+  if (launch_diagnostics(dp, s) != hipSuccess) return DRIFT_EHIP;
+  if (hipMemcpyAsync(out_host, (const char*)ws + diag_stats_offset(), sizeof(drift_stats),
+                     hipMemcpyDeviceToHost, s) != hipSuccess)
+    return DRIFT_EHIP;
+  WsHeader h;
+  if (logprob_ws &&
+      hipMemcpyAsync(&h, logprob_ws, sizeof(h), hipMemcpyDeviceToHost, s) != hipSuccess)
+    return DRIFT_EHIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return DRIFT_EHIP;
+  if (logprob_ws) {
+    const int st = status_from_header(h, nullptr);
+    if (st != DRIFT_OK) return st;
+  }
+  return out_host->status;
+}
+
+int drift_lmhead_logprob(const void* hidden, const void* weight, int64_t T, int64_t H, int64_t V,
+                         const int32_t* target_ids, const uint8_t* active, float* logp,
+                         void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0 || T > INT32_MAX || H < 1 || V < 1 || V > INT32_MAX) return DRIFT_EINVAL;
+  if (H % 8 != 0 || V % 8 != 0) return DRIFT_EINVAL;
+  if (T > 0 && (!hidden || !weight || !target_ids || !logp)) return DRIFT_EINVAL;
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(target_ids, 4) ||
+      !aligned(logp, 4))
+    return DRIFT_EINVAL;
+  if (!ws || !aligned(ws, 256) || ws_bytes < lmhead_ws_bytes(T, V)) return DRIFT_EWORKSPACE;
+  LmheadParams lp;
+  lp.T = T;
+  lp.H = H;
+  lp.V = V;
+  lp.hidden = hidden;
+  lp.weight = weight;
+  lp.ids = target_ids;
+  lp.active = active;
+  lp.logp = logp;
+  lp.ws = (char*)ws;
+  if (launch_lmhead(lp, (hipStream_t)stream) != hipSuccess) return DRIFT_EHIP;
+  return DRIFT_OK;
+}
+
+const drift_backend_desc* drift_backend_descriptor(void) {
+  static const drift_backend_desc d = {
+      DRIFT_ABI_VERSION,
+      "drift.gfx950.v1",
+      "selected_token_logprob,dlogp,drift_diagnostics,lmhead_selected_logprob",
+      "gfx950",
+      "logits:f32,bf16;ids:i32,i64;lmhead:bf16",
+      "pad_right,pad_left,packed(cu_seqlens);logits row-major [N,row_stride]",
+      "deterministic; fixed-order reductions; per-row results bitwise independent of "
+      "batch composition and position; no atomics in value paths",
+      "logits widened to fp32; exp2 in fp32 with a power-of-two running max; sums in "
+      "fp64; lse/logp/dlogp formed in fp64, rounded once to fp32; diagnostics in fp64; "
+      "lmhead products bf16 x bf16 -> fp32 accumulate, fixed k order",
+      "natural log",
+      "none: one implementation per (op, dtype); unsupported inputs fail closed",
+      DRIFT_BUILD_FINGERPRINT,
+  };
+  return &d;
+}
+
+const char* drift_strerror(int status) {
+  switch (status) {
+    case DRIFT_OK: return "ok";
+    case DRIFT_EINVAL: return "invalid argument";
+    case DRIFT_EDTYPE: return "unsupported dtype";
+    case DRIFT_EWORKSPACE: return "workspace missing, too small, misaligned or not initialised";
+    case DRIFT_ETOKEN: return "selected token id outside [0, V) on an active row";
+    case DRIFT_EMASK: return "invalid attention/action mask or packed metadata";
+    case DRIFT_ENOACTIVE: return "no active rows";
+    case DRIFT_ENONFINITE: return "non-finite logit or dlogp on an active row";
+    case DRIFT_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"
