@@ -21,6 +21,15 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "active tokens/sec + logits HBM GB/s (% of peak) for paired logprob+drift"
+WORKLOAD_TEXT = {
+    "qwen8b": "qwen8b-shaped paired scoring: bf16 logits, V=151936, B=8, L=2048 "
+              "(prompt 512 + response 1536), left padding",
+    "large": "large-batch paired scoring: bf16 logits, V=151936, B=32, L=4096 "
+             "(prompt 1024 + response U[1024,3072]), right padding",
+    "packed": "packed varlen paired scoring: fp32 logits, V=32000, 256 sequences "
+              "U[64,2048] via cu_seqlens, Student-t(2) drift",
+    "tiny": "tiny paired scoring: fp32 logits, V=1024, B=2, L=64, right padding",
+}
 
 
 def log(*a):
@@ -57,6 +66,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="qwen8b", choices=["qwen8b", "large", "packed", "tiny"],
+                    help="scoring workload (the benchmark line is quoted on qwen8b)")
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
+                    help="copy: a plain device copy of known size, to calibrate HBM counters")
+    ap.add_argument("--copy-mib", type=int, default=4096)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build has "
@@ -72,18 +86,26 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    log("[bench] generating the qwen8b-shaped workload")
-    case = synth.make_logits_case("qwen8b", device=dev)
+    if args.mode == "copy":
+        n = args.copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {n} bytes 3 times (read {n} and write {n} per copy)")
+        return
+    log(f"[bench] generating the {args.workload} workload")
+    case = synth.make_logits_case(args.workload, device=dev)
     ids = torch.as_tensor(case.ids, device=dev)
-    att = torch.as_tensor(case.attention, device=dev)
+    att = torch.as_tensor(case.attention, device=dev) if case.attention is not None else None
     act = torch.as_tensor(case.action, device=dev)
+    cu = torch.as_tensor(case.cu_seqlens, device=dev) if case.cu_seqlens is not None else None
     N, V = case.N, case.V
+    esz = case.elem_bytes
     n_active = case.n_active()
-    ws = B.workspace(B.DRIFT_OP_SELECTED_LOGPROB, N, V, B.DRIFT_BF16, dev)
-    dws = B.workspace(B.DRIFT_OP_DIAGNOSTICS, N, 1, B.DRIFT_F32, dev)
-    outs = tuple(torch.empty(N, dtype=dt, device=dev)
-                 for dt in (torch.float32, torch.float32, torch.float32, torch.uint8))
-    stream = torch.cuda.current_stream()
+    runner = B.ScoringStep(case.train, case.rollout, ids, att, act, case.layout, case.B,
+                           case.L, cu, case.eps_low, case.eps_high)
     n_ev = args.warmup + args.steps
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(n_ev)]
@@ -91,34 +113,31 @@ def main():
         e0.record()
         e1.record()
     torch.cuda.synchronize()
+    handles = [(e0.cuda_event, e1.cuda_event) for e0, e1 in evs]
 
     def step(i):
-        B.selected_logprob(case.train, case.rollout, ids, att, act, "left", case.B, case.L,
-                           ws=ws, out=outs, stream=stream,
-                           events=(evs[i][0].cuda_event, evs[i][1].cuda_event))
-        st, s = B.diagnostics(outs[2], outs[3], case.eps_low, case.eps_high, logprob_ws=ws,
-                              ws=dws, stream=stream)
+        runner.set_events(*handles[i])
+        st = runner.run()
         if st != B.DRIFT_OK:
             raise RuntimeError(f"status {B.STATUS_NAMES[st]}")
-        return s
 
     log("[bench] warmup")
     for i in range(args.warmup):
-        stats = step(i)
+        step(i)
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
     t0 = time.perf_counter()
     for i in range(args.warmup, n_ev):
-        stats = step(i)
+        step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     kern_ms = [evs[i][0].elapsed_time(evs[i][1]) for i in range(args.warmup, n_ev)]
     kern_avg = sum(kern_ms) / len(kern_ms)
-    assert stats["n_active"] == n_active, (stats["n_active"], n_active)
+    assert runner.stats.n_active == n_active, (runner.stats.n_active, n_active)
 
     ms_per_step = elapsed * 1e3 / args.steps
     value = n_active * args.steps / elapsed
-    alg_bytes = n_active * V * 2 * 2
+    alg_bytes = n_active * V * esz * 2
     achieved = alg_bytes / (kern_avg * 1e-3) / 1e9
     log(f"[bench] step {ms_per_step:.3f} ms, scoring kernel {kern_avg:.3f} ms "
         f"({achieved:.0f} GB/s), {value / 1e6:.3f} M active tok/s")
@@ -141,15 +160,14 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "qwen8b-shaped paired scoring: bf16 logits, V=151936, B=8, "
-                               "L=2048 (prompt 512 + response 1536), left padding",
-                   "V": V, "B": case.B, "L": case.L, "n_active": n_active,
-                   "logits_dtype": "bf16", "arith": "fp32 exp2, fp64 sums",
+        "config": {"workload": WORKLOAD_TEXT[args.workload],
+                   "V": V, "B": case.B, "L": case.L, "N": N, "n_active": n_active,
+                   "logits_dtype": case.dtype, "arith": "fp32 exp2, fp64 sums",
                    "parallelism": "single GPU"},
         "logits_gbs": alg_bytes * args.steps / elapsed / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "score_rows<bf16>", "kernel_ms": kern_avg,
+                     "kernel": f"score_rows<{case.dtype}>", "kernel_ms": kern_avg,
                      "bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
     }

@@ -130,6 +130,7 @@ typedef struct drift_logprob_args {
  *  max_abs_dlogp   the largest |d|; argmax_row: smallest row index attaining it
  *  n_nonfinite     active rows whose d is NaN or +-inf (then status ENONFINITE and the
  *                  means and order statistics are not meaningful)
+ *  status          the value drift_diagnostics returns
  * Means are fp64 sums in a fixed order divided by n; counts and order statistics are
  * exact. With n_active == 0 the means and order statistics are NaN, argmax_row is -1. */
 typedef struct drift_stats {

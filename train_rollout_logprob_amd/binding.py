@@ -244,3 +244,48 @@ def diagnostics(dlogp, active, eps_low=0.2, eps_high=0.2, logprob_ws=None, ws=No
     st, s = drift_diagnostics(dlogp, active, N, eps_low, eps_high, logprob_ws, ws, ws.numel(),
                               stream)
     return st, s.as_dict()
+
+
+class ScoringStep:
+    """Repeated drift_selected_logprob + drift_diagnostics on fixed tensors.
+
+    All marshalling (argument struct, output tensors, workspaces, a pinned host buffer for
+    the statistics) is done once here, so a call to `run` is two C calls."""
+
+    def __init__(self, train, rollout, ids, attention=None, action=None, layout="right",
+                 batch=0, seq_len=0, cu_seqlens=None, eps_low=0.2, eps_high=0.2,
+                 stream=None):
+        dev = train.device
+        self.args = make_args(train, rollout, ids, attention, action, layout, batch, seq_len,
+                              cu_seqlens)
+        self.N = int(self.args.num_rows)
+        self.eps = (float(eps_low), float(eps_high))
+        self.ws = workspace(DRIFT_OP_SELECTED_LOGPROB, self.N, self.args.vocab,
+                            self.args.logits_dtype, dev)
+        self.dws = workspace(DRIFT_OP_DIAGNOSTICS, self.N, 1, DRIFT_F32, dev)
+        self.out = (torch.empty(self.N, dtype=torch.float32, device=dev),
+                    torch.empty(self.N, dtype=torch.float32, device=dev),
+                    torch.empty(self.N, dtype=torch.float32, device=dev),
+                    torch.empty(self.N, dtype=torch.uint8, device=dev))
+        self._pinned = torch.empty(ctypes.sizeof(drift_stats), dtype=torch.uint8,
+                                   pin_memory=True)
+        self.stats = drift_stats.from_address(self._pinned.data_ptr())
+        self._stream = _stream(stream)
+        self._args_ref = ctypes.byref(self.args)
+        self._stats_ref = ctypes.byref(self.stats)
+        t, r, d, a = (x.data_ptr() for x in self.out)
+        self._lp_args = (self._args_ref, t, r, d, a, self.ws.data_ptr(), self.ws.numel(),
+                         self._stream)
+        self._dg_args = (d, a, self.N, self.eps[0], self.eps[1], self.ws.data_ptr(),
+                         self._stats_ref, self.dws.data_ptr(), self.dws.numel(), self._stream)
+
+    def set_events(self, ev0, ev1):
+        """hipEvent_t handles recorded around the scoring kernel (0 to disable)."""
+        self.args.prof_events[0] = ev0
+        self.args.prof_events[1] = ev1
+
+    def run(self) -> int:
+        st = lib.drift_selected_logprob(*self._lp_args)
+        if st != DRIFT_OK:
+            raise DriftError(st, "drift_selected_logprob")
+        return lib.drift_diagnostics(*self._dg_args)

@@ -14,7 +14,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdrift.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ["api.hip", "classify.hip", "logprob.hip", "diagnostics.hip", "lmhead.hip"]
+SOURCES = ["api.hip", "logprob.hip", "diagnostics.hip", "lmhead.hip"]
+HEADERS = ["common.h", "classify.h"]
 
 ARCH = "gfx950"
 FLAGS = [
@@ -36,7 +37,7 @@ def _fingerprint(hipcc: str) -> str:
     ver = subprocess.run([hipcc, "--version"], capture_output=True, text=True).stdout
     ver = " ".join(l.strip() for l in ver.splitlines() if "version" in l.lower())[:160]
     h = hashlib.sha256()
-    for s in SOURCES + ["common.h"]:
+    for s in SOURCES + HEADERS:
         with open(os.path.join(CSRC, s), "rb") as f:
             h.update(f.read())
     with open(os.path.join(INCLUDE, "drift.h"), "rb") as f:
@@ -44,34 +45,39 @@ def _fingerprint(hipcc: str) -> str:
     return f"src:{h.hexdigest()[:16]} arch:{ARCH} flags:{' '.join(FLAGS[1:7])} {ver}"
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source (always; no up-to-date check) and link libdrift.so."""
+def build(verbose: bool = False, defines=(), out: str = LIB, build_dir: str = BUILD_DIR) -> str:
+    """Compile every source (always; no up-to-date check) and link the library.
+    `defines` are extra -D options (e.g. another scoring block shape); they become part of
+    the build fingerprint."""
     hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    os.makedirs(build_dir, exist_ok=True)
     fp = _fingerprint(hipcc).replace('"', "'")
+    if defines:
+        fp += " defs:" + ",".join(defines)
     defs = [f'-DDRIFT_BUILD_FINGERPRINT="{fp}"', f"-I{INCLUDE}", f"-I{CSRC}"]
+    defs += [f"-D{d}" for d in defines]
 
     def compile_one(src):
-        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
         cmd = [hipcc, *FLAGS, *defs, "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
-        out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+        msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                         if "packed-fp32-ops" not in l)
         if r.returncode != 0:
-            raise RuntimeError(f"hipcc failed on {src}:\n{out}")
-        if verbose and out.strip():
-            print(out, file=sys.stderr)
+            raise RuntimeError(f"hipcc failed on {src}:\n{msg}")
+        if verbose and msg.strip():
+            print(msg, file=sys.stderr)
         return obj
 
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -15,19 +15,14 @@ namespace {
 inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int status_from_header(const WsHeader& h, int64_t* first_bad) {
-  static const int kCode[kNumErr] = {DRIFT_EMASK, DRIFT_ETOKEN, DRIFT_ENONFINITE};
-  if (h.magic != kWsMagic) {
-    if (first_bad) *first_bad = -1;
-    return DRIFT_EWORKSPACE;
+  const int st = header_status(h.magic, h.err_bits);
+  if (first_bad) {
+    *first_bad = -1;
+    const int cls = st == DRIFT_EMASK ? kErrMask : st == DRIFT_ETOKEN ? kErrToken
+                  : st == DRIFT_ENONFINITE ? kErrNonfinite : -1;
+    if (cls >= 0) *first_bad = (int64_t)h.first_bad[cls];
   }
-  for (int c = 0; c < kNumErr; ++c) {  // priority: mask, token, non-finite
-    if (h.err_bits & (1u << c)) {
-      if (first_bad) *first_bad = (int64_t)h.first_bad[c];
-      return kCode[c];
-    }
-  }
-  if (first_bad) *first_bad = -1;
-  return DRIFT_OK;
+  return st;
 }
 
 }  // namespace
@@ -39,7 +34,7 @@ size_t drift_workspace_size(int op, int64_t num_rows, int64_t vocab, int dtype) 
   switch (op) {
     case DRIFT_OP_SELECTED_LOGPROB:
       if (dtype != DRIFT_F32 && dtype != DRIFT_BF16) return 0;
-      return LogprobWs::make(num_rows).total;
+      return kLogprobWsBytes;
     case DRIFT_OP_DIAGNOSTICS:
       return diag_ws_bytes(num_rows);
     case DRIFT_OP_LMHEAD:
@@ -82,46 +77,29 @@ int drift_selected_logprob(const drift_logprob_args* a, float* train_logp, float
     default:
       return DRIFT_EINVAL;
   }
-  const LogprobWs lay = LogprobWs::make(N);
-  if (!ws || !aligned(ws, 256) || ws_bytes < lay.total) return DRIFT_EWORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
-
-  ClassifyParams cp;
-  cp.N = N;
-  cp.V = V;
-  cp.B = a->batch;
-  cp.L = a->layout == DRIFT_PACKED ? 1 : a->seq_len;
-  cp.nseq = a->num_seqs;
-  cp.layout = a->layout;
-  cp.ids_i64 = a->ids_dtype == DRIFT_I64;
-  cp.ids = a->target_ids;
-  cp.att = a->attention_mask;
-  cp.act = a->action_mask;
-  cp.cu = a->cu_seqlens;
-  cp.out_t = train_logp;
-  cp.out_r = rollout_logp;
-  cp.out_d = dlogp;
-  cp.active = active;
-  cp.ws = (char*)ws;
-  if (launch_classify(cp, s) != hipSuccess) return DRIFT_EHIP;
-
+  if (!ws || !aligned(ws, 256) || ws_bytes < kLogprobWsBytes) return DRIFT_EWORKSPACE;
   ScoreParams sp;
   sp.N = N;
   sp.V = V;
   sp.stride = a->row_stride;
+  sp.L = a->layout == DRIFT_PACKED ? 1 : a->seq_len;
+  sp.nseq = a->num_seqs;
   sp.dtype = a->logits_dtype;
-  sp.ids_i64 = cp.ids_i64;
+  sp.ids_i64 = a->ids_dtype == DRIFT_I64;
+  sp.layout = a->layout;
   sp.train = a->train_logits;
   sp.rollout = a->rollout_logits;
   sp.ids = a->target_ids;
+  sp.att = a->attention_mask;
+  sp.act = a->action_mask;
+  sp.cu = a->cu_seqlens;
   sp.out_t = train_logp;
   sp.out_r = rollout_logp;
   sp.out_d = dlogp;
+  sp.active = active;
   sp.ws = (char*)ws;
-  if (a->prof_events[0] && hipEventRecord((hipEvent_t)a->prof_events[0], s) != hipSuccess)
-    return DRIFT_EHIP;
-  if (launch_score(sp, s) != hipSuccess) return DRIFT_EHIP;
-  if (a->prof_events[1] && hipEventRecord((hipEvent_t)a->prof_events[1], s) != hipSuccess)
+  if (launch_score(sp, (hipStream_t)stream, (hipEvent_t)a->prof_events[0],
+                   (hipEvent_t)a->prof_events[1]) != hipSuccess)
     return DRIFT_EHIP;
   return DRIFT_OK;
 }
@@ -151,20 +129,14 @@ int drift_diagnostics(const float* dlogp, const uint8_t* active, int64_t num_row
   dp.eps_high = eps_high;
   dp.d = dlogp;
   dp.active = active;
+  dp.lp = (const WsHeader*)logprob_ws;
   dp.ws = (char*)ws;
   if (launch_diagnostics(dp, s) != hipSuccess) return DRIFT_EHIP;
+  // one copy: the device folded the logprob status into stats.status
   if (hipMemcpyAsync(out_host, (const char*)ws + diag_stats_offset(), sizeof(drift_stats),
                      hipMemcpyDeviceToHost, s) != hipSuccess)
     return DRIFT_EHIP;
-  WsHeader h;
-  if (logprob_ws &&
-      hipMemcpyAsync(&h, logprob_ws, sizeof(h), hipMemcpyDeviceToHost, s) != hipSuccess)
-    return DRIFT_EHIP;
   if (hipStreamSynchronize(s) != hipSuccess) return DRIFT_EHIP;
-  if (logprob_ws) {
-    const int st = status_from_header(h, nullptr);
-    if (st != DRIFT_OK) return st;
-  }
   return out_host->status;
 }
 

@@ -23,24 +23,10 @@ struct WsHeader {
 static_assert(sizeof(WsHeader) == 256, "header size");
 constexpr uint32_t kWsMagic = 0x44524654u;  // "DRFT"
 
-// Classification tiles: a block of 256 threads covers kClassifyTile consecutive rows.
-constexpr int kClassifyThreads = 256;
-constexpr int kClassifyTile = 2048;
-
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Workspace layout of drift_selected_logprob.
-struct LogprobWs {
-  size_t rows_off, counts_off, total;
-  __host__ __device__ static LogprobWs make(int64_t N) {
-    LogprobWs w;
-    size_t nblk = (size_t)((N + kClassifyTile - 1) / kClassifyTile);
-    w.rows_off = 256;
-    w.counts_off = w.rows_off + align_up((size_t)N * 4, 256);
-    w.total = w.counts_off + align_up(nblk * 32 + 32, 256);
-    return w;
-  }
-};
+// Workspace of drift_selected_logprob: the header only.
+constexpr size_t kLogprobWsBytes = sizeof(WsHeader);
 
 __device__ __forceinline__ void record_error(WsHeader* h, ErrClass c, int64_t row) {
   atomicOr(&h->err_bits, 1u << c);
@@ -48,9 +34,11 @@ __device__ __forceinline__ void record_error(WsHeader* h, ErrClass c, int64_t ro
 }
 
 // ---- launchers (each defined next to its kernels) --------------------------------
-struct ClassifyParams {
-  int64_t N, V, B, L, nseq;
-  int32_t layout, ids_i64;
+struct ScoreParams {
+  int64_t N, V, stride, L, nseq;
+  int32_t dtype, ids_i64, layout;
+  const void* train;
+  const void* rollout;
   const void* ids;
   const uint8_t* att;
   const uint8_t* act;
@@ -61,28 +49,27 @@ struct ClassifyParams {
   uint8_t* active;
   char* ws;
 };
-hipError_t launch_classify(const ClassifyParams& p, hipStream_t s);
-
-struct ScoreParams {
-  int64_t N, V, stride;
-  int32_t dtype, ids_i64;
-  const void* train;
-  const void* rollout;
-  const void* ids;
-  float* out_t;
-  float* out_r;
-  float* out_d;
-  char* ws;
-};
-hipError_t launch_score(const ScoreParams& p, hipStream_t s);
+// Launches the header initialisation and the scoring kernel; `ev` (nullable) are recorded
+// right before and after the scoring kernel.
+hipError_t launch_score(const ScoreParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 
 struct DiagParams {
   int64_t N;
   double eps_low, eps_high;
   const float* d;
   const uint8_t* active;
+  const WsHeader* lp;  // nullable: header of the drift_selected_logprob call that made d
   char* ws;
 };
+
+// Status recorded in a logprob workspace header (priority mask > token > non-finite).
+__host__ __device__ inline int header_status(uint32_t magic, uint32_t err_bits) {
+  if (magic != kWsMagic) return DRIFT_EWORKSPACE;
+  if (err_bits & (1u << kErrMask)) return DRIFT_EMASK;
+  if (err_bits & (1u << kErrToken)) return DRIFT_ETOKEN;
+  if (err_bits & (1u << kErrNonfinite)) return DRIFT_ENONFINITE;
+  return DRIFT_OK;
+}
 size_t diag_ws_bytes(int64_t N);
 size_t diag_stats_offset();
 hipError_t launch_diagnostics(const DiagParams& p, hipStream_t s);

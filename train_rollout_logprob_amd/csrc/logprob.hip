@@ -8,10 +8,13 @@
 // Arithmetic (precision and downcast points, "[WS2] Framework for ablation experiment",
 // LogProb knobs row 6):
 //   * stored logits (fp32, or bf16 widened exactly) are read as fp32;
-//   * each lane keeps (k, s): k an integer-valued float, a power-of-two running maximum
-//     k = ceil(max_i x_i * log2e); s = sum_i 2^(x_i*log2e - k) in fp64. A vector of
-//     16 bytes of logits contributes fp32 terms exp2(fma(x, log2e, -k)) summed in fp32,
-//     then added to s in fp64. Raising k rescales s by an exact power of two (ldexp);
+//   * each lane keeps (k, s) with s = sum_i 2^(x_i*log2e - k) in fp64 and k an integer
+//     shared by the 64 lanes of a wave: a power-of-two running maximum. A group of 16
+//     bytes of logits contributes fp32 terms exp2(fma(x, log2e, -k)) summed in fp32,
+//     then added to s in fp64. When some lane's group sum reaches 16 (a term above 2^4,
+//     the first group, or a non-finite logit) the wave raises k to ceil(max x * log2e)
+//     over the wave's group and rescales s by an exact power of two (ldexp). Terms
+//     therefore never exceed 2^4 and the running maximum costs one compare per group;
 //   * lanes, waves and the block merge (k, s) pairs in a fixed order; the online
 //     softmax tiling of LogProb knobs row 10 with the merge in a fixed global order of
 //     row 5. The element -> lane -> wave mapping depends only on V and the compile-time
@@ -23,6 +26,7 @@
 // The selected logit is read once by its single owner (LogProb knobs row 8).
 #include <math.h>
 
+#include "classify.h"
 #include "common.h"
 
 namespace drift {
@@ -54,38 +58,58 @@ __device__ __forceinline__ Acc merge(const Acc& a, const Acc& b) {
   return r;
 }
 
-// Adds one group of VEC logits to a lane's partial, in a fixed order.
+constexpr float kRaise = 16.0f;  // a group sum at or above this raises the wave's k
+
 template <int VEC>
-__device__ __forceinline__ void push(Acc& a, const float (&x)[VEC]) {
-  float m = x[0];
-#pragma unroll
-  for (int i = 1; i < VEC; ++i) m = fmaxf(m, x[i]);
-  const float kn = ceilf(m * kLog2e);
-  if (kn > a.k) {
-    if (kn == INFINITY) {
-      a.s = NAN;  // +inf logit, or |x| too large for the fp32 exponent: fail closed
-    } else {
-      a.s = rescale(a.s, a.k, kn);
-      a.k = kn;
-    }
-  }
+__device__ __forceinline__ float group_sum(const float (&x)[VEC], float nk) {
   float e[VEC];
-  if (a.k == -INFINITY) {
-    // Every logit seen so far is -inf (probability zero) or NaN.
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) e[i] = (x[i] == -INFINITY) ? 0.0f : NAN;
-  } else {
-    const float nk = -a.k;
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(x[i], kLog2e, nk));
-  }
-  // pairwise fp32 sum of the group, then one fp64 add
+  for (int i = 0; i < VEC; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(x[i], kLog2e, nk));
+  // pairwise fp32 sum of the group
 #pragma unroll
   for (int w = 1; w < VEC; w *= 2) {
 #pragma unroll
     for (int i = 0; i + w < VEC; i += 2 * w) e[i] = e[i] + e[i + w];
   }
-  a.s += (double)e[0];
+  return e[0];
+}
+
+__device__ __forceinline__ float wave_max(float m) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  return m;
+}
+
+// Adds one group of VEC logits to a lane's partial. Every lane of the wave calls it at
+// the same point (groups past the end of the row are all -inf), so k stays wave-uniform.
+template <int VEC>
+__device__ __forceinline__ void push(Acc& a, const float (&x)[VEC]) {
+  float t = group_sum<VEC>(x, -a.k);
+  if (__ballot(!(t < kRaise))) {  // wave-uniform: raise k
+    float m = x[0];
+#pragma unroll
+    for (int i = 1; i < VEC; ++i) m = fmaxf(m, x[i]);
+    m = wave_max(m);  // NaN-ignoring; -inf if every logit in the wave's group is -inf/NaN
+    const float kn = ceilf(m * kLog2e);
+    if (kn > a.k) {
+      if (kn == INFINITY) {
+        a.s = NAN;  // +inf logit, or |x| too large for the fp32 exponent: fail closed
+      } else {
+        a.s = rescale(a.s, a.k, kn);
+        a.k = kn;
+      }
+    }
+    if (a.k == -INFINITY) {
+      // every logit seen so far by the wave is -inf (probability zero) or NaN
+      t = 0.0f;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i)
+        if (!(x[i] == -INFINITY)) t = NAN;
+    } else {
+      t = group_sum<VEC>(x, -a.k);
+    }
+  }
+  a.s += (double)t;
 }
 
 template <typename T> struct Elem;
@@ -116,30 +140,30 @@ template <> struct Elem<uint16_t> {  // bf16 bit patterns
   }
 };
 
-__device__ __forceinline__ int64_t load_id(const void* ids, int64_t r, int32_t i64) {
-  return i64 ? ((const int64_t*)ids)[r] : (int64_t)((const int32_t*)ids)[r];
-}
-
-// Lane `tid` owns the 16-byte groups v = tid, tid + NT, tid + 2NT, ... of the row and
+// Lane `tid` owns the 16-byte groups g = tid, tid + NT, tid + 2NT, ... of the row and
 // pushes them in ascending order; the last partial group (V % VEC logits, padded with
-// -inf) belongs to the lane that would own group V / VEC. U groups per side are loaded
-// ahead for memory-level parallelism; U does not change the arithmetic.
+// -inf) belongs to the lane that would own group V / VEC. All lanes run the same number
+// of pushes (missing groups are all -inf and add exactly 0). U groups per side are
+// loaded ahead for memory-level parallelism; U does not change the arithmetic.
 template <typename T, int NT, int U, bool kAligned>
-__device__ __forceinline__ void stream_row(const void* rt, const void* rr, int64_t V, int tid,
+__device__ __forceinline__ void stream_row(const char* rt, const char* rr, int64_t V, int tid,
                                            Acc& at, Acc& ar) {
   constexpr int VEC = Elem<T>::kVec;
-  const int64_t nvec = V / VEC;
-  int64_t v = tid;
+  const int64_t nfull = V / VEC;                      // complete groups
+  const int64_t ngroups = (V + VEC - 1) / VEC;        // including the ragged one
+  const int64_t full_iters = nfull / NT;              // iterations where every lane is full
+  const int64_t iters = (ngroups + NT - 1) / NT;
+  int64_t j = 0;
   if constexpr (kAligned) {
     const u32x4* vt = (const u32x4*)rt;
     const u32x4* vr = (const u32x4*)rr;
-    const int64_t nround = nvec / ((int64_t)NT * U);
-    for (int64_t it = 0; it < nround; ++it) {
+    for (; j + U <= full_iters; j += U) {
       u32x4 bt[U], br[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        bt[u] = __builtin_nontemporal_load(vt + v + u * NT);
-        br[u] = __builtin_nontemporal_load(vr + v + u * NT);
+        const int64_t g = (j + u) * NT + tid;
+        bt[u] = __builtin_nontemporal_load(vt + g);
+        br[u] = __builtin_nontemporal_load(vr + g);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -149,66 +173,92 @@ __device__ __forceinline__ void stream_row(const void* rt, const void* rr, int64
         Elem<T>::unpack(br[u], x);
         push<VEC>(ar, x);
       }
-      v += (int64_t)NT * U;
-    }
-    for (; v < nvec; v += NT) {
-      const u32x4 bt = __builtin_nontemporal_load(vt + v);
-      const u32x4 br = __builtin_nontemporal_load(vr + v);
-      float x[VEC];
-      Elem<T>::unpack(bt, x);
-      push<VEC>(at, x);
-      Elem<T>::unpack(br, x);
-      push<VEC>(ar, x);
-    }
-  } else {
-    for (; v < nvec; v += NT) {
-      float xt[VEC], xr[VEC];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        xt[e] = Elem<T>::load1(rt, v * VEC + e);
-        xr[e] = Elem<T>::load1(rr, v * VEC + e);
-      }
-      push<VEC>(at, xt);
-      push<VEC>(ar, xr);
     }
   }
-  if (v == nvec && nvec * VEC < V) {  // the ragged tail group
+  for (; j < iters; ++j) {
+    const int64_t g = j * NT + tid;
     float xt[VEC], xr[VEC];
+    if (kAligned && g < nfull) {
+      Elem<T>::unpack(__builtin_nontemporal_load((const u32x4*)rt + g), xt);
+      Elem<T>::unpack(__builtin_nontemporal_load((const u32x4*)rr + g), xr);
+    } else {
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      const int64_t i = nvec * VEC + e;
-      xt[e] = (i < V) ? Elem<T>::load1(rt, i) : -INFINITY;
-      xr[e] = (i < V) ? Elem<T>::load1(rr, i) : -INFINITY;
+      for (int e = 0; e < VEC; ++e) {
+        const int64_t i = g * VEC + e;
+        xt[e] = (i < V) ? Elem<T>::load1(rt, i) : -INFINITY;
+        xr[e] = (i < V) ? Elem<T>::load1(rr, i) : -INFINITY;
+      }
     }
     push<VEC>(at, xt);
     push<VEC>(ar, xr);
   }
 }
 
+// Header initialisation (and the packed-metadata check) before the scoring kernel.
+__global__ void __launch_bounds__(256) init_header(ScoreParams p) {
+  __shared__ uint32_t s_err;
+  WsHeader* h = (WsHeader*)p.ws;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_err = 0;
+  __syncthreads();
+  if (p.layout == DRIFT_PACKED) {  // cu_seqlens starts at 0, never decreases, ends inside
+    for (int64_t i = tid; i <= p.nseq; i += 256) {
+      const int64_t c = p.cu[i];
+      if ((i == 0 && c != 0) || (i > 0 && c < (int64_t)p.cu[i - 1]) || c > p.N)
+        atomicOr(&s_err, 1u << kErrMask);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    h->err_bits = s_err;
+    h->magic = kWsMagic;
+    h->n_active = 0;
+    h->first_bad[kErrMask] = s_err ? 0ull : ~0ull;
+    h->first_bad[kErrToken] = ~0ull;
+    h->first_bad[kErrNonfinite] = ~0ull;
+    h->first_bad[3] = ~0ull;
+  }
+}
+
+// One block per row: thread 0 classifies and validates the row; active rows with a valid
+// id are streamed by the whole block.
 template <typename T, int NT, int U>
 __global__ void __launch_bounds__(NT) score_rows(ScoreParams p) {
   constexpr int NW = NT / 64;
   __shared__ float s_k[2][NW];
   __shared__ double s_s[2][NW];
+  __shared__ int64_t s_y;
   WsHeader* h = (WsHeader*)p.ws;
-  const int64_t i = blockIdx.x;
-  if (i >= h->n_active) return;
-  const int32_t* rows = (const int32_t*)(p.ws + LogprobWs::make(p.N).rows_off);
-  const int64_t r = rows[i];
-  const int64_t y = load_id(p.ids, r, p.ids_i64);
+  const int64_t r = blockIdx.x;
   const int tid = threadIdx.x;
-  if (y < 0 || y >= p.V) {  // recorded as a token error by the classification pass
-    if (tid == 0) {
+  if (tid == 0) {
+    int64_t end = p.N;
+    if (p.layout == DRIFT_PACKED) {
+      end = (int64_t)p.cu[p.nseq];
+      end = end < 0 ? 0 : (end > p.N ? p.N : end);
+    }
+    const RowClass c = classify_row(p, r, end);
+    p.active[r] = c.active ? 1 : 0;
+    if (c.err & (1u << kErrMask)) record_error(h, kErrMask, r);
+    if (c.err & (1u << kErrToken)) record_error(h, kErrToken, r);
+    if (!c.active) {
+      p.out_t[r] = 0.0f;
+      p.out_r[r] = 0.0f;
+      p.out_d[r] = 0.0f;
+    } else if (!c.score) {
       p.out_t[r] = NAN;
       p.out_r[r] = NAN;
       p.out_d[r] = NAN;
     }
-    return;
+    s_y = c.score ? c.y : -1;
   }
+  __syncthreads();
+  const int64_t y = s_y;
+  if (y < 0) return;  // block-uniform
+
   const size_t off = (size_t)r * (size_t)p.stride * sizeof(T);
   const char* rt = (const char*)p.train + off;
   const char* rr = (const char*)p.rollout + off;
-
   Acc at = {-INFINITY, 0.0}, ar = {-INFINITY, 0.0};
   if ((((uintptr_t)rt | (uintptr_t)rr) & 15) == 0) {
     stream_row<T, NT, U, true>(rt, rr, p.V, tid, at, ar);
@@ -216,7 +266,7 @@ __global__ void __launch_bounds__(NT) score_rows(ScoreParams p) {
     stream_row<T, NT, U, false>(rt, rr, p.V, tid, at, ar);
   }
 
-  // wave butterfly, then waves in index order
+  // lanes (fixed butterfly), then waves in index order
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     Acc bt, br;
@@ -255,20 +305,46 @@ __global__ void __launch_bounds__(NT) score_rows(ScoreParams p) {
   }
 }
 
-constexpr int kScoreThreads = 256;
-constexpr int kScoreUnroll = 4;
+// Block shapes of the scoring kernel, per logits dtype (measured on MI355X: bf16 rows
+// stream best with 256 threads x 8 groups in flight, fp32 rows with 512 x 4). The
+// per-row reduction tree depends on the block width, so a build fixes it once; the unroll
+// depth only changes load scheduling.
+#ifndef DRIFT_SCORE_THREADS_BF16
+#define DRIFT_SCORE_THREADS_BF16 256
+#endif
+#ifndef DRIFT_SCORE_UNROLL_BF16
+#define DRIFT_SCORE_UNROLL_BF16 8
+#endif
+#ifndef DRIFT_SCORE_THREADS_F32
+#define DRIFT_SCORE_THREADS_F32 512
+#endif
+#ifndef DRIFT_SCORE_UNROLL_F32
+#define DRIFT_SCORE_UNROLL_F32 4
+#endif
+static_assert(DRIFT_SCORE_THREADS_BF16 % 64 == 0 && DRIFT_SCORE_THREADS_BF16 <= 1024, "shape");
+static_assert(DRIFT_SCORE_THREADS_F32 % 64 == 0 && DRIFT_SCORE_THREADS_F32 <= 1024, "shape");
 
 }  // namespace
 
-hipError_t launch_score(const ScoreParams& p, hipStream_t s) {
-  if (p.N <= 0) return hipSuccess;
-  const dim3 grid((unsigned)p.N), block(kScoreThreads);
-  if (p.dtype == DRIFT_BF16) {
-    hipLaunchKernelGGL((score_rows<uint16_t, kScoreThreads, kScoreUnroll>), grid, block, 0, s, p);
-  } else {
-    hipLaunchKernelGGL((score_rows<float, kScoreThreads, kScoreUnroll>), grid, block, 0, s, p);
+hipError_t launch_score(const ScoreParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  hipLaunchKernelGGL(init_header, dim3(1), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
+  if (p.N > 0) {
+    const dim3 grid((unsigned)p.N);
+    if (p.dtype == DRIFT_BF16) {
+      hipLaunchKernelGGL(
+          (score_rows<uint16_t, DRIFT_SCORE_THREADS_BF16, DRIFT_SCORE_UNROLL_BF16>), grid,
+          dim3(DRIFT_SCORE_THREADS_BF16), 0, s, p);
+    } else {
+      hipLaunchKernelGGL((score_rows<float, DRIFT_SCORE_THREADS_F32, DRIFT_SCORE_UNROLL_F32>),
+                         grid, dim3(DRIFT_SCORE_THREADS_F32), 0, s, p);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  return hipGetLastError();
+  if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
+  return hipSuccess;
 }
 
 }  // namespace drift
