@@ -20,6 +20,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "active tokens/sec + logits HBM GB/s (% of peak) for paired logprob+drift"
 WORKLOAD_TEXT = {
     "qwen8b": "qwen8b-shaped paired scoring: bf16 logits, V=151936, B=8, L=2048 "
@@ -59,6 +60,40 @@ def cpu_baseline(case, budget_s):
                       f"numpy fp64 two-pass log-sum-exp, one process, {spent:.1f} s"}
 
 
+def lmhead_leg(steps=5, warmup=2):
+    """Fused LM-head workload (hidden [16384, 4096] x W [4096, 151936], bf16): the whole
+    drift_lmhead_logprob call timed with events on the launch stream."""
+    import torch
+
+    from train_rollout_logprob_amd import binding as B
+    from train_rollout_logprob_amd import synth
+
+    case = synth.make_lmhead_case(device="cuda:0")
+    ids = torch.as_tensor(case.ids, device="cuda:0")
+    ws = B.workspace(B.DRIFT_OP_LMHEAD, case.T, case.V, B.DRIFT_BF16, "cuda:0",
+                     hidden_dim=case.H)
+    out = torch.empty(case.T, dtype=torch.float32, device="cuda:0")
+    for _ in range(warmup):
+        B.lmhead_logprob(case.hidden, case.weight, ids, ws=ws, out=out)
+    st, _ = B.drift_get_status(ws)
+    if st != B.DRIFT_OK:
+        raise RuntimeError(f"lmhead status {B.STATUS_NAMES[st]}")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        B.lmhead_logprob(case.hidden, case.weight, ids, ws=ws, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flop = 2.0 * case.T * case.H * case.V
+    tflops = flop / (ms * 1e-3) / 1e12
+    return {"workload": f"fused LM-head: hidden [{case.T}, {case.H}] x W [{case.H}, {case.V}] "
+                        f"bf16, fp32 accumulation", "ms_per_call": ms,
+            "active_tokens_per_s": case.T / (ms * 1e-3), "tflops": tflops,
+            "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS, "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+            "flop_per_call": flop}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -66,8 +101,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="qwen8b", choices=["qwen8b", "large", "packed", "tiny"],
+    ap.add_argument("--workload", default="qwen8b",
+                    choices=["qwen8b", "large", "packed", "tiny", "lmhead"],
                     help="scoring workload (the benchmark line is quoted on qwen8b)")
+    ap.add_argument("--no-lmhead", action="store_true",
+                    help="skip the fused LM-head leg reported beside the main line")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
                     help="copy: a plain device copy of known size, to calibrate HBM counters")
     ap.add_argument("--copy-mib", type=int, default=4096)
@@ -94,6 +132,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"[bench] copied {n} bytes 3 times (read {n} and write {n} per copy)")
+        return
+    if args.workload == "lmhead":
+        print(json.dumps(lmhead_leg(args.steps, args.warmup)), flush=True)
         return
     log(f"[bench] generating the {args.workload} workload")
     case = synth.make_logits_case(args.workload, device=dev)
@@ -171,6 +212,11 @@ def main():
                      "bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
     }
+    if not args.no_lmhead and args.workload == "qwen8b":
+        del runner, case
+        torch.cuda.empty_cache()
+        log("[bench] fused LM-head leg")
+        line["lmhead"] = lmhead_leg()
     print(json.dumps(line), flush=True)
 
 

@@ -168,8 +168,10 @@ typedef struct drift_backend_desc {
 } drift_backend_desc;
 
 /* Workspace bytes for `op` over `num_rows` rows of `vocab` columns of element type
- * `dtype` (DRIFT_OP_LMHEAD: num_rows = T). Returns 0 for invalid arguments. Host only. */
-size_t drift_workspace_size(int op, int64_t num_rows, int64_t vocab, int dtype);
+ * `dtype`; `hidden_dim` is H for DRIFT_OP_LMHEAD (num_rows = T there) and ignored
+ * otherwise. Returns 0 for invalid arguments. Host only. */
+size_t drift_workspace_size(int op, int64_t num_rows, int64_t vocab, int64_t hidden_dim,
+                            int dtype);
 
 /* Per-row selected-token logprobs of both sides and their drift
  * ("Measurement Contract"). Outputs, each [N] device arrays:

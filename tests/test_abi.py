@@ -52,7 +52,7 @@ def test_descriptor_and_strerror():
 
 def test_workspace_sizes():
     from train_rollout_logprob_amd import binding as B
-    f = B.drift_workspace_size
+    f = lambda op, n, v, dt, h=0: B.drift_workspace_size(op, n, v, h, dt)
     assert f(B.DRIFT_OP_SELECTED_LOGPROB, 16384, 151936, B.DRIFT_BF16) == 256   # header only
     assert f(B.DRIFT_OP_SELECTED_LOGPROB, 0, 1, B.DRIFT_F32) >= 256
     assert f(B.DRIFT_OP_SELECTED_LOGPROB, 10, 0, B.DRIFT_F32) == 0      # V < 1
@@ -60,7 +60,10 @@ def test_workspace_sizes():
     assert f(B.DRIFT_OP_SELECTED_LOGPROB, 1 << 31, 5, B.DRIFT_F32) == 0
     assert f(B.DRIFT_OP_SELECTED_LOGPROB, 10, 5, 7) == 0                # bad dtype
     assert f(B.DRIFT_OP_DIAGNOSTICS, 270000, 1, B.DRIFT_F32) > 0
-    assert f(B.DRIFT_OP_LMHEAD, 16384, 151936, B.DRIFT_F32) == 0        # bf16 only
+    assert f(B.DRIFT_OP_LMHEAD, 16384, 151936, B.DRIFT_F32, 4096) == 0  # bf16 only
+    assert f(B.DRIFT_OP_LMHEAD, 16384, 151936, B.DRIFT_BF16, 4100) == 0 # H % 8
+    # transposed W + partials: at least H*V*2 bytes
+    assert f(B.DRIFT_OP_LMHEAD, 16384, 151936, B.DRIFT_BF16, 4096) >= 4096 * 151936 * 2
     assert f(9, 10, 10, B.DRIFT_F32) == 0
 
 

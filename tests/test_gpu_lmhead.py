@@ -1,0 +1,115 @@
+"""GPU parity of drift_lmhead_logprob (fused hidden x W_vocab + log-softmax gather)
+against the fp64 oracle, and the batch-composition bitwise control: the same rows
+re-scored inside batches of 1, 7 and 64 rows give bitwise the full-batch result."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import LOGP_TOL, status_name
+from train_rollout_logprob_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+
+
+def _bits(t):
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def _oracle(case, rows):
+    w64 = oracle.widen(_bits(case.weight), "bf16").reshape(case.H, case.V)
+    return oracle.lmhead_logprob(_bits(case.hidden), w64, case.ids, rows=rows)
+
+
+@pytest.mark.parametrize("T,H,V", [(300, 264, 1000), (128, 64, 128), (1, 8, 8), (77, 520, 4104)])
+def test_parity_ragged_shapes(T, H, V):
+    from train_rollout_logprob_amd import binding as B
+    print(f"[case] lmhead T={T} H={H} V={V}", flush=True)
+    case = synth.make_lmhead_case(device="cuda", T=T, H=H, V=V)
+    ids = torch.as_tensor(case.ids, device="cuda")
+    logp, ws = B.lmhead_logprob(case.hidden, case.weight, ids, check=True)
+    want = _oracle(case, None)
+    err = np.abs(logp.cpu().numpy().astype(np.float64) - want)
+    print(f"[case] max err {err.max():.3e}", flush=True)
+    assert err.max() <= LOGP_TOL
+
+
+def test_active_mask_and_token_errors():
+    from train_rollout_logprob_amd import binding as B
+    case = synth.make_lmhead_case(device="cuda", T=200, H=128, V=512)
+    ids = torch.as_tensor(case.ids, device="cuda")
+    act = torch.ones(200, dtype=torch.uint8, device="cuda")
+    act[::3] = 0
+    logp, ws = B.lmhead_logprob(case.hidden, case.weight, ids, act, check=True)
+    base, _ = B.lmhead_logprob(case.hidden, case.weight, ids)
+    a = act.cpu().numpy() == 1
+    assert np.all(logp.cpu().numpy()[~a] == 0.0)
+    assert np.array_equal(logp.cpu().numpy()[a], base.cpu().numpy()[a])
+    bad = ids.clone()
+    bad[5] = 512
+    logp, ws = B.lmhead_logprob(case.hidden, case.weight, bad)
+    st, row = B.drift_get_status(ws)
+    assert status_name(st) == "ETOKEN" and row == 5
+    assert np.isnan(logp[5].item())
+    bad[5] = -100
+    act[5] = 0                                       # an inactive row is never checked
+    logp, ws = B.lmhead_logprob(case.hidden, case.weight, bad, act, check=True)
+
+
+def test_batch_composition_control_is_bitwise_zero():
+    """Rows scored in the full batch, then inside batches of 1, 7 and 64 rows at other
+    positions (other rows drawn from the pool), are bitwise equal: dlogp == 0 exactly."""
+    from train_rollout_logprob_amd import binding as B
+    T, H, V = 2048, 1024, 16384
+    case = synth.make_lmhead_case(device="cuda", T=T, H=H, V=V)
+    ids = torch.as_tensor(case.ids, device="cuda")
+    full, _ = B.lmhead_logprob(case.hidden, case.weight, ids, check=True)
+    full = full.cpu().numpy()
+    rng = np.random.default_rng(11)
+    probe = [0, 5, 1000, T - 1]
+    for bs in (1, 7, 64):
+        for pr in probe:
+            rows = rng.integers(0, T, bs)
+            slot = int(rng.integers(0, bs))
+            rows[slot] = pr
+            idx = torch.as_tensor(rows, device="cuda")
+            h = case.hidden.index_select(0, idx).contiguous()
+            got, _ = B.lmhead_logprob(h, case.weight, ids.index_select(0, idx).contiguous(),
+                                      check=True)
+            g = np.float32(got[slot].item())
+            assert g.view(np.uint32) == full[pr].view(np.uint32), (bs, pr, g, full[pr])
+
+
+@pytest.mark.slow
+def test_full_size_sampled_rows_and_invariance():
+    """T=16384, H=4096, V=151936 as timed: sampled rows against the oracle, and four rows
+    (including the first and the last) re-scored in batches of 1, 7 and 64."""
+    from train_rollout_logprob_amd import binding as B
+    case = synth.make_lmhead_case(device="cuda")
+    ids = torch.as_tensor(case.ids, device="cuda")
+    logp, ws = B.lmhead_logprob(case.hidden, case.weight, ids, check=True)
+    full = logp.cpu().numpy()
+    rng = np.random.default_rng(12)
+    rows = np.unique(np.concatenate([[0, case.T - 1], rng.integers(0, case.T, 14)]))
+    want = _oracle(case, rows)
+    err = np.abs(full[rows].astype(np.float64) - want)
+    print(f"[case] lmhead full max err {err.max():.3e} over {len(rows)} rows", flush=True)
+    assert err.max() <= LOGP_TOL
+    probe = [0, 1234, 9999, case.T - 1]
+    for bs in (1, 7, 64):
+        for pr in probe:
+            rr = rng.integers(0, case.T, bs)
+            slot = int(rng.integers(0, bs))
+            rr[slot] = pr
+            idx = torch.as_tensor(rr, device="cuda")
+            got, _ = B.lmhead_logprob(case.hidden.index_select(0, idx).contiguous(),
+                                      case.weight, ids.index_select(0, idx).contiguous(),
+                                      check=True)
+            g = np.float32(got[slot].item())
+            assert g.view(np.uint32) == full[pr].view(np.uint32), (bs, pr)

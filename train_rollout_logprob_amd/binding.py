@@ -76,7 +76,7 @@ def _load():
                           f"__graft_entry__ as g; g.build()'` (no CPU fallback exists)")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
-    lib.drift_workspace_size.argtypes = [ctypes.c_int, i64, i64, ctypes.c_int]
+    lib.drift_workspace_size.argtypes = [ctypes.c_int, i64, i64, i64, ctypes.c_int]
     lib.drift_workspace_size.restype = sz
     lib.drift_selected_logprob.argtypes = [ctypes.POINTER(drift_logprob_args), vp, vp, vp, vp,
                                            vp, sz, vp]
@@ -100,8 +100,8 @@ lib = _load()
 
 # ----------------------------------------------------------------------------- C names
 
-def drift_workspace_size(op: int, num_rows: int, vocab: int, dtype: int) -> int:
-    return int(lib.drift_workspace_size(op, num_rows, vocab, dtype))
+def drift_workspace_size(op: int, num_rows: int, vocab: int, hidden_dim: int, dtype: int) -> int:
+    return int(lib.drift_workspace_size(op, num_rows, vocab, hidden_dim, dtype))
 
 
 def drift_selected_logprob(args: drift_logprob_args, train_logp, rollout_logp, dlogp, active,
@@ -171,8 +171,9 @@ class DriftError(RuntimeError):
                          f"({drift_strerror(status)})")
 
 
-def workspace(op: int, num_rows: int, vocab: int, dtype: int, device) -> torch.Tensor:
-    n = drift_workspace_size(op, num_rows, vocab, dtype)
+def workspace(op: int, num_rows: int, vocab: int, dtype: int, device, hidden_dim: int = 0
+              ) -> torch.Tensor:
+    n = drift_workspace_size(op, num_rows, vocab, hidden_dim, dtype)
     if n == 0:
         raise DriftError(DRIFT_EINVAL, "drift_workspace_size")
     return torch.empty(n, dtype=torch.uint8, device=device)
@@ -289,3 +290,29 @@ class ScoringStep:
         if st != DRIFT_OK:
             raise DriftError(st, "drift_selected_logprob")
         return lib.drift_diagnostics(*self._dg_args)
+
+
+def lmhead_logprob(hidden, weight, ids, active=None, ws=None, out=None, stream=None,
+                   check=False):
+    """Call drift_lmhead_logprob on torch tensors: hidden bf16 [T, H], weight bf16 [H, V],
+    ids int32 [T], active uint8 [T] or None. Returns (logp, ws)."""
+    T, H = hidden.shape
+    H2, V = weight.shape
+    if H2 != H or hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise ValueError("hidden [T, H] and weight [H, V] must be bf16 with matching H")
+    if not (hidden.is_contiguous() and weight.is_contiguous() and ids.is_contiguous()):
+        raise ValueError("hidden, weight and ids must be contiguous")
+    if ids.dtype != torch.int32:
+        raise ValueError("ids must be int32")
+    if ws is None:
+        ws = workspace(DRIFT_OP_LMHEAD, T, V, DRIFT_BF16, hidden.device, hidden_dim=H)
+    if out is None:
+        out = torch.empty(T, dtype=torch.float32, device=hidden.device)
+    st = drift_lmhead_logprob(hidden, weight, T, H, V, ids, active, out, ws, ws.numel(), stream)
+    if st != DRIFT_OK:
+        raise DriftError(st, "drift_lmhead_logprob")
+    if check:
+        st, _ = drift_get_status(ws, stream)
+        if st != DRIFT_OK:
+            raise DriftError(st, "drift_lmhead_logprob (device)")
+    return out, ws

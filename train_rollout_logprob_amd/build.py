@@ -15,7 +15,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdrift.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 SOURCES = ["api.hip", "logprob.hip", "diagnostics.hip", "lmhead.hip"]
-HEADERS = ["common.h", "classify.h"]
+HEADERS = ["common.h", "classify.h", "lse.h"]
 
 ARCH = "gfx950"
 FLAGS = [

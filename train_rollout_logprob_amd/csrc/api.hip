@@ -29,7 +29,8 @@ int status_from_header(const WsHeader& h, int64_t* first_bad) {
 
 extern "C" {
 
-size_t drift_workspace_size(int op, int64_t num_rows, int64_t vocab, int dtype) {
+size_t drift_workspace_size(int op, int64_t num_rows, int64_t vocab, int64_t hidden_dim,
+                            int dtype) {
   if (num_rows < 0 || num_rows > INT32_MAX || vocab < 1) return 0;
   switch (op) {
     case DRIFT_OP_SELECTED_LOGPROB:
@@ -38,8 +39,8 @@ size_t drift_workspace_size(int op, int64_t num_rows, int64_t vocab, int dtype) 
     case DRIFT_OP_DIAGNOSTICS:
       return diag_ws_bytes(num_rows);
     case DRIFT_OP_LMHEAD:
-      if (dtype != DRIFT_BF16) return 0;
-      return lmhead_ws_bytes(num_rows, vocab);
+      if (dtype != DRIFT_BF16 || hidden_dim < 1 || hidden_dim % 8 || vocab % 8) return 0;
+      return lmhead_ws_bytes(num_rows, hidden_dim, vocab);
     default:
       return 0;
   }
@@ -149,7 +150,7 @@ int drift_lmhead_logprob(const void* hidden, const void* weight, int64_t T, int6
   if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(target_ids, 4) ||
       !aligned(logp, 4))
     return DRIFT_EINVAL;
-  if (!ws || !aligned(ws, 256) || ws_bytes < lmhead_ws_bytes(T, V)) return DRIFT_EWORKSPACE;
+  if (!ws || !aligned(ws, 256) || ws_bytes < lmhead_ws_bytes(T, H, V)) return DRIFT_EWORKSPACE;
   LmheadParams lp;
   lp.T = T;
   lp.H = H;

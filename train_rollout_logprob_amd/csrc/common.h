@@ -83,7 +83,7 @@ struct LmheadParams {
   float* logp;
   char* ws;
 };
-size_t lmhead_ws_bytes(int64_t T, int64_t V);
+size_t lmhead_ws_bytes(int64_t T, int64_t H, int64_t V);
 hipError_t launch_lmhead(const LmheadParams& p, hipStream_t s);
 
 }  // namespace drift

@@ -28,35 +28,12 @@
 
 #include "classify.h"
 #include "common.h"
+#include "lse.h"
 
 namespace drift {
 namespace {
 
-constexpr float kLog2e = 1.44269504088896340736f;      // log2(e), rounded to fp32
-constexpr double kLn2 = 0.693147180559945309417232121458;  // ln(2), rounded to fp64
-
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-struct Acc {
-  float k;   // -inf while empty, else an integer
-  double s;  // sum of 2^(x*log2e - k); 0 or NaN while empty
-};
-
-__device__ __forceinline__ double rescale(double s, float k, float K) {
-  // s * 2^(k - K) for k <= K; empty partials keep their 0 (or NaN).
-  return (k == -INFINITY) ? s : ldexp(s, (int)fmaxf(k - K, -2048.0f));
-}
-
-__device__ __forceinline__ Acc merge(const Acc& a, const Acc& b) {
-  Acc r;
-  r.k = fmaxf(a.k, b.k);
-  if (r.k == -INFINITY) {
-    r.s = a.s + b.s;
-  } else {
-    r.s = rescale(a.s, a.k, r.k) + rescale(b.s, b.k, r.k);
-  }
-  return r;
-}
 
 constexpr float kRaise = 16.0f;  // a group sum at or above this raises the wave's k
 
@@ -294,13 +271,12 @@ __global__ void __launch_bounds__(NT) score_rows(ScoreParams p) {
     }
     const float xty = Elem<T>::load1(rt, y);
     const float xry = Elem<T>::load1(rr, y);
-    const double lse_t = ((double)T_.k + log2(T_.s)) * kLn2;
-    const double lse_r = ((double)R_.k + log2(R_.s)) * kLn2;
+    const double lse_t = lse_of(T_);
+    const double lse_r = lse_of(R_);
     p.out_t[r] = (float)((double)xty - lse_t);
     p.out_r[r] = (float)((double)xry - lse_r);
     p.out_d[r] = (float)(((double)xty - (double)xry) - (lse_t - lse_r));
-    const bool ok = (T_.s > 0.0) && (T_.s < INFINITY) && (R_.s > 0.0) && (R_.s < INFINITY) &&
-                    (xty > -INFINITY) && (xry > -INFINITY);
+    const bool ok = lse_ok(T_) && lse_ok(R_) && (xty > -INFINITY) && (xry > -INFINITY);
     if (!ok) record_error(h, kErrNonfinite, r);
   }
 }

@@ -1,0 +1,46 @@
+// Log-sum-exp partials in the power-of-two form used by every kernel of the library.
+//
+// A partial (k, s) stands for 2^k * s = sum_i exp(x_i) / e^0 over the logits it covers,
+// with s = sum_i 2^(x_i*log2e - k) accumulated in fp64 and k an integer-valued float
+// (-inf while empty). Merging rescales by exact powers of two (ldexp), so the only
+// roundings are the fp64 adds; merges happen in a fixed order chosen by each kernel (the
+// online-softmax merge of "[WS2] Framework for ablation experiment", LogProb knobs rows 5
+// and 10, and Attention knobs row 7). LSE is exported in the natural-log domain:
+// lse = (k + log2 s) * ln2 (Attention knobs row 6).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+namespace drift {
+
+constexpr float kLog2e = 1.44269504088896340736f;          // log2(e), rounded to fp32
+constexpr double kLn2 = 0.693147180559945309417232121458;  // ln(2), rounded to fp64
+
+struct Acc {
+  float k;   // -inf while empty, else an integer
+  double s;  // sum of 2^(x*log2e - k); 0 or NaN while empty
+};
+
+__device__ __forceinline__ double rescale(double s, float k, float K) {
+  // s * 2^(k - K) for k <= K; empty partials keep their 0 (or NaN).
+  return (k == -INFINITY) ? s : ldexp(s, (int)fmaxf(k - K, -2048.0f));
+}
+
+__device__ __forceinline__ Acc merge(const Acc& a, const Acc& b) {
+  Acc r;
+  r.k = fmaxf(a.k, b.k);
+  if (r.k == -INFINITY) {
+    r.s = a.s + b.s;
+  } else {
+    r.s = rescale(a.s, a.k, r.k) + rescale(b.s, b.k, r.k);
+  }
+  return r;
+}
+
+__device__ __forceinline__ double lse_of(const Acc& a) { return ((double)a.k + log2(a.s)) * kLn2; }
+
+// A finite, non-empty partial (some logit finite, none NaN or +inf).
+__device__ __forceinline__ bool lse_ok(const Acc& a) { return a.s > 0.0 && a.s < INFINITY; }
+
+}  // namespace drift
