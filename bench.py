@@ -33,6 +33,40 @@ WORKLOAD_TEXT = {
 }
 
 
+SCORE_SOURCES = ("logprob.hip", "classify.h", "lse.h", "common.h")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "score_rows_bf16_qwen8b.md")
+
+
+def score_source_hash():
+    """Hash of the scoring kernel's sources, to tie a recorded counter reading to them."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in SCORE_SOURCES:
+        with open(os.path.join(ROOT, "train_rollout_logprob_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the scoring kernel from the committed PMC summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated on a copy of known size), or None when the
+    kernel's sources changed since the counters were taken."""
+    try:
+        vals = {}
+        with open(TRAFFIC_PROFILE) as fh:
+            for line in fh:
+                if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch",
+                                                          "traffic_sources"):
+                    k, v = line.split(":", 1)
+                    vals[k] = v.strip()
+        if vals.get("traffic_sources") != score_source_hash():
+            return None
+        return float(vals["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -207,7 +241,8 @@ def main():
                    "parallelism": "single GPU"},
         "logits_gbs": alg_bytes * args.steps / elapsed / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": recorded_traffic() if args.workload == "qwen8b" else None,
                      "kernel": f"score_rows<{case.dtype}>", "kernel_ms": kern_avg,
                      "bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
