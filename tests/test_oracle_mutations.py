@@ -35,21 +35,41 @@ MUTATIONS = [
 ]
 
 
-@pytest.mark.parametrize("fname,old,new", MUTATIONS, ids=[f"{m[0]}:{i}" for i, m in enumerate(MUTATIONS)])
-def test_pins_catch_planted_mistake(tmp_path, fname, old, new):
-    dst = tmp_path / "oracle"
+def _run_mutation(tmp_root, idx, fname, old, new):
+    tmp_path = os.path.join(tmp_root, f"m{idx}")
+    os.makedirs(tmp_path)
+    dst = os.path.join(tmp_path, "oracle")
     shutil.copytree(os.path.join(ROOT, "oracle"), dst,
                     ignore=shutil.ignore_patterns("__pycache__"))
-    path = dst / fname
-    src = path.read_text()
-    assert src.count(old) == 1, f"mutation anchor not found once: {old!r}"
-    path.write_text(src.replace(old, new))
+    path = os.path.join(dst, fname)
+    src = open(path).read()
+    if src.count(old) != 1:
+        return f"mutation anchor not found once: {old!r}"
+    open(path, "w").write(src.replace(old, new))
     for t in PIN_TESTS:
-        shutil.copy(os.path.join(ROOT, t), tmp_path / os.path.basename(t))
-    shutil.copytree(os.path.join(ROOT, "tests", "golden"), tmp_path / "golden")
+        shutil.copy(os.path.join(ROOT, t), os.path.join(tmp_path, os.path.basename(t)))
+    shutil.copytree(os.path.join(ROOT, "tests", "golden"), os.path.join(tmp_path, "golden"))
     env = dict(os.environ, PYTHONPATH=f"{tmp_path}{os.pathsep}{ROOT}")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "--rootdir", str(tmp_path)] +
-                       [str(tmp_path / os.path.basename(t)) for t in PIN_TESTS],
-                       cwd=str(tmp_path), env=env, capture_output=True, text=True, timeout=300)
-    assert r.returncode != 0, f"planted mistake survived the pins: {new!r}\n{r.stdout[-2000:]}"
+                        "--rootdir", tmp_path] +
+                       [os.path.join(tmp_path, os.path.basename(t)) for t in PIN_TESTS],
+                       cwd=tmp_path, env=env, capture_output=True, text=True, timeout=600)
+    if r.returncode == 0:
+        return f"planted mistake survived the pins: {new!r}\n{r.stdout[-2000:]}"
+    return None
+
+
+@pytest.fixture(scope="module")
+def mutation_results(tmp_path_factory):
+    from concurrent.futures import ThreadPoolExecutor
+    root = str(tmp_path_factory.mktemp("mutations"))
+    with ThreadPoolExecutor(max_workers=6) as ex:
+        futs = [ex.submit(_run_mutation, root, i, *m) for i, m in enumerate(MUTATIONS)]
+        return [f.result() for f in futs]
+
+
+@pytest.mark.parametrize("idx", range(len(MUTATIONS)),
+                         ids=[f"{m[0]}:{i}" for i, m in enumerate(MUTATIONS)])
+def test_pins_catch_planted_mistake(mutation_results, idx):
+    err = mutation_results[idx]
+    assert err is None, err

@@ -250,22 +250,41 @@ __global__ void __launch_bounds__(kDiagThreads) diag_tile(DiagParams p) {
   SelState* st = (SelState*)p.ws;
   if (!last_block(&st->ticket[0], gridDim.x)) return;
 
-  // last tile: fold the partials in tile order
+  // last tile: lane j of wave 0 folds tiles j, j + 64, ... in order; thread 0 then folds
+  // the 64 lane results in lane order (a tree fixed by the tile count)
   __shared__ long long s_n;
+  __shared__ TilePartial s_lane[64];
+  if (wave == 0) {
+    TilePartial a = {};
+    for (int g = lane; g < lay.G; g += 64) {
+      const TilePartial b = tp[g];
+      a.s_abs += b.s_abs;
+      a.s_exp += b.s_exp;
+      a.s_kl += b.s_kl;
+      a.s_d += b.s_d;
+      a.n += b.n;
+      a.lo += b.lo;
+      a.hi += b.hi;
+      a.nonfinite += b.nonfinite;
+      a.best = b.best > a.best ? b.best : a.best;
+    }
+    s_lane[lane] = a;
+  }
+  __syncthreads();
   if (tid == 0) {
     double a_abs = 0, a_exp = 0, a_kl = 0, a_d = 0;
     long long an = 0, alo = 0, ahi = 0, anf = 0;
     unsigned long long abest = 0;
-    for (int g = 0; g < lay.G; ++g) {
-      a_abs += tp[g].s_abs;
-      a_exp += tp[g].s_exp;
-      a_kl += tp[g].s_kl;
-      a_d += tp[g].s_d;
-      an += tp[g].n;
-      alo += tp[g].lo;
-      ahi += tp[g].hi;
-      anf += tp[g].nonfinite;
-      abest = tp[g].best > abest ? tp[g].best : abest;
+    for (int g = 0; g < 64; ++g) {
+      a_abs += s_lane[g].s_abs;
+      a_exp += s_lane[g].s_exp;
+      a_kl += s_lane[g].s_kl;
+      a_d += s_lane[g].s_d;
+      an += s_lane[g].n;
+      alo += s_lane[g].lo;
+      ahi += s_lane[g].hi;
+      anf += s_lane[g].nonfinite;
+      abest = s_lane[g].best > abest ? s_lane[g].best : abest;
     }
     drift_stats& s = st->stats;
     s.n_active = an;

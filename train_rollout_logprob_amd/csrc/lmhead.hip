@@ -9,9 +9,10 @@
 //   lm_transpose_w   W [H, V] -> WT [Vp, Hp] (K contiguous, zero padded) in the workspace,
 //                    so both MFMA operands load as 16-byte K-contiguous vectors;
 //   lm_pad_hidden    (only when T or H is not a tile multiple) hidden -> [Tp, Hp], zero pad;
-//   lm_gemm_lse      C^T tiles: 128 vocab rows x 128 tokens per block, K = H in steps of 64
-//                    through double-buffered LDS, v_mfma_f32_32x32x16_bf16 with fp32
-//                    accumulation. The epilogue turns each token's 128 logits into a (k, s)
+//   lm_gemm_lse      C^T tiles: 256 vocab rows x 256 tokens per block, K = H in steps of 64
+//                    through double-buffered LDS with global loads two stages ahead,
+//                    v_mfma_f32_32x32x16_bf16 with fp32
+//                    accumulation. The epilogue turns each token's 256 logits into a (k, s)
 //                    log-sum-exp partial and records z[t, y_t] from the single owning lane;
 //   lm_merge         per token, the partials of all vocab tiles in ascending tile order.
 // The K order of every product is fixed (k-tiles ascending, 16-wide MFMA steps ascending)
@@ -30,11 +31,28 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBV = 128;        // vocab rows per block (MFMA M)
-constexpr int kBT = 128;        // tokens per block (MFMA N)
+// Block tile and wave grid. Two waves per SIMD (8 waves) let one wave's MFMAs cover the
+// other's LDS and global-load waits. The K order of the products does not depend on
+// these shapes; the epilogue tree depends only on the vocab-wave split (2).
+#ifndef DRIFT_LM_WAVES_T
+#define DRIFT_LM_WAVES_T 4
+#endif
+constexpr int kBV = 256;        // vocab rows per block (MFMA M)
+constexpr int kBT = 256;        // tokens per block (MFMA N)
 constexpr int kBK = 64;         // K per LDS stage
 constexpr int kPitch = kBK + 8; // LDS row pitch in bf16 (144 B: conflict-free 16-B reads)
-constexpr int kThreads = 256;   // 4 waves as 2 (vocab) x 2 (tokens), 64 x 64 each
+constexpr int kWavesV = 2;
+constexpr int kWavesT = DRIFT_LM_WAVES_T;
+constexpr int kThreads = 64 * kWavesV * kWavesT;
+constexpr int kWV = kBV / kWavesV;  // vocab rows per wave (128)
+constexpr int kWT = kBT / kWavesT;  // tokens per wave
+constexpr int kTM = kWV / 32;       // 32x32 MFMA tiles per wave along vocab
+constexpr int kTN = kWT / 32;       // ... along tokens
+// Stage loads: each thread moves 64 contiguous bytes (half a row's K slice) per pass, so
+// its four 16-byte loads share one address register (immediate offsets).
+constexpr int kRowsPerPass = kThreads / 2;
+constexpr int kPasses = kBV / kRowsPerPass;
+static_assert(kTN >= 1 && kPasses >= 1 && kBV == kBT && kBK == 64, "tile shape");
 constexpr int kGroupV = 16;     // vocab tiles per scheduling group
 constexpr int kGroupT = 16;     // token tiles per scheduling chunk
 
@@ -148,91 +166,130 @@ struct GemmArgs {
   float* zsel;          // [Tp]
 };
 
-__global__ void __launch_bounds__(kThreads) lm_gemm_lse(GemmArgs a) {
+__global__ void __launch_bounds__(kThreads, 1) lm_gemm_lse(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBV][kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBT][kPitch];
-  __shared__ float s_k[2][64];
-  __shared__ double s_s[2][64];
+  __shared__ float s_k[kWavesT][kWT];
+  __shared__ double s_s[kWavesT][kWT];
   int64_t vt, tt;
   tile_of(blockIdx.x, a.nVt_pad, a.nTt_pad, vt, tt);
   if (vt >= a.nVt || tt >= a.nTt) return;  // block-uniform
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wv = wave >> 1, wt = wave & 1;
+  const int wv = wave / kWavesT, wt = wave % kWavesT;
   const int lr = lane & 31, lh = lane >> 5;
   const int64_t v0 = vt * kBV, t0 = tt * kBT;
   const uint16_t* gA = a.wt + v0 * a.Hp;
   const uint16_t* gB = a.hid + t0 * a.Hp;
 
-  // stage loader: 16 KB per operand, 4 x 16 B per thread per operand
-  u32x4 ra[4], rb[4];
-  auto load_stage = [&](int64_t k0) {
+  // Two register sets of stage loads are in flight (stage j lives in set j % 2); LDS is
+  // double buffered (stage j in buffer j % 2).
+  const int lrow = tid >> 1, lcol = (tid & 1) * 32;
+  const uint16_t* pa = gA + (int64_t)lrow * a.Hp + lcol;
+  const uint16_t* pb = gB + (int64_t)lrow * a.Hp + lcol;
+  struct Set {
+    u32x4 a[kPasses][4], b[kPasses][4];
+  };
+  Set s0, s1;
+  auto load = [&](Set& R, int64_t k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + kThreads * i;
-      const int row = c >> 3, col = (c & 7) * 8;
-      ra[i] = *(const u32x4*)(gA + (int64_t)row * a.Hp + k0 + col);
-      rb[i] = *(const u32x4*)(gB + (int64_t)row * a.Hp + k0 + col);
+    for (int ps = 0; ps < kPasses; ++ps) {
+      const uint16_t* qa = pa + (int64_t)ps * kRowsPerPass * a.Hp + k0;
+      const uint16_t* qb = pb + (int64_t)ps * kRowsPerPass * a.Hp + k0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        R.a[ps][i] = *(const u32x4*)(qa + 8 * i);
+        R.b[ps][i] = *(const u32x4*)(qb + 8 * i);
+      }
     }
   };
-  auto store_stage = [&](int buf) {
+  auto store = [&](const Set& R, int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + kThreads * i;
-      const int row = c >> 3, col = (c & 7) * 8;
-      *(u32x4*)&sA[buf][row][col] = ra[i];
-      *(u32x4*)&sB[buf][row][col] = rb[i];
-    }
+    for (int ps = 0; ps < kPasses; ++ps)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        *(u32x4*)&sA[buf][ps * kRowsPerPass + lrow][lcol + 8 * i] = R.a[ps][i];
+        *(u32x4*)&sB[buf][ps * kRowsPerPass + lrow][lcol + 8 * i] = R.b[ps][i];
+      }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[kTM][kTN];
 #pragma unroll
-  for (int im = 0; im < 2; ++im)
+  for (int im = 0; im < kTM; ++im)
 #pragma unroll
-    for (int in = 0; in < 2; ++in)
+    for (int in = 0; in < kTN; ++in)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[im][in][r] = 0.0f;
 
-  const int64_t nk = a.Hp / kBK;
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const int buf = (int)(kt & 1);
-    if (kt + 1 < nk) load_stage((kt + 1) * kBK);
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
+      __builtin_amdgcn_sched_barrier(0);  // keep the K steps in order (register pressure)
       const int koff = kk * 16 + lh * 8;
-      bf16x8 fa[2], fb[2];
+      bf16x8 fb[kTN];
 #pragma unroll
-      for (int im = 0; im < 2; ++im)
-        fa[im] = *(const bf16x8*)&sA[buf][64 * wv + 32 * im + lr][koff];
+      for (int in = 0; in < kTN; ++in)
+        fb[in] = *(const bf16x8*)&sB[buf][kWT * wt + 32 * in + lr][koff];
 #pragma unroll
-      for (int in = 0; in < 2; ++in)
-        fb[in] = *(const bf16x8*)&sB[buf][64 * wt + 32 * in + lr][koff];
+      for (int im = 0; im < kTM; ++im) {
+        const bf16x8 fa = *(const bf16x8*)&sA[buf][kWV * wv + 32 * im + lr][koff];
 #pragma unroll
-      for (int im = 0; im < 2; ++im)
-#pragma unroll
-        for (int in = 0; in < 2; ++in)
-          acc[im][in] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[im], fb[in], acc[im][in], 0, 0, 0);
+        for (int in = 0; in < kTN; ++in)
+          acc[im][in] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb[in], acc[im][in], 0, 0, 0);
+      }
     }
-    if (kt + 1 < nk) store_stage(buf ^ 1);
+  };
+
+  const int64_t nk = a.Hp / kBK;
+  load(s0, 0);
+  if (nk > 1) load(s1, kBK);
+  store(s0, 0);
+  __syncthreads();
+  // Stage j is loaded into set j % 2 two stages ahead and computed from buffer j % 2.
+  // Per pair of stages (kt, kt + 1): load kt+2 into s0, compute buffer 0, move s1 (stage
+  // kt+1) into buffer 1, barrier; load kt+3 into s1, compute buffer 1, move s0 (stage
+  // kt+2) into buffer 0, barrier. An odd last stage is computed from buffer 0.
+  const int64_t nk2 = nk & ~(int64_t)1;
+  for (int64_t kt = 0; kt < nk2; kt += 2) {
+    if (kt + 2 < nk) load(s0, (kt + 2) * kBK);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(0);
+    __builtin_amdgcn_sched_barrier(0);
+    store(s1, 1);
+    __syncthreads();
+    if (kt + 3 < nk) load(s1, (kt + 3) * kBK);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 2 < nk) store(s0, 0);
+    __syncthreads();
+  }
+  if (nk & 1) {
+    compute(0);
     __syncthreads();
   }
 
-  // Epilogue. Lane (lr, lh) of wave (wv, wt) holds, for token t = t0 + 64 wt + 32 in + lr,
-  // the logits of vocab rows v0 + 64 wv + 32 im + 8 (r / 4) + 4 lh + (r % 4).
+  // Epilogue. Lane (lr, lh) of wave (wv, wt) holds, for token t = t0 + kWT wt + 32 in + lr,
+  // the logits of vocab rows vb + 32 im + 8 (r / 4) + (r % 4), vb = v0 + kWV wv + 4 lh.
+  // Row tests compare the compile-time offset 32 im + 8 (r / 4) + (r % 4) against
+  // per-lane limits, so no per-element index is materialised.
+  const int64_t vb = v0 + kWV * wv + 4 * lh;
+  const int64_t vlim64 = a.V - vb;  // offsets below this are real vocab rows
+  const int vlim = vlim64 > kWV ? kWV : (int)vlim64;
 #pragma unroll
-  for (int in = 0; in < 2; ++in) {
-    const int64_t t = t0 + 64 * wt + 32 * in + lr;
+  for (int in = 0; in < kTN; ++in) {
+    const int64_t t = t0 + kWT * wt + 32 * in + lr;
     const int64_t y = (t < a.T) ? (int64_t)a.ids[t] : -1;
+    const int64_t yr64 = y - vb;
+    const int yrel = (y >= 0 && yr64 >= 0 && yr64 < kWV) ? (int)yr64 : -1;
     float m = -INFINITY;
 #pragma unroll
-    for (int im = 0; im < 2; ++im)
+    for (int im = 0; im < kTM; ++im)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t v = v0 + 64 * wv + 32 * im + 8 * (r / 4) + 4 * lh + (r % 4);
-        if (v < a.V) m = fmaxf(m, acc[im][in][r]);
-        if (v == y) a.zsel[t] = acc[im][in][r];  // the single owner of z[t, y_t]
+        const int off = 32 * im + 8 * (r / 4) + (r % 4);
+        const float z = acc[im][in][r];
+        if (off < vlim) m = fmaxf(m, z);
+        if (off == yrel) a.zsel[t] = z;  // the single owner of z[t, y_t]
       }
     Acc p = {-INFINITY, 0.0};
     if (m > -INFINITY) {
@@ -241,12 +298,13 @@ __global__ void __launch_bounds__(kThreads) lm_gemm_lse(GemmArgs a) {
       if (k == INFINITY) {
         s = NAN;
       } else {
+        const float nk = -k;
 #pragma unroll
-        for (int im = 0; im < 2; ++im)
+        for (int im = 0; im < kTM; ++im)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int64_t v = v0 + 64 * wv + 32 * im + 8 * (r / 4) + 4 * lh + (r % 4);
-            if (v < a.V) s += __builtin_amdgcn_exp2f(fmaf(acc[im][in][r], kLog2e, -k));
+            const int off = 32 * im + 8 * (r / 4) + (r % 4);
+            if (off < vlim) s += __builtin_amdgcn_exp2f(fmaf(acc[im][in][r], kLog2e, nk));
           }
       }
       p.k = (k == INFINITY) ? 0.0f : k;
@@ -265,7 +323,7 @@ __global__ void __launch_bounds__(kThreads) lm_gemm_lse(GemmArgs a) {
       s_s[wt][32 * in + lr] = p.s;
     }
     __syncthreads();
-    if (wv == 0 && lh == 0 && t < a.Tp) {
+    if (wv == 0 && lh == 0) {
       const Acc q = merge(p, Acc{s_k[wt][32 * in + lr], s_s[wt][32 * in + lr]});
       Partial out;
       out.k = q.k;
@@ -277,14 +335,46 @@ __global__ void __launch_bounds__(kThreads) lm_gemm_lse(GemmArgs a) {
   }
 }
 
+// Four lanes per token: lane q folds the vocab tiles [q*c, (q+1)*c) in ascending order
+// (c = ceil(nVt / 4)), then the four results are folded in q order. The tree depends only
+// on the number of vocab tiles.
+constexpr int kMergeSplit = 4;
+
 __global__ void __launch_bounds__(256) lm_merge(const Partial* __restrict__ part,
                                                  const float* __restrict__ zsel,
                                                  const int32_t* __restrict__ ids,
                                                  const uint8_t* __restrict__ active,
                                                  float* __restrict__ logp, int64_t T,
                                                  int64_t Tp, int64_t V, int64_t nVt, char* ws) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= T) return;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t t = gid / kMergeSplit;
+  const int q = (int)(gid % kMergeSplit);
+  const bool live = t < T && (!active || active[t]);
+  const int64_t c = (nVt + kMergeSplit - 1) / kMergeSplit;
+  const int64_t j0 = (int64_t)q * c, j1 = j0 + c < nVt ? j0 + c : nVt;
+  Acc A = {-INFINITY, 0.0};
+  if (live) {
+    int64_t j = j0;
+    for (; j + 8 <= j1; j += 8) {
+      Partial b[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) b[u] = part[(j + u) * Tp + t];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) A = merge(A, Acc{b[u].k, b[u].s});
+    }
+    for (; j < j1; ++j) {
+      const Partial b = part[j * Tp + t];
+      A = merge(A, Acc{b.k, b.s});
+    }
+  }
+  // fold the four lanes of the token in q order (lanes 4i..4i+3 of the wave)
+  Acc P[kMergeSplit];
+#pragma unroll
+  for (int i = 0; i < kMergeSplit; ++i) {
+    P[i].k = __shfl(A.k, (threadIdx.x & ~(kMergeSplit - 1)) + i);
+    P[i].s = __shfl(A.s, (threadIdx.x & ~(kMergeSplit - 1)) + i);
+  }
+  if (q != 0 || t >= T) return;
   if (active && !active[t]) {
     logp[t] = 0.0f;
     return;
@@ -296,14 +386,12 @@ __global__ void __launch_bounds__(256) lm_merge(const Partial* __restrict__ part
     record_error(h, kErrToken, t);
     return;
   }
-  Acc A = {-INFINITY, 0.0};
-  for (int64_t j = 0; j < nVt; ++j) {  // vocab tiles in ascending order
-    const Partial q = part[j * Tp + t];
-    A = merge(A, Acc{q.k, q.s});
-  }
+  Acc R = P[0];
+#pragma unroll
+  for (int i = 1; i < kMergeSplit; ++i) R = merge(R, P[i]);
   const float z = zsel[t];
-  logp[t] = (float)((double)z - lse_of(A));
-  if (!lse_ok(A) || !(fabsf(z) < INFINITY)) record_error(h, kErrNonfinite, t);
+  logp[t] = (float)((double)z - lse_of(R));
+  if (!lse_ok(R) || !(fabsf(z) < INFINITY)) record_error(h, kErrNonfinite, t);
 }
 
 }  // namespace
@@ -342,7 +430,8 @@ hipError_t launch_lmhead(const LmheadParams& p, hipStream_t s) {
   g.zsel = (float*)(p.ws + l.zsel_off);
   const int64_t nblocks = g.nVt_pad * g.nTt_pad;
   hipLaunchKernelGGL(lm_gemm_lse, dim3((unsigned)nblocks), dim3(kThreads), 0, s, g);
-  hipLaunchKernelGGL(lm_merge, dim3((unsigned)((p.T + 255) / 256)), dim3(256), 0, s, g.part,
+  hipLaunchKernelGGL(lm_merge, dim3((unsigned)((p.T * kMergeSplit + 255) / 256)), dim3(256), 0, s,
+                     g.part,
                      g.zsel, p.ids, p.active, p.logp, p.T, l.Tp, p.V, l.nVt, p.ws);
   return hipGetLastError();
 }
