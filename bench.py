@@ -143,6 +143,8 @@ def main():
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
                     help="copy: a plain device copy of known size, to calibrate HBM counters")
     ap.add_argument("--copy-mib", type=int, default=4096)
+    ap.add_argument("--xf", default="none", choices=["none", "temperature", "softcap"],
+                    help="apply a logit transform on both sides (cost of the option)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build has "
@@ -179,8 +181,10 @@ def main():
     N, V = case.N, case.V
     esz = case.elem_bytes
     n_active = case.n_active()
+    chain = {"none": None, "temperature": [("temperature", 0.7)],
+             "softcap": [("softcap", 30.0)]}[args.xf]
     runner = B.ScoringStep(case.train, case.rollout, ids, att, act, case.layout, case.B,
-                           case.L, cu, case.eps_low, case.eps_high)
+                           case.L, cu, case.eps_low, case.eps_high, transforms=(chain, chain))
     n_ev = args.warmup + args.steps
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(n_ev)]
@@ -238,16 +242,17 @@ def main():
         "config": {"workload": WORKLOAD_TEXT[args.workload],
                    "V": V, "B": case.B, "L": case.L, "N": N, "n_active": n_active,
                    "logits_dtype": case.dtype, "arith": "fp32 exp2, fp64 sums",
-                   "parallelism": "single GPU"},
+                   "transforms": args.xf, "parallelism": "single GPU"},
         "logits_gbs": alg_bytes * args.steps / elapsed / 1e9,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": recorded_traffic() if args.workload == "qwen8b" else None,
+                     "traffic": recorded_traffic()
+                     if args.workload == "qwen8b" and args.xf == "none" else None,
                      "kernel": f"score_rows<{case.dtype}>", "kernel_ms": kern_avg,
                      "bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
     }
-    if not args.no_lmhead and args.workload == "qwen8b":
+    if not args.no_lmhead and args.workload == "qwen8b" and args.xf == "none":
         del runner, case
         torch.cuda.empty_cache()
         log("[bench] fused LM-head leg")

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define DRIFT_ABI_VERSION 1
+#define DRIFT_ABI_VERSION 2
 
 /* ---- status codes ---------------------------------------------------------------- */
 #define DRIFT_OK          0
@@ -64,6 +64,19 @@ extern "C" {
 #define DRIFT_PAD_RIGHT 0  /* each sequence: attended rows, then padding              */
 #define DRIFT_PAD_LEFT  1  /* each sequence: padding, then attended rows              */
 #define DRIFT_PACKED    2  /* sequences packed back to back, delimited by cu_seqlens  */
+
+/* ---- logit transforms ("[WS2] Framework for ablation experiment", LogProb knobs row 7:
+ *      an ordered chain applied to every logit before the softmax) ---------------------- */
+#define DRIFT_XF_SCALE       1  /* x -> x * value        (logit_scale)                   */
+#define DRIFT_XF_TEMPERATURE 2  /* x -> x / value        (value > 0; as x * (1/value))   */
+#define DRIFT_XF_SOFTCAP     3  /* x -> value * tanh(x * (1/value))  (value > 0)         */
+#define DRIFT_MAX_TRANSFORMS 4
+
+typedef struct drift_transform {
+  int32_t count;                       /* steps in use, 0 = identity                     */
+  int32_t op[DRIFT_MAX_TRANSFORMS];    /* DRIFT_XF_*, applied in index order             */
+  float value[DRIFT_MAX_TRANSFORMS];   /* finite; > 0 for TEMPERATURE and SOFTCAP        */
+} drift_transform;
 
 /* ---- operations (for drift_workspace_size) ---------------------------------------- */
 #define DRIFT_OP_SELECTED_LOGPROB 0
@@ -97,6 +110,12 @@ extern "C" {
  *  num_seqs        PACKED: number of sequences.
  *  prof_events     optional pair of hipEvent_t (as void*), recorded on `stream` right
  *                  before and after the scoring kernel; NULL entries are skipped.
+ *  vocab_real      columns that enter the log-sum-exp: 0 or V = all ("include"), else
+ *                  the first vocab_real columns only ("mask": padded vocab rows are
+ *                  excluded, LogProb knobs row 2); selected ids must lie below it.
+ *  transforms      [0] train side, [1] rollout side: ordered logit transforms applied to
+ *                  every logit of that side (the selected one included) before the
+ *                  softmax (LogProb knobs row 7). count = 0 on both sides = none.
  *
  * A row is active iff attention != 0 and action != 0 (and, PACKED, it is before the end).
  */
@@ -118,6 +137,8 @@ typedef struct drift_logprob_args {
   const int32_t* cu_seqlens;
   int64_t num_seqs;
   void* prof_events[2];
+  int64_t vocab_real;
+  drift_transform transforms[2];
 } drift_logprob_args;
 
 /* Statistics of drift_diagnostics ("Diagnostics" table; every metric over active rows).

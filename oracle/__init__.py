@@ -9,7 +9,8 @@ It is a plain, slow, textbook implementation in float64 numpy / Python:
 * ``logprob``     - active-row rule, logical-input validation, two-pass log-sum-exp,
                     selected-logit gather and dlogp (page "WS2 Cross-Config Logprob Drift
                     Contract", section "Measurement Contract"; page "[WS2] Framework for
-                    ablation experiment", LogProb knobs rows 2, 6, 8).
+                    ablation experiment", LogProb knobs rows 2, 6, 8), the vocab-padding
+                    mask (row 2) and the ordered logit transform chain (row 7).
 * ``diagnostics`` - ratio0, clipfrac0, approx_kl0 and mean/p95/p99/max |dlogp| (page "WS2
                     Cross-Config Logprob Drift Contract", section "Diagnostics" table).
 * ``lmhead``      - hidden x W_vocab followed by the same log-softmax gather (page "[WS2]
@@ -19,9 +20,9 @@ Each function is pinned by tests against closed forms, brute force at 50 decimal
 and textbook library routines; none is "parity unpinned".
 """
 from .logprob import (STATUS, widen, logsumexp_row, selected_logprob, validate_inputs,
-                      active_rows, score_row, score_rows)
+                      active_rows, score_row, score_rows, apply_transforms, TRANSFORMS)
 from .diagnostics import diagnostics, nearest_rank
 from .lmhead import lmhead_logprob
 
 __all__ = ["STATUS", "widen", "logsumexp_row", "selected_logprob", "validate_inputs",
-           "active_rows", "score_row", "score_rows", "diagnostics", "nearest_rank", "lmhead_logprob"]
+           "active_rows", "score_row", "score_rows", "apply_transforms", "TRANSFORMS", "diagnostics", "nearest_rank", "lmhead_logprob"]

@@ -119,6 +119,31 @@ def validate_inputs(attention, action, ids, V, N, layout, B=0, L=0, cu_seqlens=N
     return errs
 
 
+# Logit transforms, applied element-wise in the order given, before the softmax ("[WS2]
+# Framework for ablation experiment", LogProb knobs row 7: temperature, logit_scale,
+# soft_cap as an ordered chain). Each step is (kind, value):
+#   "scale"        x -> x * value
+#   "temperature"  x -> x / value
+#   "softcap"      x -> value * tanh(x / value)
+TRANSFORMS = ("scale", "temperature", "softcap")
+
+
+def apply_transforms(x, chain):
+    """float64 logits after the ordered transform chain (None or [] = identity)."""
+    x = np.asarray(x, dtype=np.float64)
+    for kind, value in (chain or ()):
+        v = float(value)
+        if kind == "scale":
+            x = x * v
+        elif kind == "temperature":
+            x = x / v
+        elif kind == "softcap":
+            x = v * np.tanh(x / v)
+        else:
+            raise ValueError(kind)
+    return x
+
+
 def score_row(train_row, rollout_row, y):
     """Per-row teacher-forced scoring of one active row with a valid id.
 
@@ -141,13 +166,18 @@ def score_row(train_row, rollout_row, y):
 
 
 def selected_logprob(train, rollout, dtype, ids, attention, action, V, layout,
-                     B=0, L=0, cu_seqlens=None):
+                     B=0, L=0, cu_seqlens=None, vocab_real=None, transforms=(None, None)):
     """Whole-batch oracle.
 
-    train, rollout: stored logits [N, V] (float32 or bf16 bit patterns as uint16).
+    train, rollout: stored logits [N, >=V] (float32 or bf16 bit patterns as uint16).
+    vocab_real: number of leading columns that enter the log-sum-exp (the "mask" vocab
+    padding policy of LogProb knobs row 2); None = all V ("include"). Selected ids must
+    lie below it. transforms: (train chain, rollout chain), see `apply_transforms`.
     Returns dict(train_logp, rollout_logp, dlogp: float64 [N], active: uint8 [N],
     status: str). Inactive rows carry 0.0; active rows with an out-of-range id carry NaN.
     """
+    if vocab_real is not None:
+        V = int(vocab_real)
     train = np.asarray(train)
     rollout = np.asarray(rollout)
     N = train.shape[0]
@@ -162,7 +192,9 @@ def selected_logprob(train, rollout, dtype, ids, attention, action, V, layout,
         if not (0 <= y < V):
             out_t[r] = out_r[r] = out_d[r] = math.nan
             continue
-        lpt, lpr, d, bad = score_row(widen(train[r, :V], dtype), widen(rollout[r, :V], dtype), y)
+        xt = apply_transforms(widen(train[r, :V], dtype), transforms[0])
+        xr = apply_transforms(widen(rollout[r, :V], dtype), transforms[1])
+        lpt, lpr, d, bad = score_row(xt, xr, y)
         out_t[r], out_r[r], out_d[r] = lpt, lpr, d
         if bad:
             errs.add("ENONFINITE")
@@ -175,7 +207,8 @@ def selected_logprob(train, rollout, dtype, ids, attention, action, V, layout,
             "active": act.astype(np.uint8), "status": status}
 
 
-def score_rows(train_rows, rollout_rows, dtype, ids_rows):
+def score_rows(train_rows, rollout_rows, dtype, ids_rows, vocab_real=None,
+               transforms=(None, None)):
     """Oracle on a sample of active rows (rows already known valid): returns float64
     arrays (train_logp, rollout_logp, dlogp). Used at full sizes, where only sampled rows
     are copied to the host."""
@@ -184,6 +217,8 @@ def score_rows(train_rows, rollout_rows, dtype, ids_rows):
     r = np.empty(k)
     d = np.empty(k)
     for i in range(k):
-        t[i], r[i], d[i], _ = score_row(widen(train_rows[i], dtype),
-                                        widen(rollout_rows[i], dtype), int(ids_rows[i]))
+        V = train_rows.shape[1] if vocab_real is None else int(vocab_real)
+        xt = apply_transforms(widen(train_rows[i][:V], dtype), transforms[0])
+        xr = apply_transforms(widen(rollout_rows[i][:V], dtype), transforms[1])
+        t[i], r[i], d[i], _ = score_row(xt, xr, int(ids_rows[i]))
     return t, r, d

@@ -33,15 +33,17 @@ def test_library_exports_every_declared_symbol():
 
 def test_struct_layouts_match_header():
     from train_rollout_logprob_amd import binding as B
-    # drift_logprob_args: 4 x i32, 3 x i64, 5 pointers, 2 x i64, pointer, i64, 2 pointers
-    assert ctypes.sizeof(B.drift_logprob_args) == 16 + 24 + 40 + 16 + 8 + 8 + 16
+    # drift_logprob_args: 4 x i32, 3 x i64, 5 pointers, 2 x i64, pointer, i64, 2 pointers,
+    # i64 vocab_real, 2 x drift_transform (i32 count, 4 x i32 op, 4 x f32 value)
+    assert ctypes.sizeof(B.drift_transform) == 36
+    assert ctypes.sizeof(B.drift_logprob_args) == 16 + 24 + 40 + 16 + 8 + 8 + 16 + 8 + 72
     assert ctypes.sizeof(B.drift_stats) == 5 * 8 + 5 * 8 + 3 * 4 + 4
 
 
 def test_descriptor_and_strerror():
     from train_rollout_logprob_amd import binding as B
     d = B.drift_backend_descriptor()
-    assert d["abi_version"] == 1 and d["archs"] == "gfx950"
+    assert d["abi_version"] == 2 and d["archs"] == "gfx950"
     assert "batch composition" in d["determinism"]
     assert d["lse_domain"] == "natural log"
     assert d["build_fingerprint"].startswith("src:")
@@ -96,3 +98,23 @@ def test_host_checks_fail_closed_without_launching():
     assert lib.drift_lmhead_logprob(None, None, 4, 4100, 16, None, None, None, None, 0,
                                     None) == B.DRIFT_EINVAL             # H % 8 != 0
     assert lib.drift_get_status(None, None, None) == B.DRIFT_EWORKSPACE
+    # vocab_real and transform chains are checked before the workspace
+    a.layout, a.num_rows, a.batch, a.seq_len, a.vocab, a.row_stride = B.DRIFT_PAD_RIGHT, 0, 0, 1, 10, 10
+    a.vocab_real = 11                                                  # > V
+    assert lib.drift_selected_logprob(ctypes.byref(a), None, None, None, None, None, 0,
+                                      None) == B.DRIFT_EINVAL
+    a.vocab_real = 0
+    for chain in ([("temperature", 0.0)], [("softcap", -1.0)], [("scale", float("nan"))],
+                  [("scale", 1.0)] * 5):
+        try:
+            B.set_chain(a.transforms[1], chain)
+        except ValueError:
+            continue                                                   # more than 4 steps
+        assert lib.drift_selected_logprob(ctypes.byref(a), None, None, None, None, None, 0,
+                                          None) == B.DRIFT_EINVAL, chain
+    B.set_chain(a.transforms[1], [])
+    a.transforms[0].count = 1
+    a.transforms[0].op[0] = 9                                          # unknown op
+    a.transforms[0].value[0] = 1.0
+    assert lib.drift_selected_logprob(ctypes.byref(a), None, None, None, None, None, 0,
+                                      None) == B.DRIFT_EINVAL

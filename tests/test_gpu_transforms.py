@@ -1,0 +1,104 @@
+"""GPU parity of the vocab-padding mask and the per-side logit transform chains
+("[WS2] Framework for ablation experiment", LogProb knobs rows 2 and 7) against the
+fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import (LOGP_TOL, assert_logprob_parity, device_inputs, host_logits, make_small,
+                     run_library, status_name)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+
+
+def _oracle(case, vocab_real=None, transforms=(None, None), ids=None):
+    return oracle.selected_logprob(host_logits(case.train), host_logits(case.rollout), case.dtype,
+                                   case.ids if ids is None else ids, case.attention, case.action,
+                                   case.V, case.layout, case.B, case.L, case.cu_seqlens,
+                                   vocab_real=vocab_real, transforms=transforms)
+
+
+CHAINS = {
+    "temperature": ([("temperature", 0.7)], [("temperature", 0.7)]),
+    "scale": ([("scale", 1.3)], [("scale", 1.3)]),
+    "softcap": ([("softcap", 15.0)], [("softcap", 15.0)]),
+    "chain3": ([("scale", 2.0), ("softcap", 30.0), ("temperature", 1.5)],
+               [("scale", 2.0), ("softcap", 30.0), ("temperature", 1.5)]),
+    "per_side": (None, [("temperature", 0.9)]),
+    "order_swapped": ([("scale", 3.0), ("softcap", 10.0)], [("softcap", 10.0), ("scale", 3.0)]),
+}
+
+
+@pytest.mark.parametrize("spec", [dict(name="qwen8b", B=2, L=48), dict(name="packed", nseq=3,
+                                  len_lo=40, len_hi=90, V=3001)], ids=["bf16", "f32_ragged"])
+@pytest.mark.parametrize("chain", list(CHAINS))
+def test_transform_chain_parity(spec, chain):
+    case = make_small(spec)
+    tr = CHAINS[chain]
+    print(f"[case] {spec['name']} chain={chain}", flush=True)
+    got = run_library(case, transforms=tr)
+    want = _oracle(case, transforms=tr)
+    assert status_name(got["status"]) == want["status"] == "OK"
+    assert_logprob_parity(got, want)
+
+
+def test_identity_chain_is_bitwise_the_plain_path():
+    case = make_small(dict(name="qwen8b", B=2, L=48))
+    plain = run_library(case)
+    ident = run_library(case, transforms=([("scale", 1.0)], [("temperature", 1.0)]))
+    for k in ("train_logp", "rollout_logp", "dlogp"):
+        assert np.array_equal(plain[k].view(np.uint32), ident[k].view(np.uint32)), k
+
+
+@pytest.mark.parametrize("dtype_spec", [dict(name="qwen8b", B=2, L=32, V=1000),
+                                        dict(name="tiny", B=2, L=32, V=1003, prompt=8)])
+def test_vocab_mask(dtype_spec):
+    case = make_small(dtype_spec)
+    Vr = case.V - 63
+    ids = case.ids % Vr
+    case.ids = ids.astype(np.int32)
+    # make the padded columns large so that "include" and "mask" differ a lot
+    case.train[:, Vr:] = 20.0
+    case.rollout[:, Vr:] = 20.0
+    got = run_library(case, vocab_real=Vr)
+    want = _oracle(case, vocab_real=Vr)
+    assert status_name(got["status"]) == want["status"] == "OK"
+    assert_logprob_parity(got, want)
+    both = run_library(case, vocab_real=Vr, transforms=([("softcap", 12.0)], None))
+    want2 = _oracle(case, vocab_real=Vr, transforms=([("softcap", 12.0)], None))
+    assert_logprob_parity(both, want2)
+    # an active selected id inside the padded columns is a token error
+    bad = case.ids.copy()
+    r0 = int(np.nonzero(got["active"])[0][0])
+    bad[r0] = Vr + 5
+    case.ids = bad
+    st = run_library(case, vocab_real=Vr)
+    assert status_name(st["status"]) == _oracle(case, vocab_real=Vr)["status"] == "ETOKEN"
+    assert st["first_bad"] == r0
+
+
+def test_transforms_keep_batch_composition_invariance():
+    from train_rollout_logprob_amd import binding as B
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    V = 151936
+    pool = torch.randn((20, V), generator=g, device="cuda").mul_(3).to(torch.bfloat16)
+    ids = torch.randint(0, V, (20,), generator=g, device="cuda", dtype=torch.int32)
+    tr = ([("softcap", 30.0), ("temperature", 0.8)], [("temperature", 0.8)])
+    ref = None
+    for bs, slot in ((1, 0), (9, 4), (20, 13)):
+        rows = torch.arange(bs, device="cuda") % 20
+        rows[slot] = 3
+        t, r, d, a, ws = B.selected_logprob(pool[rows], pool[rows], ids[rows], layout="right",
+                                            batch=1, seq_len=bs, check=True, transforms=tr)
+        v = np.array([t[slot].item(), r[slot].item(), d[slot].item()], np.float32)
+        if ref is None:
+            ref = v
+        assert np.array_equal(v.view(np.uint32), ref.view(np.uint32)), bs

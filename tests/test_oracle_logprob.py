@@ -243,3 +243,65 @@ def test_bf16_path_widens_before_scoring():
     ref = torch.log_softmax(xb.double(), dim=1).numpy()
     for r in range(3):
         assert abs(out["train_logp"][r] - ref[r, ids[r]]) <= 1e-13
+
+
+# --------------------------------------------------------------------------- mask + transforms
+
+def test_transform_identities_and_closed_forms():
+    x = RNG.standard_normal(500) * 3
+    assert np.array_equal(oracle.apply_transforms(x, None), x)
+    assert np.array_equal(oracle.apply_transforms(x, [("temperature", 1.0)]), x)
+    assert np.array_equal(oracle.apply_transforms(x, [("scale", 2.0), ("temperature", 2.0)]), x)
+    # soft cap: value * tanh(x / value), odd, bounded by the cap, ~x for |x| << cap
+    y = oracle.apply_transforms(x, [("softcap", 5.0)])
+    assert np.all(np.abs(y) < 5.0) and np.allclose(-y, oracle.apply_transforms(-x, [("softcap", 5.0)]))
+    small = np.array([1e-4, -2e-4])
+    assert np.allclose(oracle.apply_transforms(small, [("softcap", 30.0)]), small, rtol=1e-8)
+    assert oracle.apply_transforms(np.array([15.0]), [("softcap", 30.0)])[0] == 30.0 * math.tanh(0.5)
+
+
+def test_transform_order_matters_two_token_closed_form():
+    """V = 2: logp(y) = -log1p(exp(f(x_o) - f(x_y))) for the chain f; scale-then-cap and
+    cap-then-scale give different closed forms."""
+    xy, xo = 4.0, -2.0
+    f1 = lambda v: 10.0 * math.tanh((v * 3.0) / 10.0)     # scale 3 then cap 10
+    f2 = lambda v: 3.0 * (10.0 * math.tanh(v / 10.0))     # cap 10 then scale 3
+    row = np.array([xo, xy])
+    for chain, f in (([("scale", 3.0), ("softcap", 10.0)], f1),
+                     ([("softcap", 10.0), ("scale", 3.0)], f2)):
+        z = oracle.apply_transforms(row, chain)
+        got = z[1] - oracle.logsumexp_row(z)
+        want = -math.log1p(math.exp(f(xo) - f(xy)))
+        assert abs(got - want) <= 1e-14
+    assert abs(f1(xy) - f2(xy)) > 1.0
+
+
+def test_vocab_mask_excludes_padded_columns():
+    N, V, Vr = 4, 40, 33
+    x = RNG.standard_normal((N, V)).astype(np.float32)
+    x[:, Vr:] = 50.0                                       # padded columns, huge logits
+    ids = np.array([0, 5, 32, 17])
+    act = np.ones(N, np.uint8)
+    out = oracle.selected_logprob(x, x, "f32", ids, None, act, V, "right", 1, N, vocab_real=Vr)
+    assert out["status"] == "OK"
+    for r in range(N):
+        want = _decimal_logp(x[r, :Vr].astype(np.float64), int(ids[r]))
+        assert abs(out["train_logp"][r] - want) <= 1e-13
+    inc = oracle.selected_logprob(x, x, "f32", ids, None, act, V, "right", 1, N)
+    assert np.all(inc["train_logp"] < out["train_logp"] - 10)   # "include" sees the pad mass
+    bad = ids.copy(); bad[1] = Vr                          # an id in the padded region
+    assert oracle.selected_logprob(x, x, "f32", bad, None, act, V, "right", 1, N,
+                                   vocab_real=Vr)["status"] == "ETOKEN"
+
+
+def test_per_side_transforms_make_drift():
+    """Same logits, temperature 1 on train and 2 on rollout: the closed form of a
+    two-valued row."""
+    V, a, b, y = 20, 3.0, 1.0, 0
+    row = np.full((1, V), b, np.float32)
+    row[0, y] = a
+    out = oracle.selected_logprob(row, row, "f32", np.array([y]), None, np.ones(1, np.uint8), V,
+                                  "right", 1, 1, transforms=(None, [("temperature", 2.0)]))
+    lp = lambda aa, bb: aa - math.log(math.exp(aa) + (V - 1) * math.exp(bb))
+    want = lp(a, b) - lp(a / 2, b / 2)
+    assert abs(out["dlogp"][0] - want) <= 1e-14

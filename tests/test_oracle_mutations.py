@@ -30,6 +30,9 @@ MUTATIONS = [
      "math.fsum(math.exp(v) for v in vals) / (n + 1)"),
     ("diagnostics.py", 'out["argmax_row"] = int(r)\n            break',
      'out["argmax_row"] = int(r)'),                                              # last tie
+    ("logprob.py", "            x = x * v", "            x = x / v"),                 # scale
+    ("logprob.py", "x = v * np.tanh(x / v)", "x = np.tanh(x / v)"),               # soft cap
+    ("logprob.py", "        V = int(vocab_real)", "        pass"),                      # mask
     ("lmhead.py", "z[i, int(ids[r])]", "z[i, int(ids[i])]"),
     ("lmhead.py", "z = h @ weight_f64", "z = (h[:, ::-1] @ weight_f64)"),        # reversed K
 ]

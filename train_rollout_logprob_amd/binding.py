@@ -32,10 +32,19 @@ DRIFT_F32, DRIFT_BF16, DRIFT_I32, DRIFT_I64 = 0, 1, 2, 3
 DRIFT_PAD_RIGHT, DRIFT_PAD_LEFT, DRIFT_PACKED = 0, 1, 2
 LAYOUTS = {"right": DRIFT_PAD_RIGHT, "left": DRIFT_PAD_LEFT, "packed": DRIFT_PACKED}
 DRIFT_OP_SELECTED_LOGPROB, DRIFT_OP_DIAGNOSTICS, DRIFT_OP_LMHEAD = 0, 1, 2
+DRIFT_XF_SCALE, DRIFT_XF_TEMPERATURE, DRIFT_XF_SOFTCAP = 1, 2, 3
+DRIFT_MAX_TRANSFORMS = 4
+XF_CODES = {"scale": DRIFT_XF_SCALE, "temperature": DRIFT_XF_TEMPERATURE,
+            "softcap": DRIFT_XF_SOFTCAP}
 
 EXPORTS = ("drift_workspace_size", "drift_selected_logprob", "drift_get_status",
            "drift_diagnostics", "drift_lmhead_logprob", "drift_backend_descriptor",
            "drift_strerror")
+
+
+class drift_transform(ctypes.Structure):
+    _fields_ = [("count", ctypes.c_int32), ("op", ctypes.c_int32 * DRIFT_MAX_TRANSFORMS),
+                ("value", ctypes.c_float * DRIFT_MAX_TRANSFORMS)]
 
 
 class drift_logprob_args(ctypes.Structure):
@@ -47,7 +56,8 @@ class drift_logprob_args(ctypes.Structure):
                 ("attention_mask", ctypes.c_void_p), ("action_mask", ctypes.c_void_p),
                 ("batch", ctypes.c_int64), ("seq_len", ctypes.c_int64),
                 ("cu_seqlens", ctypes.c_void_p), ("num_seqs", ctypes.c_int64),
-                ("prof_events", ctypes.c_void_p * 2)]
+                ("prof_events", ctypes.c_void_p * 2), ("vocab_real", ctypes.c_int64),
+                ("transforms", drift_transform * 2)]
 
 
 class drift_stats(ctypes.Structure):
@@ -179,9 +189,23 @@ def workspace(op: int, num_rows: int, vocab: int, dtype: int, device, hidden_dim
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def set_chain(t: drift_transform, chain):
+    """Fill a drift_transform from [(kind, value), ...] with kind in XF_CODES."""
+    chain = list(chain or ())
+    if len(chain) > DRIFT_MAX_TRANSFORMS:
+        raise ValueError("at most 4 transform steps")
+    t.count = len(chain)
+    for i, (kind, value) in enumerate(chain):
+        t.op[i] = XF_CODES[kind]
+        t.value[i] = float(value)
+
+
 def make_args(train, rollout, ids, attention=None, action=None, layout="right", batch=0,
-              seq_len=0, cu_seqlens=None, vocab=None, events=None) -> drift_logprob_args:
-    """Describe torch tensors to the C ABI (no copies, no conversions)."""
+              seq_len=0, cu_seqlens=None, vocab=None, events=None, vocab_real=None,
+              transforms=(None, None)) -> drift_logprob_args:
+    """Describe torch tensors to the C ABI (no copies, no conversions). `vocab_real`:
+    leading columns that enter the log-sum-exp (None = all); `transforms`: (train chain,
+    rollout chain), each [(kind, value), ...]."""
     if train.dtype != rollout.dtype or train.shape != rollout.shape:
         raise ValueError("train and rollout logits must share dtype and shape")
     if train.stride(1) != 1 or rollout.stride(0) != train.stride(0):
@@ -206,19 +230,22 @@ def make_args(train, rollout, ids, attention=None, action=None, layout="right", 
     if events is not None:
         a.prof_events[0] = events[0]
         a.prof_events[1] = events[1]
+    a.vocab_real = 0 if vocab_real is None else int(vocab_real)
+    set_chain(a.transforms[0], transforms[0])
+    set_chain(a.transforms[1], transforms[1])
     return a
 
 
 def selected_logprob(train, rollout, ids, attention=None, action=None, layout="right",
                      batch=0, seq_len=0, cu_seqlens=None, ws=None, out=None, stream=None,
-                     events=None, check=False):
+                     events=None, check=False, vocab_real=None, transforms=(None, None)):
     """Allocate outputs (and a workspace unless given) and call drift_selected_logprob.
     Returns (train_logp, rollout_logp, dlogp, active, ws). With check=True, synchronizes
     and raises DriftError on a data-dependent status."""
     N = train.shape[0]
     dev = train.device
     args = make_args(train, rollout, ids, attention, action, layout, batch, seq_len,
-                     cu_seqlens, events=events)
+                     cu_seqlens, events=events, vocab_real=vocab_real, transforms=transforms)
     if ws is None:
         ws = workspace(DRIFT_OP_SELECTED_LOGPROB, N, args.vocab, args.logits_dtype, dev)
     if out is None:
@@ -255,10 +282,10 @@ class ScoringStep:
 
     def __init__(self, train, rollout, ids, attention=None, action=None, layout="right",
                  batch=0, seq_len=0, cu_seqlens=None, eps_low=0.2, eps_high=0.2,
-                 stream=None):
+                 stream=None, vocab_real=None, transforms=(None, None)):
         dev = train.device
         self.args = make_args(train, rollout, ids, attention, action, layout, batch, seq_len,
-                              cu_seqlens)
+                              cu_seqlens, vocab_real=vocab_real, transforms=transforms)
         self.N = int(self.args.num_rows)
         self.eps = (float(eps_low), float(eps_high))
         self.ws = workspace(DRIFT_OP_SELECTED_LOGPROB, self.N, self.args.vocab,

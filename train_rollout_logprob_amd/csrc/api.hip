@@ -1,5 +1,6 @@
 // C entry points of the drift library: argument checks (fail closed, before any launch),
 // workspace sizing, dispatch to the kernels, status readback and the backend descriptor.
+#include <math.h>
 #include <string.h>
 
 #include "common.h"
@@ -78,10 +79,34 @@ int drift_selected_logprob(const drift_logprob_args* a, float* train_logp, float
     default:
       return DRIFT_EINVAL;
   }
+  if (a->vocab_real < 0 || a->vocab_real > V) return DRIFT_EINVAL;
+  const int64_t Vr = a->vocab_real == 0 ? V : a->vocab_real;
+  for (int side = 0; side < 2; ++side) {
+    const drift_transform& t = a->transforms[side];
+    if (t.count < 0 || t.count > DRIFT_MAX_TRANSFORMS) return DRIFT_EINVAL;
+    for (int i = 0; i < t.count; ++i) {
+      const float v = t.value[i];
+      if (!(v == v) || v == INFINITY || v == -INFINITY) return DRIFT_EINVAL;
+      if (t.op[i] == DRIFT_XF_SCALE) continue;
+      if ((t.op[i] == DRIFT_XF_TEMPERATURE || t.op[i] == DRIFT_XF_SOFTCAP) && v > 0.0f) continue;
+      return DRIFT_EINVAL;
+    }
+  }
   if (!ws || !aligned(ws, 256) || ws_bytes < kLogprobWsBytes) return DRIFT_EWORKSPACE;
   ScoreParams sp;
   sp.N = N;
-  sp.V = V;
+  sp.V = Vr;
+  for (int side = 0; side < 2; ++side) {
+    const drift_transform& t = a->transforms[side];
+    sp.xf_n[side] = t.count;
+    for (int i = 0; i < DRIFT_MAX_TRANSFORMS; ++i) {
+      const bool used = i < t.count;
+      sp.xf_op[side][i] = used ? t.op[i] : 0;
+      const float v = used ? t.value[i] : 1.0f;
+      sp.xf_inv[side][i] = (float)(1.0 / (double)v);
+      sp.xf_v[side][i] = (used && t.op[i] == DRIFT_XF_TEMPERATURE) ? sp.xf_inv[side][i] : v;
+    }
+  }
   sp.stride = a->row_stride;
   sp.L = a->layout == DRIFT_PACKED ? 1 : a->seq_len;
   sp.nseq = a->num_seqs;

@@ -35,8 +35,12 @@ __device__ __forceinline__ void record_error(WsHeader* h, ErrClass c, int64_t ro
 
 // ---- launchers (each defined next to its kernels) --------------------------------
 struct ScoreParams {
-  int64_t N, V, stride, L, nseq;
+  int64_t N, V, stride, L, nseq;  // V: columns that enter the log-sum-exp
   int32_t dtype, ids_i64, layout;
+  int32_t xf_n[2];                // transform steps per side (train, rollout)
+  int32_t xf_op[2][DRIFT_MAX_TRANSFORMS];
+  float xf_v[2][DRIFT_MAX_TRANSFORMS];   // the value (the reciprocal for TEMPERATURE)
+  float xf_inv[2][DRIFT_MAX_TRANSFORMS]; // 1 / value
   const void* train;
   const void* rollout;
   const void* ids;

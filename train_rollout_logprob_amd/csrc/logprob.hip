@@ -117,14 +117,34 @@ template <> struct Elem<uint16_t> {  // bf16 bit patterns
   }
 };
 
+// Ordered logit transforms of one side ("[WS2] Framework for ablation experiment",
+// LogProb knobs row 7), applied to a group in place. The branches are uniform: the chain
+// is an argument of the call.
+template <int VEC>
+__device__ __forceinline__ void apply_chain(float (&x)[VEC], const ScoreParams& p, int side) {
+#pragma unroll
+  for (int i = 0; i < DRIFT_MAX_TRANSFORMS; ++i) {
+    if (i >= p.xf_n[side]) break;
+    const float v = p.xf_v[side][i];
+    if (p.xf_op[side][i] == DRIFT_XF_SOFTCAP) {
+      const float inv = p.xf_inv[side][i];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) x[e] = v * tanhf(x[e] * inv);
+    } else {  // SCALE multiplies by the value, TEMPERATURE by its reciprocal
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) x[e] = x[e] * v;
+    }
+  }
+}
+
 // Lane `tid` owns the 16-byte groups g = tid, tid + NT, tid + 2NT, ... of the row and
 // pushes them in ascending order; the last partial group (V % VEC logits, padded with
 // -inf) belongs to the lane that would own group V / VEC. All lanes run the same number
 // of pushes (missing groups are all -inf and add exactly 0). U groups per side are
 // loaded ahead for memory-level parallelism; U does not change the arithmetic.
-template <typename T, int NT, int U, bool kAligned>
+template <typename T, int NT, int U, bool kAligned, bool XF>
 __device__ __forceinline__ void stream_row(const char* rt, const char* rr, int64_t V, int tid,
-                                           Acc& at, Acc& ar) {
+                                           Acc& at, Acc& ar, const ScoreParams& p) {
   constexpr int VEC = Elem<T>::kVec;
   const int64_t nfull = V / VEC;                      // complete groups
   const int64_t ngroups = (V + VEC - 1) / VEC;        // including the ragged one
@@ -146,8 +166,10 @@ __device__ __forceinline__ void stream_row(const char* rt, const char* rr, int64
       for (int u = 0; u < U; ++u) {
         float x[VEC];
         Elem<T>::unpack(bt[u], x);
+        if constexpr (XF) apply_chain<VEC>(x, p, 0);
         push<VEC>(at, x);
         Elem<T>::unpack(br[u], x);
+        if constexpr (XF) apply_chain<VEC>(x, p, 1);
         push<VEC>(ar, x);
       }
     }
@@ -165,6 +187,10 @@ __device__ __forceinline__ void stream_row(const char* rt, const char* rr, int64
         xt[e] = (i < V) ? Elem<T>::load1(rt, i) : -INFINITY;
         xr[e] = (i < V) ? Elem<T>::load1(rr, i) : -INFINITY;
       }
+    }
+    if constexpr (XF) {
+      apply_chain<VEC>(xt, p, 0);
+      apply_chain<VEC>(xr, p, 1);
     }
     push<VEC>(at, xt);
     push<VEC>(ar, xr);
@@ -199,7 +225,7 @@ __global__ void __launch_bounds__(256) init_header(ScoreParams p) {
 
 // One block per row: thread 0 classifies and validates the row; active rows with a valid
 // id are streamed by the whole block.
-template <typename T, int NT, int U>
+template <typename T, int NT, int U, bool XF>
 __global__ void __launch_bounds__(NT) score_rows(ScoreParams p) {
   constexpr int NW = NT / 64;
   __shared__ float s_k[2][NW];
@@ -238,9 +264,9 @@ __global__ void __launch_bounds__(NT) score_rows(ScoreParams p) {
   const char* rr = (const char*)p.rollout + off;
   Acc at = {-INFINITY, 0.0}, ar = {-INFINITY, 0.0};
   if ((((uintptr_t)rt | (uintptr_t)rr) & 15) == 0) {
-    stream_row<T, NT, U, true>(rt, rr, p.V, tid, at, ar);
+    stream_row<T, NT, U, true, XF>(rt, rr, p.V, tid, at, ar, p);
   } else {
-    stream_row<T, NT, U, false>(rt, rr, p.V, tid, at, ar);
+    stream_row<T, NT, U, false, XF>(rt, rr, p.V, tid, at, ar, p);
   }
 
   // lanes (fixed butterfly), then waves in index order
@@ -269,8 +295,16 @@ __global__ void __launch_bounds__(NT) score_rows(ScoreParams p) {
       T_ = merge(T_, Acc{s_k[0][w], s_s[0][w]});
       R_ = merge(R_, Acc{s_k[1][w], s_s[1][w]});
     }
-    const float xty = Elem<T>::load1(rt, y);
-    const float xry = Elem<T>::load1(rr, y);
+    float xty = Elem<T>::load1(rt, y);
+    float xry = Elem<T>::load1(rr, y);
+    if constexpr (XF) {  // the selected logit goes through the same chain
+      float one[1] = {xty};
+      apply_chain<1>(one, p, 0);
+      xty = one[0];
+      one[0] = xry;
+      apply_chain<1>(one, p, 1);
+      xry = one[0];
+    }
     const double lse_t = lse_of(T_);
     const double lse_r = lse_of(R_);
     p.out_t[r] = (float)((double)xty - lse_t);
@@ -309,13 +343,19 @@ hipError_t launch_score(const ScoreParams& p, hipStream_t s, hipEvent_t ev0, hip
   if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
   if (p.N > 0) {
     const dim3 grid((unsigned)p.N);
+    const bool xf = p.xf_n[0] > 0 || p.xf_n[1] > 0;
+    constexpr int NB = DRIFT_SCORE_THREADS_BF16, UB = DRIFT_SCORE_UNROLL_BF16;
+    constexpr int NF = DRIFT_SCORE_THREADS_F32, UF = DRIFT_SCORE_UNROLL_F32;
     if (p.dtype == DRIFT_BF16) {
-      hipLaunchKernelGGL(
-          (score_rows<uint16_t, DRIFT_SCORE_THREADS_BF16, DRIFT_SCORE_UNROLL_BF16>), grid,
-          dim3(DRIFT_SCORE_THREADS_BF16), 0, s, p);
+      if (xf)
+        hipLaunchKernelGGL((score_rows<uint16_t, NB, UB, true>), grid, dim3(NB), 0, s, p);
+      else
+        hipLaunchKernelGGL((score_rows<uint16_t, NB, UB, false>), grid, dim3(NB), 0, s, p);
     } else {
-      hipLaunchKernelGGL((score_rows<float, DRIFT_SCORE_THREADS_F32, DRIFT_SCORE_UNROLL_F32>),
-                         grid, dim3(DRIFT_SCORE_THREADS_F32), 0, s, p);
+      if (xf)
+        hipLaunchKernelGGL((score_rows<float, NF, UF, true>), grid, dim3(NF), 0, s, p);
+      else
+        hipLaunchKernelGGL((score_rows<float, NF, UF, false>), grid, dim3(NF), 0, s, p);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
