@@ -15,6 +15,8 @@ It is a plain, slow, textbook implementation in float64 numpy / Python:
                     Cross-Config Logprob Drift Contract", section "Diagnostics" table).
 * ``lmhead``      - hidden x W_vocab followed by the same log-softmax gather (page "[WS2]
                     Framework for ablation experiment", LogProb knobs rows 9 and 10).
+* ``training``    - entropy of the softmax and dlogits of the selected logprob (LogProb
+                    knobs row 11).
 
 Each function is pinned by tests against closed forms, brute force at 50 decimal digits
 and textbook library routines; none is "parity unpinned".
@@ -23,6 +25,10 @@ from .logprob import (STATUS, widen, logsumexp_row, selected_logprob, validate_i
                       active_rows, score_row, score_rows, apply_transforms, TRANSFORMS)
 from .diagnostics import diagnostics, nearest_rank
 from .lmhead import lmhead_logprob
+from .training import (chain_derivative, dlogits_row, dlogits_rows, entropy_row, entropy_rows,
+                       softmax_row)
 
 __all__ = ["STATUS", "widen", "logsumexp_row", "selected_logprob", "validate_inputs",
-           "active_rows", "score_row", "score_rows", "apply_transforms", "TRANSFORMS", "diagnostics", "nearest_rank", "lmhead_logprob"]
+           "active_rows", "score_row", "score_rows", "apply_transforms", "TRANSFORMS", "diagnostics", "nearest_rank", "lmhead_logprob",
+           "entropy_row", "entropy_rows", "dlogits_row", "dlogits_rows", "chain_derivative",
+           "softmax_row"]

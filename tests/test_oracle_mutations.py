@@ -9,7 +9,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PIN_TESTS = ["tests/test_oracle_logprob.py", "tests/test_oracle_diagnostics.py",
-             "tests/test_oracle_lmhead.py"]
+             "tests/test_oracle_lmhead.py", "tests/test_oracle_training.py"]
 
 MUTATIONS = [
     ("logprob.py", "lpt = xt - lt", "lpt = lt - xt"),                          # sign
@@ -33,6 +33,14 @@ MUTATIONS = [
     ("logprob.py", "            x = x * v", "            x = x / v"),                 # scale
     ("logprob.py", "x = v * np.tanh(x / v)", "x = np.tanh(x / v)"),               # soft cap
     ("logprob.py", "        V = int(vocab_real)", "        pass"),                      # mask
+    ("training.py", "-math.fsum((p[nz] * (x[nz] - lse)).tolist())",
+     "-math.fsum((p[nz] * x[nz]).tolist())"),                                   # entropy
+    ("training.py", "g[int(y)] += 1.0", "g[int(y)] -= 1.0"),                      # dlogits
+    ("training.py", "d = d * (1.0 - t * t)", "d = d * (1.0 - t)"),                # cap slope
+    ("training.py", "            d = d / v", "            d = d * v"),              # temp slope
+    ("training.py", "g = dlogits_row(z, y) * chain_derivative(x, transform)",
+     "g = dlogits_row(z, y)"),                                                   # chain rule
+    ("training.py", "out[r, :Vr] = np.nan", "out[r, :Vr] = 0.0"),                 # bad id
     ("lmhead.py", "z[i, int(ids[r])]", "z[i, int(ids[i])]"),
     ("lmhead.py", "z = h @ weight_f64", "z = (h[:, ::-1] @ weight_f64)"),        # reversed K
 ]
