@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define DRIFT_ABI_VERSION 2
+#define DRIFT_ABI_VERSION 3
 
 /* ---- status codes ---------------------------------------------------------------- */
 #define DRIFT_OK          0
@@ -116,6 +116,15 @@ typedef struct drift_transform {
  *  transforms      [0] train side, [1] rollout side: ordered logit transforms applied to
  *                  every logit of that side (the selected one included) before the
  *                  softmax (LogProb knobs row 7). count = 0 on both sides = none.
+ *  entropy         optional outputs ([0] train, [1] rollout; NULL = not computed): fp32
+ *                  [N] device arrays, the entropy -sum_v p_v log p_v of the row's softmax
+ *                  (after the transforms, over the vocab_real columns), from the same pass
+ *                  (LogProb knobs row 11, entropy reduction). 0 on inactive rows, NaN on
+ *                  active rows with a rejected id.
+ *  lse             optional outputs ([0] train, [1] rollout; NULL = not written): fp64 [N]
+ *                  device arrays, the natural-log LSE of the row (the input of
+ *                  drift_dlogits). 0 on inactive rows, NaN on active rows with a rejected
+ *                  id. Writing it costs no extra pass.
  *
  * A row is active iff attention != 0 and action != 0 (and, PACKED, it is before the end).
  */
@@ -139,6 +148,8 @@ typedef struct drift_logprob_args {
   void* prof_events[2];
   int64_t vocab_real;
   drift_transform transforms[2];
+  float* entropy[2];
+  double* lse[2];
 } drift_logprob_args;
 
 /* Statistics of drift_diagnostics ("Diagnostics" table; every metric over active rows).
@@ -237,6 +248,31 @@ int drift_diagnostics(const float* dlogp, const uint8_t* active, int64_t num_row
 int drift_lmhead_logprob(const void* hidden, const void* weight, int64_t T, int64_t H,
                          int64_t V, const int32_t* target_ids, const uint8_t* active,
                          float* logp, void* ws, size_t ws_bytes, void* stream);
+
+/* Gradient of the selected-token logprob of one side with respect to its stored logits
+ * ("[WS2] Framework for ablation experiment", LogProb knobs row 11: dlogits), for the
+ * backward pass of a loss L over logp. For an active row r with selected id y, upstream
+ * gradient g_r = dL/dlogp_r and z = chain(x) (the side's transform chain):
+ *   grad_logits[r, v] = g_r * ([v == y] - exp(z_v - lse[r])) * dz_v/dx_v   for v < vocab_real
+ *                     = 0                                                  for vocab_real <= v < V
+ * Inactive rows (active[r] == 0) are written with zeros; columns past V (up to out_stride)
+ * are not touched. NaN lse (a row the forward pass rejected) gives a NaN row.
+ *   args        the drift_selected_logprob arguments of the forward pass: logits_dtype,
+ *               ids_dtype, num_rows, vocab, row_stride, the side's logits, target_ids,
+ *               vocab_real and transforms[side] are read; masks and layout are not (the
+ *               forward pass's `active` carries them)
+ *   side        0 = train logits, 1 = rollout logits
+ *   lse         fp64 [N] device: args->lse[side] written by the forward pass
+ *   active      uint8 [N] device: the forward pass's `active`
+ *   grad_logp   fp32 [N] device, or NULL = 1 on every row
+ *   out_dtype   DRIFT_F32, or DRIFT_BF16 (rounded to nearest even: the gradient
+ *               downcast point of row 11)
+ *   grad_logits [N, out_stride] of out_dtype, out_stride >= V; caller-owned
+ * Elementwise: each row is read once and written once. Asynchronous; returns EINVAL /
+ * EDTYPE for bad arguments before any launch, EHIP if the launch fails. */
+int drift_dlogits(const drift_logprob_args* args, int side, const double* lse,
+                  const uint8_t* active, const float* grad_logp, int out_dtype,
+                  void* grad_logits, int64_t out_stride, void* stream);
 
 const drift_backend_desc* drift_backend_descriptor(void);
 

@@ -20,7 +20,7 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     assert names == sorted(["drift_workspace_size", "drift_selected_logprob",
                             "drift_get_status", "drift_diagnostics", "drift_lmhead_logprob",
-                            "drift_backend_descriptor", "drift_strerror"])
+                            "drift_dlogits", "drift_backend_descriptor", "drift_strerror"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -34,16 +34,18 @@ def test_library_exports_every_declared_symbol():
 def test_struct_layouts_match_header():
     from train_rollout_logprob_amd import binding as B
     # drift_logprob_args: 4 x i32, 3 x i64, 5 pointers, 2 x i64, pointer, i64, 2 pointers,
-    # i64 vocab_real, 2 x drift_transform (i32 count, 4 x i32 op, 4 x f32 value)
+    # i64 vocab_real, 2 x drift_transform (i32 count, 4 x i32 op, 4 x f32 value),
+    # 2 entropy pointers, 2 lse pointers (offsets 208 and 224, as gcc lays out the header)
     assert ctypes.sizeof(B.drift_transform) == 36
-    assert ctypes.sizeof(B.drift_logprob_args) == 16 + 24 + 40 + 16 + 8 + 8 + 16 + 8 + 72
+    assert ctypes.sizeof(B.drift_logprob_args) == 16 + 24 + 40 + 16 + 8 + 8 + 16 + 8 + 72 + 32
+    assert B.drift_logprob_args.entropy.offset == 208 and B.drift_logprob_args.lse.offset == 224
     assert ctypes.sizeof(B.drift_stats) == 5 * 8 + 5 * 8 + 3 * 4 + 4
 
 
 def test_descriptor_and_strerror():
     from train_rollout_logprob_amd import binding as B
     d = B.drift_backend_descriptor()
-    assert d["abi_version"] == 2 and d["archs"] == "gfx950"
+    assert d["abi_version"] == 3 and d["archs"] == "gfx950"
     assert "batch composition" in d["determinism"]
     assert d["lse_domain"] == "natural log"
     assert d["build_fingerprint"].startswith("src:")
@@ -118,3 +120,24 @@ def test_host_checks_fail_closed_without_launching():
     a.transforms[0].value[0] = 1.0
     assert lib.drift_selected_logprob(ctypes.byref(a), None, None, None, None, None, 0,
                                       None) == B.DRIFT_EINVAL
+
+
+def test_dlogits_host_checks_fail_closed_without_launching():
+    from train_rollout_logprob_amd import binding as B
+    f = B.lib.drift_dlogits
+    a = B.drift_logprob_args()
+    a.logits_dtype, a.ids_dtype, a.layout = B.DRIFT_BF16, B.DRIFT_I64, B.DRIFT_PAD_RIGHT
+    a.num_rows, a.vocab, a.row_stride = 0, 10, 10
+    assert f(None, 0, None, None, None, B.DRIFT_F32, None, 10, None) == B.DRIFT_EINVAL
+    assert f(ctypes.byref(a), 2, None, None, None, B.DRIFT_F32, None, 10, None) == B.DRIFT_EINVAL
+    assert f(ctypes.byref(a), 0, None, None, None, B.DRIFT_I32, None, 10, None) == B.DRIFT_EDTYPE
+    assert f(ctypes.byref(a), 1, None, None, None, B.DRIFT_BF16, None, 9, None) == B.DRIFT_EINVAL
+    assert f(ctypes.byref(a), 1, None, None, None, B.DRIFT_BF16, None, 10, None) == B.DRIFT_OK
+    a.num_rows = 4                                                    # outputs required
+    assert f(ctypes.byref(a), 0, None, None, None, B.DRIFT_F32, None, 10, None) == B.DRIFT_EINVAL
+    a.num_rows, a.vocab_real = 0, 11
+    assert f(ctypes.byref(a), 0, None, None, None, B.DRIFT_F32, None, 10, None) == B.DRIFT_EINVAL
+    a.vocab_real = 0
+    B.set_chain(a.transforms[0], [("temperature", -2.0)])
+    assert f(ctypes.byref(a), 0, None, None, None, B.DRIFT_F32, None, 10, None) == B.DRIFT_EINVAL
+    assert f(ctypes.byref(a), 1, None, None, None, B.DRIFT_F32, None, 10, None) == B.DRIFT_OK

@@ -38,8 +38,8 @@ XF_CODES = {"scale": DRIFT_XF_SCALE, "temperature": DRIFT_XF_TEMPERATURE,
             "softcap": DRIFT_XF_SOFTCAP}
 
 EXPORTS = ("drift_workspace_size", "drift_selected_logprob", "drift_get_status",
-           "drift_diagnostics", "drift_lmhead_logprob", "drift_backend_descriptor",
-           "drift_strerror")
+           "drift_diagnostics", "drift_lmhead_logprob", "drift_dlogits",
+           "drift_backend_descriptor", "drift_strerror")
 
 
 class drift_transform(ctypes.Structure):
@@ -57,7 +57,8 @@ class drift_logprob_args(ctypes.Structure):
                 ("batch", ctypes.c_int64), ("seq_len", ctypes.c_int64),
                 ("cu_seqlens", ctypes.c_void_p), ("num_seqs", ctypes.c_int64),
                 ("prof_events", ctypes.c_void_p * 2), ("vocab_real", ctypes.c_int64),
-                ("transforms", drift_transform * 2)]
+                ("transforms", drift_transform * 2), ("entropy", ctypes.c_void_p * 2),
+                ("lse", ctypes.c_void_p * 2)]
 
 
 class drift_stats(ctypes.Structure):
@@ -98,6 +99,9 @@ def _load():
     lib.drift_diagnostics.restype = ctypes.c_int
     lib.drift_lmhead_logprob.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]
     lib.drift_lmhead_logprob.restype = ctypes.c_int
+    lib.drift_dlogits.argtypes = [ctypes.POINTER(drift_logprob_args), ctypes.c_int, vp, vp, vp,
+                                  ctypes.c_int, vp, i64, vp]
+    lib.drift_dlogits.restype = ctypes.c_int
     lib.drift_backend_descriptor.argtypes = []
     lib.drift_backend_descriptor.restype = ctypes.POINTER(drift_backend_desc)
     lib.drift_strerror.argtypes = [ctypes.c_int]
@@ -141,6 +145,13 @@ def drift_lmhead_logprob(hidden, weight, T: int, H: int, V: int, target_ids, act
     return int(lib.drift_lmhead_logprob(_ptr(hidden), _ptr(weight), T, H, V, _ptr(target_ids),
                                         _ptr(active), _ptr(logp), _ptr(ws), ws_bytes,
                                         _stream(stream)))
+
+
+def drift_dlogits(args: drift_logprob_args, side: int, lse, active, grad_logp, out_dtype: int,
+                  grad_logits, out_stride: int, stream=None) -> int:
+    return int(lib.drift_dlogits(ctypes.byref(args), side, _ptr(lse), _ptr(active),
+                                 _ptr(grad_logp), out_dtype, _ptr(grad_logits), out_stride,
+                                 _stream(stream)))
 
 
 def drift_backend_descriptor() -> dict:
@@ -202,10 +213,12 @@ def set_chain(t: drift_transform, chain):
 
 def make_args(train, rollout, ids, attention=None, action=None, layout="right", batch=0,
               seq_len=0, cu_seqlens=None, vocab=None, events=None, vocab_real=None,
-              transforms=(None, None)) -> drift_logprob_args:
+              transforms=(None, None), entropy=(None, None), lse=(None, None)
+              ) -> drift_logprob_args:
     """Describe torch tensors to the C ABI (no copies, no conversions). `vocab_real`:
     leading columns that enter the log-sum-exp (None = all); `transforms`: (train chain,
-    rollout chain), each [(kind, value), ...]."""
+    rollout chain), each [(kind, value), ...]; `entropy` / `lse`: optional per-side
+    output tensors (fp32 / fp64 [N])."""
     if train.dtype != rollout.dtype or train.shape != rollout.shape:
         raise ValueError("train and rollout logits must share dtype and shape")
     if train.stride(1) != 1 or rollout.stride(0) != train.stride(0):
@@ -233,19 +246,30 @@ def make_args(train, rollout, ids, attention=None, action=None, layout="right", 
     a.vocab_real = 0 if vocab_real is None else int(vocab_real)
     set_chain(a.transforms[0], transforms[0])
     set_chain(a.transforms[1], transforms[1])
+    for side in (0, 1):
+        e, l = entropy[side], lse[side]
+        if e is not None and (e.dtype != torch.float32 or e.numel() < a.num_rows):
+            raise ValueError("entropy outputs are fp32 [N]")
+        if l is not None and (l.dtype != torch.float64 or l.numel() < a.num_rows):
+            raise ValueError("lse outputs are fp64 [N]")
+        a.entropy[side] = e.data_ptr() if e is not None else None
+        a.lse[side] = l.data_ptr() if l is not None else None
     return a
 
 
 def selected_logprob(train, rollout, ids, attention=None, action=None, layout="right",
                      batch=0, seq_len=0, cu_seqlens=None, ws=None, out=None, stream=None,
-                     events=None, check=False, vocab_real=None, transforms=(None, None)):
+                     events=None, check=False, vocab_real=None, transforms=(None, None),
+                     entropy=(None, None), lse=(None, None)):
     """Allocate outputs (and a workspace unless given) and call drift_selected_logprob.
     Returns (train_logp, rollout_logp, dlogp, active, ws). With check=True, synchronizes
-    and raises DriftError on a data-dependent status."""
+    and raises DriftError on a data-dependent status. `entropy` / `lse`: optional output
+    tensors per side, filled by the same call."""
     N = train.shape[0]
     dev = train.device
     args = make_args(train, rollout, ids, attention, action, layout, batch, seq_len,
-                     cu_seqlens, events=events, vocab_real=vocab_real, transforms=transforms)
+                     cu_seqlens, events=events, vocab_real=vocab_real, transforms=transforms,
+                     entropy=entropy, lse=lse)
     if ws is None:
         ws = workspace(DRIFT_OP_SELECTED_LOGPROB, N, args.vocab, args.logits_dtype, dev)
     if out is None:
@@ -272,6 +296,28 @@ def diagnostics(dlogp, active, eps_low=0.2, eps_high=0.2, logprob_ws=None, ws=No
     st, s = drift_diagnostics(dlogp, active, N, eps_low, eps_high, logprob_ws, ws, ws.numel(),
                               stream)
     return st, s.as_dict()
+
+
+def dlogits(train, rollout, ids, side, lse, active, grad_logp=None, out_dtype=torch.float32,
+            out=None, vocab_real=None, transforms=(None, None), stream=None):
+    """Call drift_dlogits for one side (0 = train, 1 = rollout): the gradient of that side's
+    selected logprob with respect to its logits, given the forward pass's `lse[side]` and
+    `active`. Returns the [N, V] gradient tensor (out_dtype float32 or bfloat16)."""
+    args = make_args(train, rollout, ids, vocab_real=vocab_real, transforms=transforms)
+    N, V = int(args.num_rows), int(args.vocab)
+    code = {torch.float32: DRIFT_F32, torch.bfloat16: DRIFT_BF16}.get(out_dtype, 99)
+    if out is None:
+        out = torch.empty(N, V, dtype=out_dtype, device=train.device)
+    if out.dim() != 2 or out.shape[0] != N or out.stride(1) != 1:
+        raise ValueError("out must be [N, >= V] with contiguous rows")
+    if lse.dtype != torch.float64 or active.dtype != torch.uint8:
+        raise ValueError("lse must be float64 and active uint8")
+    if grad_logp is not None and grad_logp.dtype != torch.float32:
+        raise ValueError("grad_logp must be float32")
+    st = drift_dlogits(args, side, lse, active, grad_logp, code, out, out.stride(0), stream)
+    if st != DRIFT_OK:
+        raise DriftError(st, "drift_dlogits")
+    return out
 
 
 class ScoringStep:

@@ -14,8 +14,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdrift.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ["api.hip", "logprob.hip", "diagnostics.hip", "lmhead.hip"]
-HEADERS = ["common.h", "classify.h", "lse.h"]
+SOURCES = ["api.hip", "logprob.hip", "diagnostics.hip", "lmhead.hip", "dlogits.hip"]
+HEADERS = ["common.h", "classify.h", "lse.h", "rowio.h"]
 
 ARCH = "gfx950"
 FLAGS = [

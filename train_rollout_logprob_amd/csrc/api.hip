@@ -26,6 +26,34 @@ int status_from_header(const WsHeader& h, int64_t* first_bad) {
   return st;
 }
 
+// Transform chain checks: at most DRIFT_MAX_TRANSFORMS known steps with finite values,
+// positive for TEMPERATURE and SOFTCAP.
+bool chain_ok(const drift_transform& t) {
+  if (t.count < 0 || t.count > DRIFT_MAX_TRANSFORMS) return false;
+  for (int i = 0; i < t.count; ++i) {
+    const float v = t.value[i];
+    if (!(v == v) || v == INFINITY || v == -INFINITY) return false;
+    if (t.op[i] == DRIFT_XF_SCALE) continue;
+    if ((t.op[i] == DRIFT_XF_TEMPERATURE || t.op[i] == DRIFT_XF_SOFTCAP) && v > 0.0f) continue;
+    return false;
+  }
+  return true;
+}
+
+// The kernels' form of a checked chain: TEMPERATURE multiplies by the reciprocal.
+Chain make_chain(const drift_transform& t) {
+  Chain c;
+  c.n = t.count;
+  for (int i = 0; i < DRIFT_MAX_TRANSFORMS; ++i) {
+    const bool used = i < t.count;
+    c.op[i] = used ? t.op[i] : 0;
+    const float v = used ? t.value[i] : 1.0f;
+    c.inv[i] = (float)(1.0 / (double)v);
+    c.v[i] = (used && t.op[i] == DRIFT_XF_TEMPERATURE) ? c.inv[i] : v;
+  }
+  return c;
+}
+
 }  // namespace
 
 extern "C" {
@@ -81,32 +109,18 @@ int drift_selected_logprob(const drift_logprob_args* a, float* train_logp, float
   }
   if (a->vocab_real < 0 || a->vocab_real > V) return DRIFT_EINVAL;
   const int64_t Vr = a->vocab_real == 0 ? V : a->vocab_real;
+  if (!chain_ok(a->transforms[0]) || !chain_ok(a->transforms[1])) return DRIFT_EINVAL;
   for (int side = 0; side < 2; ++side) {
-    const drift_transform& t = a->transforms[side];
-    if (t.count < 0 || t.count > DRIFT_MAX_TRANSFORMS) return DRIFT_EINVAL;
-    for (int i = 0; i < t.count; ++i) {
-      const float v = t.value[i];
-      if (!(v == v) || v == INFINITY || v == -INFINITY) return DRIFT_EINVAL;
-      if (t.op[i] == DRIFT_XF_SCALE) continue;
-      if ((t.op[i] == DRIFT_XF_TEMPERATURE || t.op[i] == DRIFT_XF_SOFTCAP) && v > 0.0f) continue;
+    if ((a->entropy[side] && !aligned(a->entropy[side], 4)) ||
+        (a->lse[side] && !aligned(a->lse[side], 8)))
       return DRIFT_EINVAL;
-    }
   }
   if (!ws || !aligned(ws, 256) || ws_bytes < kLogprobWsBytes) return DRIFT_EWORKSPACE;
   ScoreParams sp;
   sp.N = N;
   sp.V = Vr;
-  for (int side = 0; side < 2; ++side) {
-    const drift_transform& t = a->transforms[side];
-    sp.xf_n[side] = t.count;
-    for (int i = 0; i < DRIFT_MAX_TRANSFORMS; ++i) {
-      const bool used = i < t.count;
-      sp.xf_op[side][i] = used ? t.op[i] : 0;
-      const float v = used ? t.value[i] : 1.0f;
-      sp.xf_inv[side][i] = (float)(1.0 / (double)v);
-      sp.xf_v[side][i] = (used && t.op[i] == DRIFT_XF_TEMPERATURE) ? sp.xf_inv[side][i] : v;
-    }
-  }
+  sp.xf[0] = make_chain(a->transforms[0]);
+  sp.xf[1] = make_chain(a->transforms[1]);
   sp.stride = a->row_stride;
   sp.L = a->layout == DRIFT_PACKED ? 1 : a->seq_len;
   sp.nseq = a->num_seqs;
@@ -123,6 +137,10 @@ int drift_selected_logprob(const drift_logprob_args* a, float* train_logp, float
   sp.out_r = rollout_logp;
   sp.out_d = dlogp;
   sp.active = active;
+  for (int side = 0; side < 2; ++side) {
+    sp.ent[side] = a->entropy[side];
+    sp.lse[side] = a->lse[side];
+  }
   sp.ws = (char*)ws;
   if (launch_score(sp, (hipStream_t)stream, (hipEvent_t)a->prof_events[0],
                    (hipEvent_t)a->prof_events[1]) != hipSuccess)
@@ -190,11 +208,54 @@ int drift_lmhead_logprob(const void* hidden, const void* weight, int64_t T, int6
   return DRIFT_OK;
 }
 
+int drift_dlogits(const drift_logprob_args* a, int side, const double* lse,
+                  const uint8_t* active, const float* grad_logp, int out_dtype,
+                  void* grad_logits, int64_t out_stride, void* stream) {
+  if (!a || (side != 0 && side != 1)) return DRIFT_EINVAL;
+  if (a->logits_dtype != DRIFT_F32 && a->logits_dtype != DRIFT_BF16) return DRIFT_EDTYPE;
+  if (a->ids_dtype != DRIFT_I32 && a->ids_dtype != DRIFT_I64) return DRIFT_EDTYPE;
+  if (out_dtype != DRIFT_F32 && out_dtype != DRIFT_BF16) return DRIFT_EDTYPE;
+  const int64_t N = a->num_rows, V = a->vocab;
+  if (N < 0 || N > INT32_MAX || V < 1 || V > INT32_MAX || a->row_stride < V || out_stride < V)
+    return DRIFT_EINVAL;
+  if (a->vocab_real < 0 || a->vocab_real > V) return DRIFT_EINVAL;
+  const drift_transform& t = a->transforms[side];
+  if (!chain_ok(t)) return DRIFT_EINVAL;
+  const void* logits = side == 0 ? a->train_logits : a->rollout_logits;
+  const size_t esz = a->logits_dtype == DRIFT_F32 ? 4 : 2;
+  const size_t isz = a->ids_dtype == DRIFT_I32 ? 4 : 8;
+  const size_t osz = out_dtype == DRIFT_F32 ? 4 : 2;
+  if (N > 0) {
+    if (!logits || !a->target_ids || !lse || !active || !grad_logits) return DRIFT_EINVAL;
+    if (!aligned(logits, esz) || !aligned(a->target_ids, isz) || !aligned(lse, 8) ||
+        !aligned(grad_logits, osz) || (grad_logp && !aligned(grad_logp, 4)))
+      return DRIFT_EINVAL;
+  }
+  DlogitsParams dp;
+  dp.N = N;
+  dp.V = V;
+  dp.Vr = a->vocab_real == 0 ? V : a->vocab_real;
+  dp.stride = a->row_stride;
+  dp.out_stride = out_stride;
+  dp.dtype = a->logits_dtype;
+  dp.ids_i64 = a->ids_dtype == DRIFT_I64;
+  dp.out_dtype = out_dtype;
+  dp.xf = make_chain(t);
+  dp.logits = logits;
+  dp.ids = a->target_ids;
+  dp.lse = lse;
+  dp.active = active;
+  dp.grad = grad_logp;
+  dp.out = grad_logits;
+  if (launch_dlogits(dp, (hipStream_t)stream) != hipSuccess) return DRIFT_EHIP;
+  return DRIFT_OK;
+}
+
 const drift_backend_desc* drift_backend_descriptor(void) {
   static const drift_backend_desc d = {
       DRIFT_ABI_VERSION,
       "drift.gfx950.v1",
-      "selected_token_logprob,dlogp,drift_diagnostics,lmhead_selected_logprob",
+      "selected_token_logprob,dlogp,entropy,lse,drift_diagnostics,lmhead_selected_logprob,dlogits",
       "gfx950",
       "logits:f32,bf16;ids:i32,i64;lmhead:bf16",
       "pad_right,pad_left,packed(cu_seqlens);logits row-major [N,row_stride]",

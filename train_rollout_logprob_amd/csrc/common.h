@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "drift.h"
+#include "rowio.h"
 
 namespace drift {
 
@@ -37,10 +38,7 @@ __device__ __forceinline__ void record_error(WsHeader* h, ErrClass c, int64_t ro
 struct ScoreParams {
   int64_t N, V, stride, L, nseq;  // V: columns that enter the log-sum-exp
   int32_t dtype, ids_i64, layout;
-  int32_t xf_n[2];                // transform steps per side (train, rollout)
-  int32_t xf_op[2][DRIFT_MAX_TRANSFORMS];
-  float xf_v[2][DRIFT_MAX_TRANSFORMS];   // the value (the reciprocal for TEMPERATURE)
-  float xf_inv[2][DRIFT_MAX_TRANSFORMS]; // 1 / value
+  Chain xf[2];                    // transform chain per side (train, rollout)
   const void* train;
   const void* rollout;
   const void* ids;
@@ -51,6 +49,8 @@ struct ScoreParams {
   float* out_r;
   float* out_d;
   uint8_t* active;
+  float* ent[2];   // optional per-row entropy of each side's softmax
+  double* lse[2];  // optional per-row natural-log LSE of each side
   char* ws;
 };
 // Launches the header initialisation and the scoring kernel; `ev` (nullable) are recorded
@@ -89,5 +89,18 @@ struct LmheadParams {
 };
 size_t lmhead_ws_bytes(int64_t T, int64_t H, int64_t V);
 hipError_t launch_lmhead(const LmheadParams& p, hipStream_t s);
+
+struct DlogitsParams {
+  int64_t N, V, Vr, stride, out_stride;  // Vr: columns that entered the log-sum-exp
+  int32_t dtype, ids_i64, out_dtype;
+  Chain xf;
+  const void* logits;
+  const void* ids;
+  const double* lse;
+  const uint8_t* active;
+  const float* grad;  // nullable: 1 on every active row
+  void* out;
+};
+hipError_t launch_dlogits(const DlogitsParams& p, hipStream_t s);
 
 }  // namespace drift

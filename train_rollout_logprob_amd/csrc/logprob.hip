@@ -26,29 +26,39 @@
 // The selected logit is read once by its single owner (LogProb knobs row 8).
 #include <math.h>
 
+#include <type_traits>
+
 #include "classify.h"
 #include "common.h"
 #include "lse.h"
+#include "rowio.h"
 
 namespace drift {
 namespace {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
 constexpr float kRaise = 16.0f;  // a group sum at or above this raises the wave's k
 
-template <int VEC>
-__device__ __forceinline__ float group_sum(const float (&x)[VEC], float nk) {
-  float e[VEC];
+// exp2 terms of one group in fp32, summed pairwise; with ENT also the first moment of
+// the exponent (sum of 2^a a, a = x*log2e - k; -inf exponents contribute 0).
+template <int VEC, bool ENT>
+__device__ __forceinline__ void group_sums(const float (&x)[VEC], float nk, float& t, float& t2) {
+  float e[VEC], w[VEC];
 #pragma unroll
-  for (int i = 0; i < VEC; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(x[i], kLog2e, nk));
-  // pairwise fp32 sum of the group
-#pragma unroll
-  for (int w = 1; w < VEC; w *= 2) {
-#pragma unroll
-    for (int i = 0; i + w < VEC; i += 2 * w) e[i] = e[i] + e[i + w];
+  for (int i = 0; i < VEC; ++i) {
+    const float a = fmaf(x[i], kLog2e, nk);
+    e[i] = __builtin_amdgcn_exp2f(a);
+    if constexpr (ENT) w[i] = e[i] * fmaxf(a, -1.0e30f);
   }
-  return e[0];
+#pragma unroll
+  for (int st = 1; st < VEC; st *= 2) {
+#pragma unroll
+    for (int i = 0; i + st < VEC; i += 2 * st) {
+      e[i] = e[i] + e[i + st];
+      if constexpr (ENT) w[i] = w[i] + w[i + st];
+    }
+  }
+  t = e[0];
+  t2 = ENT ? w[0] : 0.0f;
 }
 
 __device__ __forceinline__ float wave_max(float m) {
@@ -57,11 +67,14 @@ __device__ __forceinline__ float wave_max(float m) {
   return m;
 }
 
-// Adds one group of VEC logits to a lane's partial. Every lane of the wave calls it at
-// the same point (groups past the end of the row are all -inf), so k stays wave-uniform.
-template <int VEC>
-__device__ __forceinline__ void push(Acc& a, const float (&x)[VEC]) {
-  float t = group_sum<VEC>(x, -a.k);
+// Adds one group of VEC logits to a lane's partial (Acc, or AccE with the entropy moment).
+// Every lane of the wave calls it at the same point (groups past the end of the row are all
+// -inf), so k stays wave-uniform.
+template <int VEC, typename A>
+__device__ __forceinline__ void push(A& a, const float (&x)[VEC]) {
+  constexpr bool ENT = std::is_same<A, AccE>::value;
+  float t, t2;
+  group_sums<VEC, ENT>(x, -a.k, t, t2);
   if (__ballot(!(t < kRaise))) {  // wave-uniform: raise k
     float m = x[0];
 #pragma unroll
@@ -71,7 +84,9 @@ __device__ __forceinline__ void push(Acc& a, const float (&x)[VEC]) {
     if (kn > a.k) {
       if (kn == INFINITY) {
         a.s = NAN;  // +inf logit, or |x| too large for the fp32 exponent: fail closed
+        if constexpr (ENT) a.s2 = NAN;
       } else {
+        if constexpr (ENT) a.s2 = rescale2(a.s2, a.s, a.k, kn);
         a.s = rescale(a.s, a.k, kn);
         a.k = kn;
       }
@@ -82,59 +97,13 @@ __device__ __forceinline__ void push(Acc& a, const float (&x)[VEC]) {
 #pragma unroll
       for (int i = 0; i < VEC; ++i)
         if (!(x[i] == -INFINITY)) t = NAN;
+      t2 = t;
     } else {
-      t = group_sum<VEC>(x, -a.k);
+      group_sums<VEC, ENT>(x, -a.k, t, t2);
     }
   }
   a.s += (double)t;
-}
-
-template <typename T> struct Elem;
-template <> struct Elem<float> {
-  static constexpr int kVec = 4;
-  __device__ static __forceinline__ void unpack(const u32x4& v, float (&x)[4]) {
-    x[0] = __uint_as_float(v.x);
-    x[1] = __uint_as_float(v.y);
-    x[2] = __uint_as_float(v.z);
-    x[3] = __uint_as_float(v.w);
-  }
-  __device__ static __forceinline__ float load1(const void* p, int64_t i) {
-    return ((const float*)p)[i];
-  }
-};
-template <> struct Elem<uint16_t> {  // bf16 bit patterns
-  static constexpr int kVec = 8;
-  __device__ static __forceinline__ void unpack(const u32x4& v, float (&x)[8]) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[2 * j] = __uint_as_float(w[j] << 16);
-      x[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
-    }
-  }
-  __device__ static __forceinline__ float load1(const void* p, int64_t i) {
-    return __uint_as_float(((uint32_t)((const uint16_t*)p)[i]) << 16);
-  }
-};
-
-// Ordered logit transforms of one side ("[WS2] Framework for ablation experiment",
-// LogProb knobs row 7), applied to a group in place. The branches are uniform: the chain
-// is an argument of the call.
-template <int VEC>
-__device__ __forceinline__ void apply_chain(float (&x)[VEC], const ScoreParams& p, int side) {
-#pragma unroll
-  for (int i = 0; i < DRIFT_MAX_TRANSFORMS; ++i) {
-    if (i >= p.xf_n[side]) break;
-    const float v = p.xf_v[side][i];
-    if (p.xf_op[side][i] == DRIFT_XF_SOFTCAP) {
-      const float inv = p.xf_inv[side][i];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) x[e] = v * tanhf(x[e] * inv);
-    } else {  // SCALE multiplies by the value, TEMPERATURE by its reciprocal
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) x[e] = x[e] * v;
-    }
-  }
+  if constexpr (ENT) a.s2 += (double)t2;
 }
 
 // Lane `tid` owns the 16-byte groups g = tid, tid + NT, tid + 2NT, ... of the row and
@@ -142,9 +111,9 @@ __device__ __forceinline__ void apply_chain(float (&x)[VEC], const ScoreParams& 
 // -inf) belongs to the lane that would own group V / VEC. All lanes run the same number
 // of pushes (missing groups are all -inf and add exactly 0). U groups per side are
 // loaded ahead for memory-level parallelism; U does not change the arithmetic.
-template <typename T, int NT, int U, bool kAligned, bool XF>
+template <typename T, int NT, int U, bool kAligned, bool XF, typename A>
 __device__ __forceinline__ void stream_row(const char* rt, const char* rr, int64_t V, int tid,
-                                           Acc& at, Acc& ar, const ScoreParams& p) {
+                                           A& at, A& ar, const ScoreParams& p) {
   constexpr int VEC = Elem<T>::kVec;
   const int64_t nfull = V / VEC;                      // complete groups
   const int64_t ngroups = (V + VEC - 1) / VEC;        // including the ragged one
@@ -166,10 +135,10 @@ __device__ __forceinline__ void stream_row(const char* rt, const char* rr, int64
       for (int u = 0; u < U; ++u) {
         float x[VEC];
         Elem<T>::unpack(bt[u], x);
-        if constexpr (XF) apply_chain<VEC>(x, p, 0);
+        if constexpr (XF) apply_chain<VEC>(x, p.xf[0]);
         push<VEC>(at, x);
         Elem<T>::unpack(br[u], x);
-        if constexpr (XF) apply_chain<VEC>(x, p, 1);
+        if constexpr (XF) apply_chain<VEC>(x, p.xf[1]);
         push<VEC>(ar, x);
       }
     }
@@ -184,13 +153,21 @@ __device__ __forceinline__ void stream_row(const char* rt, const char* rr, int64
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         const int64_t i = g * VEC + e;
-        xt[e] = (i < V) ? Elem<T>::load1(rt, i) : -INFINITY;
-        xr[e] = (i < V) ? Elem<T>::load1(rr, i) : -INFINITY;
+        xt[e] = (i < V) ? Elem<T>::load1(rt, i) : 0.0f;
+        xr[e] = (i < V) ? Elem<T>::load1(rr, i) : 0.0f;
       }
     }
     if constexpr (XF) {
-      apply_chain<VEC>(xt, p, 0);
-      apply_chain<VEC>(xr, p, 1);
+      apply_chain<VEC>(xt, p.xf[0]);
+      apply_chain<VEC>(xr, p.xf[1]);
+    }
+    // columns past the end are -inf after the chain (a chain may map -inf to a finite value)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      if (g * VEC + e >= V) {
+        xt[e] = -INFINITY;
+        xr[e] = -INFINITY;
+      }
     }
     push<VEC>(at, xt);
     push<VEC>(ar, xr);
@@ -225,11 +202,13 @@ __global__ void __launch_bounds__(256) init_header(ScoreParams p) {
 
 // One block per row: thread 0 classifies and validates the row; active rows with a valid
 // id are streamed by the whole block.
-template <typename T, int NT, int U, bool XF>
+template <typename T, int NT, int U, bool XF, bool ENT>
 __global__ void __launch_bounds__(NT) score_rows(ScoreParams p) {
+  using A = std::conditional_t<ENT, AccE, Acc>;
   constexpr int NW = NT / 64;
   __shared__ float s_k[2][NW];
   __shared__ double s_s[2][NW];
+  __shared__ double s_s2[2][ENT ? NW : 1];
   __shared__ int64_t s_y;
   WsHeader* h = (WsHeader*)p.ws;
   const int64_t r = blockIdx.x;
@@ -244,14 +223,16 @@ __global__ void __launch_bounds__(NT) score_rows(ScoreParams p) {
     p.active[r] = c.active ? 1 : 0;
     if (c.err & (1u << kErrMask)) record_error(h, kErrMask, r);
     if (c.err & (1u << kErrToken)) record_error(h, kErrToken, r);
-    if (!c.active) {
-      p.out_t[r] = 0.0f;
-      p.out_r[r] = 0.0f;
-      p.out_d[r] = 0.0f;
-    } else if (!c.score) {
-      p.out_t[r] = NAN;
-      p.out_r[r] = NAN;
-      p.out_d[r] = NAN;
+    if (!c.score) {  // inactive rows get 0, active rows with a bad id NaN
+      const float f = c.active ? NAN : 0.0f;
+      p.out_t[r] = f;
+      p.out_r[r] = f;
+      p.out_d[r] = f;
+#pragma unroll
+      for (int side = 0; side < 2; ++side) {
+        if (p.ent[side]) p.ent[side][r] = f;
+        if (p.lse[side]) p.lse[side][r] = (double)f;
+      }
     }
     s_y = c.score ? c.y : -1;
   }
@@ -262,7 +243,10 @@ __global__ void __launch_bounds__(NT) score_rows(ScoreParams p) {
   const size_t off = (size_t)r * (size_t)p.stride * sizeof(T);
   const char* rt = (const char*)p.train + off;
   const char* rr = (const char*)p.rollout + off;
-  Acc at = {-INFINITY, 0.0}, ar = {-INFINITY, 0.0};
+  A at, ar;
+  at.k = ar.k = -INFINITY;
+  at.s = ar.s = 0.0;
+  if constexpr (ENT) at.s2 = ar.s2 = 0.0;
   if ((((uintptr_t)rt | (uintptr_t)rr) & 15) == 0) {
     stream_row<T, NT, U, true, XF>(rt, rr, p.V, tid, at, ar, p);
   } else {
@@ -272,11 +256,15 @@ __global__ void __launch_bounds__(NT) score_rows(ScoreParams p) {
   // lanes (fixed butterfly), then waves in index order
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    Acc bt, br;
+    A bt, br;
     bt.k = __shfl_xor(at.k, o);
     bt.s = __shfl_xor(at.s, o);
     br.k = __shfl_xor(ar.k, o);
     br.s = __shfl_xor(ar.s, o);
+    if constexpr (ENT) {
+      bt.s2 = __shfl_xor(at.s2, o);
+      br.s2 = __shfl_xor(ar.s2, o);
+    }
     at = merge(at, bt);
     ar = merge(ar, br);
   }
@@ -286,23 +274,34 @@ __global__ void __launch_bounds__(NT) score_rows(ScoreParams p) {
     s_s[0][wave] = at.s;
     s_k[1][wave] = ar.k;
     s_s[1][wave] = ar.s;
+    if constexpr (ENT) {
+      s_s2[0][wave] = at.s2;
+      s_s2[1][wave] = ar.s2;
+    }
   }
   __syncthreads();
   if (tid == 0) {
-    Acc T_ = {s_k[0][0], s_s[0][0]}, R_ = {s_k[1][0], s_s[1][0]};
+    auto lds = [&](int side, int w) {
+      A v;
+      v.k = s_k[side][w];
+      v.s = s_s[side][w];
+      if constexpr (ENT) v.s2 = s_s2[side][w];
+      return v;
+    };
+    A T_ = lds(0, 0), R_ = lds(1, 0);
 #pragma unroll
     for (int w = 1; w < NW; ++w) {
-      T_ = merge(T_, Acc{s_k[0][w], s_s[0][w]});
-      R_ = merge(R_, Acc{s_k[1][w], s_s[1][w]});
+      T_ = merge(T_, lds(0, w));
+      R_ = merge(R_, lds(1, w));
     }
     float xty = Elem<T>::load1(rt, y);
     float xry = Elem<T>::load1(rr, y);
     if constexpr (XF) {  // the selected logit goes through the same chain
       float one[1] = {xty};
-      apply_chain<1>(one, p, 0);
+      apply_chain<1>(one, p.xf[0]);
       xty = one[0];
       one[0] = xry;
-      apply_chain<1>(one, p, 1);
+      apply_chain<1>(one, p.xf[1]);
       xry = one[0];
     }
     const double lse_t = lse_of(T_);
@@ -310,6 +309,12 @@ __global__ void __launch_bounds__(NT) score_rows(ScoreParams p) {
     p.out_t[r] = (float)((double)xty - lse_t);
     p.out_r[r] = (float)((double)xry - lse_r);
     p.out_d[r] = (float)(((double)xty - (double)xry) - (lse_t - lse_r));
+    if (p.lse[0]) p.lse[0][r] = lse_t;
+    if (p.lse[1]) p.lse[1][r] = lse_r;
+    if constexpr (ENT) {
+      if (p.ent[0]) p.ent[0][r] = (float)entropy_of(T_);
+      if (p.ent[1]) p.ent[1][r] = (float)entropy_of(R_);
+    }
     const bool ok = lse_ok(T_) && lse_ok(R_) && (xty > -INFINITY) && (xry > -INFINITY);
     if (!ok) record_error(h, kErrNonfinite, r);
   }
@@ -343,20 +348,24 @@ hipError_t launch_score(const ScoreParams& p, hipStream_t s, hipEvent_t ev0, hip
   if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
   if (p.N > 0) {
     const dim3 grid((unsigned)p.N);
-    const bool xf = p.xf_n[0] > 0 || p.xf_n[1] > 0;
+    const bool xf = p.xf[0].n > 0 || p.xf[1].n > 0;
+    const bool ent = p.ent[0] != nullptr || p.ent[1] != nullptr;
     constexpr int NB = DRIFT_SCORE_THREADS_BF16, UB = DRIFT_SCORE_UNROLL_BF16;
     constexpr int NF = DRIFT_SCORE_THREADS_F32, UF = DRIFT_SCORE_UNROLL_F32;
+#define DRIFT_SCORE_LAUNCH(T, NT, U, X, E) \
+  hipLaunchKernelGGL((score_rows<T, NT, U, X, E>), grid, dim3(NT), 0, s, p)
     if (p.dtype == DRIFT_BF16) {
-      if (xf)
-        hipLaunchKernelGGL((score_rows<uint16_t, NB, UB, true>), grid, dim3(NB), 0, s, p);
-      else
-        hipLaunchKernelGGL((score_rows<uint16_t, NB, UB, false>), grid, dim3(NB), 0, s, p);
+      if (xf && ent) DRIFT_SCORE_LAUNCH(uint16_t, NB, UB, true, true);
+      else if (xf) DRIFT_SCORE_LAUNCH(uint16_t, NB, UB, true, false);
+      else if (ent) DRIFT_SCORE_LAUNCH(uint16_t, NB, UB, false, true);
+      else DRIFT_SCORE_LAUNCH(uint16_t, NB, UB, false, false);
     } else {
-      if (xf)
-        hipLaunchKernelGGL((score_rows<float, NF, UF, true>), grid, dim3(NF), 0, s, p);
-      else
-        hipLaunchKernelGGL((score_rows<float, NF, UF, false>), grid, dim3(NF), 0, s, p);
+      if (xf && ent) DRIFT_SCORE_LAUNCH(float, NF, UF, true, true);
+      else if (xf) DRIFT_SCORE_LAUNCH(float, NF, UF, true, false);
+      else if (ent) DRIFT_SCORE_LAUNCH(float, NF, UF, false, true);
+      else DRIFT_SCORE_LAUNCH(float, NF, UF, false, false);
     }
+#undef DRIFT_SCORE_LAUNCH
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;

@@ -43,4 +43,42 @@ __device__ __forceinline__ double lse_of(const Acc& a) { return ((double)a.k + l
 // A finite, non-empty partial (some logit finite, none NaN or +inf).
 __device__ __forceinline__ bool lse_ok(const Acc& a) { return a.s > 0.0 && a.s < INFINITY; }
 
+// Partial with the first moment of the exponent, for the entropy of the softmax:
+// s2 = sum_i 2^(a_i) a_i with a_i = x_i*log2e - k. Then, with p_i = 2^(a_i) / s,
+//   H = -sum_i p_i ln p_i = ln2 (log2 s - s2 / s)
+// ("[WS2] Framework for ablation experiment", LogProb knobs row 11, entropy). Moving the
+// reference from k to K >= k shifts every a_i by k - K, so
+//   s2 -> 2^(k-K) (s2 - (K - k) s),   s -> 2^(k-K) s.
+struct AccE {
+  float k;
+  double s;
+  double s2;
+};
+
+__device__ __forceinline__ double rescale2(double s2, double s, float k, float K) {
+  return (k == -INFINITY) ? s2
+                          : ldexp(s2 - (double)(K - k) * s, (int)fmaxf(k - K, -2048.0f));
+}
+
+__device__ __forceinline__ AccE merge(const AccE& a, const AccE& b) {
+  AccE r;
+  r.k = fmaxf(a.k, b.k);
+  if (r.k == -INFINITY) {
+    r.s = a.s + b.s;
+    r.s2 = a.s2 + b.s2;
+  } else {
+    r.s2 = rescale2(a.s2, a.s, a.k, r.k) + rescale2(b.s2, b.s, b.k, r.k);
+    r.s = rescale(a.s, a.k, r.k) + rescale(b.s, b.k, r.k);
+  }
+  return r;
+}
+
+__device__ __forceinline__ double lse_of(const AccE& a) {
+  return ((double)a.k + log2(a.s)) * kLn2;
+}
+__device__ __forceinline__ bool lse_ok(const AccE& a) { return a.s > 0.0 && a.s < INFINITY; }
+__device__ __forceinline__ double entropy_of(const AccE& a) {
+  return (log2(a.s) - a.s2 / a.s) * kLn2;
+}
+
 }  // namespace drift
