@@ -9,6 +9,10 @@ Prints ONE JSON line (rank 0). `roofline` is for the dominant kernel (the paired
 kernel): algorithmic bytes = active rows x V x 2 bytes x 2 sides, divided by its average
 duration measured with HIP events recorded by the library around that kernel on the launch
 stream. `cpu_baseline` is the fp64 CPU oracle timed on a bounded sample of the same rows.
+
+Two further legs are reported beside the main line, outside its timed region: `training`
+(the scoring kernel with per-row entropy and LSE written, and the dlogits kernel on the
+same batch) and `lmhead` (the fused LM-head selected logprob).
 """
 import argparse
 import json
@@ -33,34 +37,40 @@ WORKLOAD_TEXT = {
 }
 
 
-SCORE_SOURCES = ("logprob.hip", "classify.h", "lse.h", "common.h")
+SCORE_SOURCES = ("logprob.hip", "classify.h", "lse.h", "common.h", "rowio.h")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "score_rows_bf16_qwen8b.md")
+DLOGITS_SOURCES = ("dlogits.hip", "classify.h", "common.h", "rowio.h")
+DLOGITS_PROFILE = os.path.join(ROOT, "profiles", "dlogits_rows_bf16_qwen8b.md")
 
 
-def score_source_hash():
-    """Hash of the scoring kernel's sources, to tie a recorded counter reading to them."""
+def source_hash(files=SCORE_SOURCES):
+    """Hash of a kernel's sources, to tie a recorded counter reading to them."""
     import hashlib
 
     h = hashlib.sha256()
-    for f in SCORE_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "train_rollout_logprob_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic():
-    """HBM bytes per launch of the scoring kernel from the committed PMC summary
-    (FETCH_SIZE + WRITE_SIZE, calibrated on a copy of known size), or None when the
-    kernel's sources changed since the counters were taken."""
+def score_source_hash():
+    return source_hash(SCORE_SOURCES)
+
+
+def recorded_traffic(profile=TRAFFIC_PROFILE, files=SCORE_SOURCES):
+    """HBM bytes per launch of a kernel from its committed PMC summary (FETCH_SIZE +
+    WRITE_SIZE, calibrated on a copy of known size), or None when the kernel's sources
+    changed since the counters were taken."""
     try:
         vals = {}
-        with open(TRAFFIC_PROFILE) as fh:
+        with open(profile) as fh:
             for line in fh:
                 if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch",
                                                           "traffic_sources"):
                     k, v = line.split(":", 1)
                     vals[k] = v.strip()
-        if vals.get("traffic_sources") != score_source_hash():
+        if vals.get("traffic_sources") != source_hash(files):
             return None
         return float(vals["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -128,6 +138,70 @@ def lmhead_leg(steps=5, warmup=2):
             "flop_per_call": flop}
 
 
+def training_leg(case, ids, att, act, cu, steps=10, warmup=2):
+    """Training-only state on the same batch: the scoring kernel with per-row entropy and
+    LSE written for both sides (kernel time from events on the launch stream), then
+    drift_dlogits of the train side into bf16 with a per-row upstream gradient."""
+    import torch
+
+    from train_rollout_logprob_amd import binding as B
+
+    dev = case.train.device
+    N, V, esz = case.N, case.V, case.elem_bytes
+    n_active = case.n_active()
+    ent = tuple(torch.empty(N, dtype=torch.float32, device=dev) for _ in range(2))
+    lse = tuple(torch.empty(N, dtype=torch.float64, device=dev) for _ in range(2))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    out = None
+    for i in range(warmup + steps):
+        evs = (ev[2 * (i - warmup)].cuda_event, ev[2 * (i - warmup) + 1].cuda_event) \
+            if i >= warmup else None
+        out = B.selected_logprob(case.train, case.rollout, ids, att, act, case.layout, case.B,
+                                 case.L, cu, ws=out[4] if out else None,
+                                 out=out[:4] if out else None, events=evs, entropy=ent,
+                                 lse=lse)
+    torch.cuda.synchronize()
+    st, _ = B.drift_get_status(out[4])
+    if st != B.DRIFT_OK:
+        raise RuntimeError(f"scoring with entropy: status {B.STATUS_NAMES[st]}")
+    ent_ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)) / steps
+    ent_bytes = n_active * V * esz * 2
+    active = out[3]
+    g = torch.randn(N, dtype=torch.float32, device=dev, generator=torch.Generator(
+        device=dev).manual_seed(11))
+    grad = torch.empty((N, V), dtype=torch.bfloat16, device=dev)
+    for _ in range(warmup):
+        B.dlogits(case.train, case.rollout, ids, 0, lse[0], active, grad_logp=g,
+                  out_dtype=torch.bfloat16, out=grad)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        B.dlogits(case.train, case.rollout, ids, 0, lse[0], active, grad_logp=g,
+                  out_dtype=torch.bfloat16, out=grad)
+    e1.record()
+    torch.cuda.synchronize()
+    dl_ms = e0.elapsed_time(e1) / steps
+    dl_bytes = n_active * V * esz + N * V * 2
+    del grad
+    return {
+        "workload": "same batch; entropy + LSE of both sides from the scoring pass, then "
+                    "dlogits of the train side (bf16 out, upstream gradient per row)",
+        "score_with_entropy": {"kernel": f"score_rows<{case.dtype}, entropy>",
+                               "kernel_ms": ent_ms, "bytes_per_launch": ent_bytes,
+                               "achieved_gbs": ent_bytes / (ent_ms * 1e-3) / 1e9,
+                               "frac": ent_bytes / (ent_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "dlogits": {"kernel": f"dlogits_rows<{case.dtype}, bf16>", "kernel_ms": dl_ms,
+                    "bytes_per_launch": dl_bytes,
+                    "achieved_gbs": dl_bytes / (dl_ms * 1e-3) / 1e9,
+                    "frac": dl_bytes / (dl_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "traffic": recorded_traffic(DLOGITS_PROFILE, DLOGITS_SOURCES)
+                    if case.name == "qwen8b" else None},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,6 +212,8 @@ def main():
     ap.add_argument("--workload", default="qwen8b",
                     choices=["qwen8b", "large", "packed", "tiny", "lmhead"],
                     help="scoring workload (the benchmark line is quoted on qwen8b)")
+    ap.add_argument("--no-training", action="store_true",
+                    help="skip the entropy / dlogits leg reported beside the main line")
     ap.add_argument("--no-lmhead", action="store_true",
                     help="skip the fused LM-head leg reported beside the main line")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
@@ -167,7 +243,22 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-        log(f"[bench] copied {n} bytes 3 times (read {n} and write {n} per copy)")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        e0.record()
+        for _ in range(5):
+            dst.fill_(7)
+        e1.record()
+        torch.cuda.synchronize()
+        ms_fill = e0.elapsed_time(e1) / 5
+        log(f"[bench] copied {n} bytes 8 times (read {n} and write {n} per copy): "
+            f"{ms:.3f} ms per copy = {2 * n / (ms * 1e-3) / 1e9:.0f} GB/s read+write; "
+            f"fill {ms_fill:.3f} ms = {n / (ms_fill * 1e-3) / 1e9:.0f} GB/s write")
         return
     if args.workload == "lmhead":
         print(json.dumps(lmhead_leg(args.steps, args.warmup)), flush=True)
@@ -222,9 +313,6 @@ def main():
         f"({achieved:.0f} GB/s), {value / 1e6:.3f} M active tok/s")
 
     cpu = None
-    if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (oracle)")
-        cpu = cpu_baseline(case, args.cpu_seconds)
 
     line = {
         "metric": METRIC,
@@ -252,11 +340,19 @@ def main():
                      "bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
     }
+    del runner
+    if not args.no_training and args.xf == "none":
+        log("[bench] training-state leg (entropy, lse, dlogits)")
+        torch.cuda.empty_cache()
+        line["training"] = training_leg(case, ids, att, act, cu)
     if not args.no_lmhead and args.workload == "qwen8b" and args.xf == "none":
-        del runner, case
         torch.cuda.empty_cache()
         log("[bench] fused LM-head leg")
         line["lmhead"] = lmhead_leg()
+    # the CPU leg runs last, so the GPU legs above run at the clocks of a busy GPU
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

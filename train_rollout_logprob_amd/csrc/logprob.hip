@@ -39,26 +39,25 @@ namespace {
 constexpr float kRaise = 16.0f;  // a group sum at or above this raises the wave's k
 
 // exp2 terms of one group in fp32, summed pairwise; with ENT also the first moment of
-// the exponent (sum of 2^a a, a = x*log2e - k; -inf exponents contribute 0).
+// the exponent, sum of 2^a * a over the group (a = x*log2e - k) as a chain of fp32 FMAs in
+// element order; -inf exponents contribute 0.
 template <int VEC, bool ENT>
 __device__ __forceinline__ void group_sums(const float (&x)[VEC], float nk, float& t, float& t2) {
-  float e[VEC], w[VEC];
+  float e[VEC];
+  float w = 0.0f;
 #pragma unroll
   for (int i = 0; i < VEC; ++i) {
     const float a = fmaf(x[i], kLog2e, nk);
     e[i] = __builtin_amdgcn_exp2f(a);
-    if constexpr (ENT) w[i] = e[i] * fmaxf(a, -1.0e30f);
+    if constexpr (ENT) w = fmaf(e[i], fmaxf(a, -1.0e30f), w);
   }
 #pragma unroll
   for (int st = 1; st < VEC; st *= 2) {
 #pragma unroll
-    for (int i = 0; i + st < VEC; i += 2 * st) {
-      e[i] = e[i] + e[i + st];
-      if constexpr (ENT) w[i] = w[i] + w[i + st];
-    }
+    for (int i = 0; i + st < VEC; i += 2 * st) e[i] = e[i] + e[i + st];
   }
   t = e[0];
-  t2 = ENT ? w[0] : 0.0f;
+  t2 = w;
 }
 
 __device__ __forceinline__ float wave_max(float m) {
