@@ -23,12 +23,12 @@ and textbook library routines; none is "parity unpinned".
 """
 from .logprob import (STATUS, widen, logsumexp_row, selected_logprob, validate_inputs,
                       active_rows, score_row, score_rows, apply_transforms, TRANSFORMS)
-from .diagnostics import diagnostics, nearest_rank
+from .diagnostics import diagnostics, nearest_rank, segment_diagnostics
 from .lmhead import lmhead_logprob
 from .training import (chain_derivative, dlogits_row, dlogits_rows, entropy_row, entropy_rows,
                        softmax_row)
 
 __all__ = ["STATUS", "widen", "logsumexp_row", "selected_logprob", "validate_inputs",
-           "active_rows", "score_row", "score_rows", "apply_transforms", "TRANSFORMS", "diagnostics", "nearest_rank", "lmhead_logprob",
+           "active_rows", "score_row", "score_rows", "apply_transforms", "TRANSFORMS", "diagnostics", "nearest_rank", "segment_diagnostics", "lmhead_logprob",
            "entropy_row", "entropy_rows", "dlogits_row", "dlogits_rows", "chain_derivative",
            "softmax_row"]

@@ -11,7 +11,14 @@ Contract" (every metric over active response/action tokens only):
 * approx_kl0  = masked mean of exp(dlogp) - 1 - dlogp, evaluated as expm1(d) - d, which is
                 the same quantity without cancellation;
 * mean_abs_dlogp, and the max of |dlogp|;
-* p95 / p99 of |dlogp| by the nearest-rank rule: the ceil(q*n)-th smallest value.
+* p95 / p99 of |dlogp| by the nearest-rank rule: the ceil(q*n)-th smallest value;
+* mismatch_kl = forward mismatch KL of the "Attention Debug Matrix" Metrics section: the
+                k1 estimator of KL(rollout || train) from rollout-sampled tokens, the mean
+                of log pi_rollout(y) - log pi_train(y) = mean of -dlogp. (approx_kl0 is the
+                k3 estimator of the same KL, the metric that page calls mismatch_k3_kl.)
+
+Per-sequence / per-rank views ("Diagnostics" table, per-rank versions when distributed)
+are the same statistics over contiguous row segments given by offsets.
 
 Sums use ``math.fsum`` (correctly rounded). Percentiles come from a full sort. The
 worst-token row is the smallest row index attaining the maximum (the B1 acceptance list asks
@@ -45,7 +52,7 @@ def diagnostics(d, active, eps_low=0.2, eps_high=0.2):
            "argmax_row": -1, "ratio0": math.nan, "clipfrac0": math.nan,
            "approx_kl0": math.nan, "mean_abs_dlogp": math.nan, "mean_dlogp": math.nan,
            "p95_abs_dlogp": math.nan, "p99_abs_dlogp": math.nan,
-           "max_abs_dlogp": math.nan, "status": "OK"}
+           "max_abs_dlogp": math.nan, "mismatch_kl": math.nan, "status": "OK"}
     if n == 0:
         out["status"] = "ENOACTIVE"
         return out
@@ -71,6 +78,7 @@ def diagnostics(d, active, eps_low=0.2, eps_high=0.2):
     out["clipfrac0"] = (n_lo + n_hi) / n
     out["mean_abs_dlogp"] = math.fsum(abs(v) for v in vals) / n
     out["mean_dlogp"] = math.fsum(vals) / n
+    out["mismatch_kl"] = math.fsum(-v for v in vals) / n
     a = sorted(abs(v) for v in vals)
     out["p95_abs_dlogp"] = a[nearest_rank(n, 95, 100) - 1]
     out["p99_abs_dlogp"] = a[nearest_rank(n, 99, 100) - 1]
@@ -80,4 +88,26 @@ def diagnostics(d, active, eps_low=0.2, eps_high=0.2):
         if abs(v) == mx:
             out["argmax_row"] = int(r)
             break
+    return out
+
+
+def segment_diagnostics(d, active, offsets, eps_low=0.2, eps_high=0.2):
+    """Statistics of each segment [offsets[s], offsets[s+1]) of the rows (cu_seqlens for
+    sequences, b*L for batch rows, or one range per rank). argmax_row is the global row
+    index. A segment whose bounds are not 0 <= lo <= hi <= N gets status "EMASK"."""
+    d = np.asarray(d)
+    active = np.asarray(active)
+    N = len(d)
+    out = []
+    for s in range(len(offsets) - 1):
+        lo, hi = int(offsets[s]), int(offsets[s + 1])
+        if not 0 <= lo <= hi <= N:
+            bad = diagnostics(d[:0], active[:0], eps_low, eps_high)
+            bad["status"] = "EMASK"
+            out.append(bad)
+            continue
+        st = diagnostics(d[lo:hi], active[lo:hi], eps_low, eps_high)
+        if st["argmax_row"] >= 0:
+            st["argmax_row"] += lo
+        out.append(st)
     return out

@@ -141,3 +141,56 @@ def test_golden_worked_examples():
                 assert s[k] == want, (c["name"], k)
             else:
                 assert abs(s[k] - want) <= 1e-15 * max(1.0, abs(want)), (c["name"], k, s[k], want)
+
+
+def test_mismatch_kl_and_k3_equal_the_exact_forward_kl():
+    """Tokens drawn in exact proportion to a rational rollout law q, scored by a train law p:
+    the k1 mean of -dlogp and the k3 mean of exp(d) - 1 - d both equal KL(q || p) exactly
+    (E_q[p/q] = 1), the library routine scipy.stats.entropy(q, p) being the reference."""
+    from scipy.stats import entropy as kl
+    rng = np.random.default_rng(3)
+    counts = rng.integers(1, 40, size=23)
+    q = counts / counts.sum()
+    p = rng.dirichlet(np.ones(23))
+    d = np.repeat(np.log(p) - np.log(q), counts)            # dlogp = train - rollout
+    st = oracle.diagnostics(d, np.ones(len(d), np.uint8))
+    want = float(kl(q, p))
+    assert abs(st["mismatch_kl"] - want) <= 1e-12
+    assert abs(st["approx_kl0"] - want) <= 1e-12
+    # the reverse direction is a different number: the estimator is not symmetric by accident
+    assert abs(float(kl(p, q)) - want) > 1e-3
+
+
+def test_mismatch_kl_closed_forms():
+    act = np.ones(5, np.uint8)
+    st = oracle.diagnostics(np.full(5, -0.25), act)
+    assert st["mismatch_kl"] == 0.25 and abs(st["approx_kl0"] - (math.exp(-0.25) - 0.75)) < 1e-16
+    assert oracle.diagnostics(np.zeros(5), act)["mismatch_kl"] == 0.0
+    assert math.isnan(oracle.diagnostics(np.zeros(5), np.zeros(5))["mismatch_kl"])
+
+
+def test_segment_diagnostics_match_slices_and_the_whole():
+    rng = np.random.default_rng(8)
+    N = 3000
+    d = (rng.standard_t(3, N) * 1e-2).astype(np.float32)
+    act = (rng.random(N) < 0.8).astype(np.uint8)
+    offsets = np.array([0, 0, 17, 1000, 1001, 2500, 3000])
+    segs = oracle.segment_diagnostics(d, act, offsets)
+    assert segs[0]["status"] == "ENOACTIVE" and segs[0]["n_active"] == 0   # empty segment
+    assert sum(s["n_active"] for s in segs) == int(act.sum())
+    for s, (lo, hi) in zip(segs, zip(offsets[:-1], offsets[1:])):
+        if s["n_active"] == 0:
+            continue
+        a = np.abs(d[lo:hi][act[lo:hi] == 1].astype(np.float64))
+        assert s["max_abs_dlogp"] == a.max()
+        r = s["argmax_row"]
+        assert lo <= r < hi and act[r] == 1 and abs(float(d[r])) == a.max()
+        srt = np.sort(a)
+        assert s["p99_abs_dlogp"] == srt[math.ceil(0.99 * len(a) - 1e-9) - 1]
+    whole = oracle.segment_diagnostics(d, act, np.array([0, N]))[0]
+    ref = oracle.diagnostics(d, act)
+    for k in ref:
+        assert (whole[k] == ref[k]) or (isinstance(ref[k], float) and math.isnan(ref[k])), k
+    bad = oracle.segment_diagnostics(d, act, np.array([0, 10, 5, N]))
+    assert bad[1]["status"] == "EMASK" and bad[0]["status"] == "OK"
+    assert oracle.segment_diagnostics(d, act, np.array([0, N + 1]))[0]["status"] == "EMASK"

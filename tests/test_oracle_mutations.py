@@ -41,6 +41,9 @@ MUTATIONS = [
     ("training.py", "g = dlogits_row(z, y) * chain_derivative(x, transform)",
      "g = dlogits_row(z, y)"),                                                   # chain rule
     ("training.py", "out[r, :Vr] = np.nan", "out[r, :Vr] = 0.0"),                 # bad id
+    ("diagnostics.py", "math.fsum(-v for v in vals) / n", "math.fsum(vals) / n"),  # kl sign
+    ("diagnostics.py", 'st["argmax_row"] += lo', 'st["argmax_row"] += 0'),         # local row
+    ("diagnostics.py", "if not 0 <= lo <= hi <= N:", "if not 0 <= lo <= N:"),       # bounds
     ("lmhead.py", "z[i, int(ids[r])]", "z[i, int(ids[i])]"),
     ("lmhead.py", "z = h @ weight_f64", "z = (h[:, ::-1] @ weight_f64)"),        # reversed K
 ]
