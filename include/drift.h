@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define DRIFT_ABI_VERSION 3
+#define DRIFT_ABI_VERSION 4
 
 /* ---- status codes ---------------------------------------------------------------- */
 #define DRIFT_OK          0
@@ -156,7 +156,11 @@ typedef struct drift_logprob_args {
  *  ratio0          mean over active rows of exp(dlogp)
  *  clipfrac0       (n_clip_low + n_clip_high) / n_active; a ratio is clipped iff
  *                  exp(d) < 1 - eps_low or exp(d) > 1 + eps_high (evaluated in fp64)
- *  approx_kl0      mean of exp(d) - 1 - d, evaluated as expm1(d) - d in fp64
+ *  approx_kl0      mean of exp(d) - 1 - d, evaluated as expm1(d) - d in fp64: the k3
+ *                  estimator of KL(rollout || train) from rollout-sampled tokens
+ *                  ("Attention Debug Matrix", Metrics: mismatch_k3_kl)
+ *  mismatch_kl     mean of -d = mean of log pi_rollout(y) - log pi_train(y): the k1
+ *                  estimator of the same KL (the forward mismatch_kl of that section)
  *  mean_abs_dlogp  mean |d|;   mean_dlogp: mean d
  *  p95/p99_abs_dlogp  nearest rank: the ceil(q*n)-th smallest |d| (exact)
  *  max_abs_dlogp   the largest |d|; argmax_row: smallest row index attaining it
@@ -180,6 +184,7 @@ typedef struct drift_stats {
   float p99_abs_dlogp;
   float max_abs_dlogp;
   int32_t status;
+  double mismatch_kl;
 } drift_stats;
 
 /* Backend descriptor ("Kernel Integration Contract": stable id, semantic operator,
@@ -236,6 +241,22 @@ int drift_get_status(const void* ws, void* stream, int64_t* first_bad_row);
 int drift_diagnostics(const float* dlogp, const uint8_t* active, int64_t num_rows,
                       double eps_low, double eps_high, const void* logprob_ws,
                       drift_stats* out_host, void* ws, size_t ws_bytes, void* stream);
+
+/* The same statistics per segment of rows ("Diagnostics" table: per-sequence views, and
+ * the per-rank versions of a distributed run, each rank's rows being one segment).
+ *   seg_offsets   int32 [num_segments + 1] device: segment s is rows
+ *                 [seg_offsets[s], seg_offsets[s+1]) (cu_seqlens for packed sequences,
+ *                 b * L for batch rows); a segment with bounds outside 0 <= lo <= hi <= N
+ *                 gets status EMASK
+ *   out_dev       drift_stats [num_segments] device, caller-owned; argmax_row is the
+ *                 global row index; status per segment as drift_diagnostics returns it
+ *   logprob_ws    nullable, as for drift_diagnostics (its status outranks each segment's)
+ * Needs no workspace: each segment's reduction and exact radix select run in one block.
+ * Asynchronous; returns EINVAL for bad arguments before any launch. */
+int drift_segment_diagnostics(const float* dlogp, const uint8_t* active, int64_t num_rows,
+                              const int32_t* seg_offsets, int64_t num_segments,
+                              double eps_low, double eps_high, const void* logprob_ws,
+                              drift_stats* out_dev, void* stream);
 
 /* Fused LM-head selected logprob: logits z = hidden x W are formed tile by tile on the
  * matrix cores and never written to memory; logp[t] = z[t, y_t] - LSE(z[t]).

@@ -82,9 +82,10 @@ def assert_stats_exact(got, want):
             assert np.isnan(g), k
         else:
             assert abs(g - w) <= MEAN_RTOL * abs(w) + 1e-300, (k, g, w)
-    g, w = got["mean_dlogp"], want["mean_dlogp"]
-    if not np.isnan(w):
-        assert abs(g - w) <= MEAN_RTOL * max(abs(w), want["mean_abs_dlogp"]), (g, w)
+    for k in ("mean_dlogp", "mismatch_kl"):
+        g, w = got[k], want[k]
+        if not np.isnan(w):
+            assert abs(g - w) <= MEAN_RTOL * max(abs(w), want["mean_abs_dlogp"]), (k, g, w)
 
 
 def small_variants():

@@ -20,7 +20,8 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     assert names == sorted(["drift_workspace_size", "drift_selected_logprob",
                             "drift_get_status", "drift_diagnostics", "drift_lmhead_logprob",
-                            "drift_dlogits", "drift_backend_descriptor", "drift_strerror"])
+                            "drift_dlogits", "drift_segment_diagnostics",
+                            "drift_backend_descriptor", "drift_strerror"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -39,13 +40,14 @@ def test_struct_layouts_match_header():
     assert ctypes.sizeof(B.drift_transform) == 36
     assert ctypes.sizeof(B.drift_logprob_args) == 16 + 24 + 40 + 16 + 8 + 8 + 16 + 8 + 72 + 32
     assert B.drift_logprob_args.entropy.offset == 208 and B.drift_logprob_args.lse.offset == 224
-    assert ctypes.sizeof(B.drift_stats) == 5 * 8 + 5 * 8 + 3 * 4 + 4
+    assert ctypes.sizeof(B.drift_stats) == 5 * 8 + 5 * 8 + 3 * 4 + 4 + 8
+    assert B.drift_stats.mismatch_kl.offset == 96
 
 
 def test_descriptor_and_strerror():
     from train_rollout_logprob_amd import binding as B
     d = B.drift_backend_descriptor()
-    assert d["abi_version"] == 3 and d["archs"] == "gfx950"
+    assert d["abi_version"] == 4 and d["archs"] == "gfx950"
     assert "batch composition" in d["determinism"]
     assert d["lse_domain"] == "natural log"
     assert d["build_fingerprint"].startswith("src:")
@@ -141,3 +143,12 @@ def test_dlogits_host_checks_fail_closed_without_launching():
     B.set_chain(a.transforms[0], [("temperature", -2.0)])
     assert f(ctypes.byref(a), 0, None, None, None, B.DRIFT_F32, None, 10, None) == B.DRIFT_EINVAL
     assert f(ctypes.byref(a), 1, None, None, None, B.DRIFT_F32, None, 10, None) == B.DRIFT_OK
+
+
+def test_segment_diagnostics_host_checks():
+    from train_rollout_logprob_amd import binding as B
+    f = B.lib.drift_segment_diagnostics
+    assert f(None, None, 10, None, 0, 0.2, 0.2, None, None, None) == B.DRIFT_OK   # no segments
+    assert f(None, None, 10, None, 2, 0.2, 0.2, None, None, None) == B.DRIFT_EINVAL
+    assert f(None, None, -1, None, 0, 0.2, 0.2, None, None, None) == B.DRIFT_EINVAL
+    assert f(None, None, 10, None, 0, 0.2, 1.0, None, None, None) == B.DRIFT_EINVAL

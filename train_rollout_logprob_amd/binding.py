@@ -38,7 +38,8 @@ XF_CODES = {"scale": DRIFT_XF_SCALE, "temperature": DRIFT_XF_TEMPERATURE,
             "softcap": DRIFT_XF_SOFTCAP}
 
 EXPORTS = ("drift_workspace_size", "drift_selected_logprob", "drift_get_status",
-           "drift_diagnostics", "drift_lmhead_logprob", "drift_dlogits",
+           "drift_diagnostics", "drift_segment_diagnostics", "drift_lmhead_logprob",
+           "drift_dlogits",
            "drift_backend_descriptor", "drift_strerror")
 
 
@@ -68,7 +69,8 @@ class drift_stats(ctypes.Structure):
                 ("clipfrac0", ctypes.c_double), ("approx_kl0", ctypes.c_double),
                 ("mean_abs_dlogp", ctypes.c_double), ("mean_dlogp", ctypes.c_double),
                 ("p95_abs_dlogp", ctypes.c_float), ("p99_abs_dlogp", ctypes.c_float),
-                ("max_abs_dlogp", ctypes.c_float), ("status", ctypes.c_int32)]
+                ("max_abs_dlogp", ctypes.c_float), ("status", ctypes.c_int32),
+                ("mismatch_kl", ctypes.c_double)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -97,6 +99,9 @@ def _load():
     lib.drift_diagnostics.argtypes = [vp, vp, i64, ctypes.c_double, ctypes.c_double, vp,
                                       ctypes.POINTER(drift_stats), vp, sz, vp]
     lib.drift_diagnostics.restype = ctypes.c_int
+    lib.drift_segment_diagnostics.argtypes = [vp, vp, i64, vp, i64, ctypes.c_double,
+                                              ctypes.c_double, vp, vp, vp]
+    lib.drift_segment_diagnostics.restype = ctypes.c_int
     lib.drift_lmhead_logprob.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]
     lib.drift_lmhead_logprob.restype = ctypes.c_int
     lib.drift_dlogits.argtypes = [ctypes.POINTER(drift_logprob_args), ctypes.c_int, vp, vp, vp,
@@ -138,6 +143,15 @@ def drift_diagnostics(dlogp, active, num_rows: int, eps_low: float, eps_high: fl
                                    _ptr(logprob_ws), ctypes.byref(out), _ptr(ws), ws_bytes,
                                    _stream(stream)))
     return st, out
+
+
+def drift_segment_diagnostics(dlogp, active, num_rows: int, seg_offsets, num_segments: int,
+                              eps_low: float, eps_high: float, logprob_ws, out_dev,
+                              stream=None) -> int:
+    return int(lib.drift_segment_diagnostics(_ptr(dlogp), _ptr(active), num_rows,
+                                             _ptr(seg_offsets), num_segments, eps_low,
+                                             eps_high, _ptr(logprob_ws), _ptr(out_dev),
+                                             _stream(stream)))
 
 
 def drift_lmhead_logprob(hidden, weight, T: int, H: int, V: int, target_ids, active, logp, ws,
@@ -317,6 +331,47 @@ def dlogits(train, rollout, ids, side, lse, active, grad_logp=None, out_dtype=to
     st = drift_dlogits(args, side, lse, active, grad_logp, code, out, out.stride(0), stream)
     if st != DRIFT_OK:
         raise DriftError(st, "drift_dlogits")
+    return out
+
+
+def segment_diagnostics(dlogp, active, seg_offsets, eps_low=0.2, eps_high=0.2, logprob_ws=None,
+                        stream=None):
+    """Call drift_segment_diagnostics; seg_offsets is an int32 device tensor [S + 1].
+    Returns a list of S stats dicts (one synchronizing copy of the device results)."""
+    N = dlogp.shape[0]
+    if seg_offsets.dtype != torch.int32 or seg_offsets.dim() != 1 or seg_offsets.numel() < 1:
+        raise ValueError("seg_offsets must be an int32 vector [S + 1]")
+    S = seg_offsets.numel() - 1
+    out = torch.empty(max(S, 1) * ctypes.sizeof(drift_stats), dtype=torch.uint8,
+                      device=dlogp.device)
+    st = drift_segment_diagnostics(dlogp, active, N, seg_offsets, S, eps_low, eps_high,
+                                   logprob_ws, out, stream)
+    if st != DRIFT_OK:
+        raise DriftError(st, "drift_segment_diagnostics")
+    host = bytearray(out.cpu().numpy().tobytes())
+    arr = (drift_stats * max(S, 1)).from_buffer(host)
+    return [arr[i].as_dict() for i in range(S)]
+
+
+def report(stats: dict, segments=None, **metadata) -> dict:
+    """One JSON-ready report of a comparison ("Diagnostics" table, report layout): the
+    statistics, optional per-segment versions, and metadata (the backend descriptor plus
+    whatever the caller records: dtype, padding side, parallelism, cache mode, ...)."""
+    desc = drift_backend_descriptor()
+    out = {"metrics": {k: stats[k] for k in ("max_abs_dlogp", "mean_abs_dlogp",
+                                             "p95_abs_dlogp", "p99_abs_dlogp", "ratio0",
+                                             "clipfrac0", "approx_kl0", "mismatch_kl")},
+           "mismatch_k3_kl": stats["approx_kl0"],
+           "worst_token": {"row": stats["argmax_row"], "abs_dlogp": stats["max_abs_dlogp"]},
+           "counts": {k: stats[k] for k in ("n_active", "n_clip_low", "n_clip_high",
+                                            "n_nonfinite")},
+           "status": STATUS_NAMES.get(stats["status"], stats["status"]),
+           "metadata": dict(metadata, backend=desc)}
+    if segments is not None:
+        out["segments"] = [{"metrics": {k: s[k] for k in out["metrics"]},
+                            "n_active": s["n_active"], "worst_row": s["argmax_row"],
+                            "status": STATUS_NAMES.get(s["status"], s["status"])}
+                           for s in segments]
     return out
 
 

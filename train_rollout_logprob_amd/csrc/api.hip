@@ -184,6 +184,33 @@ int drift_diagnostics(const float* dlogp, const uint8_t* active, int64_t num_row
   return out_host->status;
 }
 
+int drift_segment_diagnostics(const float* dlogp, const uint8_t* active, int64_t num_rows,
+                              const int32_t* seg_offsets, int64_t num_segments,
+                              double eps_low, double eps_high, const void* logprob_ws,
+                              drift_stats* out_dev, void* stream) {
+  if (num_rows < 0 || num_rows > INT32_MAX || num_segments < 0 || num_segments > INT32_MAX)
+    return DRIFT_EINVAL;
+  if (!(eps_low >= 0.0 && eps_low < 1.0 && eps_high >= 0.0 && eps_high < 1.0))
+    return DRIFT_EINVAL;
+  if (num_segments > 0) {
+    if (!seg_offsets || !out_dev || !aligned(seg_offsets, 4) || !aligned(out_dev, 8))
+      return DRIFT_EINVAL;
+    if (num_rows > 0 && (!dlogp || !active || !aligned(dlogp, 4))) return DRIFT_EINVAL;
+  }
+  SegParams sp;
+  sp.N = num_rows;
+  sp.S = num_segments;
+  sp.eps_low = eps_low;
+  sp.eps_high = eps_high;
+  sp.d = dlogp;
+  sp.active = active;
+  sp.off = seg_offsets;
+  sp.lp = (const WsHeader*)logprob_ws;
+  sp.out = out_dev;
+  if (launch_segment_diagnostics(sp, (hipStream_t)stream) != hipSuccess) return DRIFT_EHIP;
+  return DRIFT_OK;
+}
+
 int drift_lmhead_logprob(const void* hidden, const void* weight, int64_t T, int64_t H, int64_t V,
                          const int32_t* target_ids, const uint8_t* active, float* logp,
                          void* ws, size_t ws_bytes, void* stream) {
@@ -255,7 +282,7 @@ const drift_backend_desc* drift_backend_descriptor(void) {
   static const drift_backend_desc d = {
       DRIFT_ABI_VERSION,
       "drift.gfx950.v1",
-      "selected_token_logprob,dlogp,entropy,lse,drift_diagnostics,lmhead_selected_logprob,dlogits",
+      "selected_token_logprob,dlogp,entropy,lse,drift_diagnostics,segment_diagnostics,mismatch_kl,lmhead_selected_logprob,dlogits",
       "gfx950",
       "logits:f32,bf16;ids:i32,i64;lmhead:bf16",
       "pad_right,pad_left,packed(cu_seqlens);logits row-major [N,row_stride]",

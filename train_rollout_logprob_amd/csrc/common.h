@@ -74,6 +74,16 @@ __host__ __device__ inline int header_status(uint32_t magic, uint32_t err_bits) 
   if (err_bits & (1u << kErrNonfinite)) return DRIFT_ENONFINITE;
   return DRIFT_OK;
 }
+struct SegParams {
+  int64_t N, S;
+  double eps_low, eps_high;
+  const float* d;
+  const uint8_t* active;
+  const int32_t* off;  // [S + 1] segment row offsets
+  const WsHeader* lp;  // nullable
+  drift_stats* out;    // [S], device
+};
+hipError_t launch_segment_diagnostics(const SegParams& p, hipStream_t s);
 size_t diag_ws_bytes(int64_t N);
 size_t diag_stats_offset();
 hipError_t launch_diagnostics(const DiagParams& p, hipStream_t s);

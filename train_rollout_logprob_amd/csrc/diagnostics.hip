@@ -103,17 +103,56 @@ __device__ __forceinline__ bool last_block(unsigned int* ticket, unsigned int G)
   return true;
 }
 
-// Picks the digit of pass `pass` for both quantiles from the global histograms
-// (block of kDiagThreads threads; each owns kBins / kDiagThreads adjacent bins). The
-// selection state is read by thread 0, shared through LDS, and written back by thread 0.
-__device__ void select_digit(SelState* st, const DiagParams& p, int pass) {
+// Block-cooperative: in histogram h (nbins <= kBins counts, global or LDS), finds the bin
+// holding the 1-based rank `rank`, i.e. the digit d with below < rank <= below + h[d],
+// where below counts the keys in bins before d. Each thread owns kBins / kDiagThreads
+// adjacent bins; an inclusive scan over threads locates the bin. Every thread gets the
+// result.
+__device__ void pick_digit(const unsigned int* h, int nbins, long long rank, int& digit,
+                           long long& below) {
   constexpr int PER = kBins / kDiagThreads;
   __shared__ long long s_scan[kDiagThreads / 64];
   __shared__ int s_digit;
   __shared__ long long s_below;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  long long c[PER];
+  long long mine = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int b = tid * PER + i;
+    c[i] = b < nbins ? (long long)h[b] : 0;
+    mine += c[i];
+  }
+  long long inc = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const long long t = __shfl_up(inc, o);
+    if (lane >= o) inc += t;
+  }
+  if (lane == 63) s_scan[wave] = inc;
+  __syncthreads();
+  long long run = inc - mine;
+  for (int w = 0; w < wave; ++w) run += s_scan[w];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (run < rank && rank <= run + c[i]) {
+      s_digit = tid * PER + i;
+      s_below = run;
+    }
+    run += c[i];
+  }
+  __syncthreads();
+  digit = s_digit;
+  below = s_below;
+  __syncthreads();  // s_scan / s_digit are reused by the next call
+}
+
+// Picks the digit of pass `pass` for both quantiles from the global histograms and
+// updates the selection state (read and written by thread 0).
+__device__ void select_digit(SelState* st, const DiagParams& p, int pass) {
   __shared__ long long s_rank[kNumQ];
   __shared__ unsigned int s_prefix[kNumQ];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   if (tid == 0) {
     for (int q = 0; q < kNumQ; ++q) {
       s_rank[q] = st->rank[q];
@@ -123,39 +162,12 @@ __device__ void select_digit(SelState* st, const DiagParams& p, int pass) {
   __syncthreads();
   const int nbins = 1 << kBitsOf[pass];
   for (int q = 0; q < kNumQ; ++q) {
-    const unsigned int* gh = hist_of(p, pass, pass == 0 ? 0 : q);
-    long long c[PER];
-    long long mine = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int b = tid * PER + i;
-      c[i] = b < nbins ? (long long)gh[b] : 0;
-      mine += c[i];
-    }
-    long long inc = mine;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const long long t = __shfl_up(inc, o);
-      if (lane >= o) inc += t;
-    }
-    if (lane == 63) s_scan[wave] = inc;
-    __syncthreads();
-    long long before = inc - mine;
-    for (int w = 0; w < wave; ++w) before += s_scan[w];
-    const long long rank = s_rank[q];
-    long long run = before;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      if (run < rank && rank <= run + c[i]) {
-        s_digit = tid * PER + i;
-        s_below = run;
-      }
-      run += c[i];
-    }
-    __syncthreads();
+    int digit;
+    long long below;
+    pick_digit(hist_of(p, pass, pass == 0 ? 0 : q), nbins, s_rank[q], digit, below);
     if (tid == 0) {
-      s_prefix[q] |= (unsigned int)s_digit << kShift[pass];
-      s_rank[q] = rank - s_below;
+      s_prefix[q] |= (unsigned int)digit << kShift[pass];
+      s_rank[q] -= below;
     }
     __syncthreads();
   }
@@ -174,77 +186,133 @@ __global__ void __launch_bounds__(1024) diag_init(DiagParams p) {
   if (threadIdx.x < 3) st->ticket[threadIdx.x] = 0;
 }
 
+// Running statistics of a set of active rows. Thread partials are combined by
+// block_reduce in a fixed order (lane butterfly, then waves in index order), tile partials
+// in tile order.
+struct RowStats {
+  double s_abs, s_exp, s_kl, s_d;
+  long long n, lo, hi, nf;
+  unsigned long long best;  // (key << 32) | (0xffffffff - row): max = largest key, first row
+};
+
+__device__ __forceinline__ void add_row(RowStats& a, float df, int64_t r, double lo_edge,
+                                        double hi_edge) {
+  const double v = (double)df;
+  const double e = exp(v);
+  ++a.n;
+  a.s_abs += fabs(v);
+  a.s_exp += e;
+  a.s_kl += expm1(v) - v;
+  a.s_d += v;
+  if (e < lo_edge) ++a.lo;
+  else if (e > hi_edge) ++a.hi;
+  if (!isfinite(df)) ++a.nf;
+  const unsigned long long cand = ((unsigned long long)key_of(df) << 32) |
+                                  (unsigned long long)(0xffffffffu - (unsigned int)r);
+  a.best = cand > a.best ? cand : a.best;
+}
+
+__device__ __forceinline__ void add_stats(RowStats& a, const RowStats& b) {
+  a.s_abs += b.s_abs;
+  a.s_exp += b.s_exp;
+  a.s_kl += b.s_kl;
+  a.s_d += b.s_d;
+  a.n += b.n;
+  a.lo += b.lo;
+  a.hi += b.hi;
+  a.nf += b.nf;
+  a.best = b.best > a.best ? b.best : a.best;
+}
+
+// Block-cooperative; the total is returned in thread 0.
+__device__ RowStats block_reduce(RowStats a) {
+  __shared__ RowStats s_w[kDiagThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  a.s_abs = wave_sum(a.s_abs);
+  a.s_exp = wave_sum(a.s_exp);
+  a.s_kl = wave_sum(a.s_kl);
+  a.s_d = wave_sum(a.s_d);
+  a.n = wave_sum(a.n);
+  a.lo = wave_sum(a.lo);
+  a.hi = wave_sum(a.hi);
+  a.nf = wave_sum(a.nf);
+  a.best = wave_max(a.best);
+  if (lane == 0) s_w[wave] = a;
+  __syncthreads();
+  RowStats t = {};
+  if (tid == 0)
+    for (int w = 0; w < kDiagThreads / 64; ++w) add_stats(t, s_w[w]);
+  __syncthreads();
+  return t;
+}
+
+// Fills everything but the percentiles; `lp` (nullable) is a logprob workspace header
+// whose status outranks the diagnostics status.
+__device__ void finish_stats(drift_stats& s, const RowStats& a, const WsHeader* lp) {
+  s.n_active = a.n;
+  s.n_clip_low = a.lo;
+  s.n_clip_high = a.hi;
+  s.n_nonfinite = a.nf;
+  if (a.n == 0) {
+    s.argmax_row = -1;
+    s.ratio0 = s.clipfrac0 = s.approx_kl0 = s.mean_abs_dlogp = s.mean_dlogp = NAN;
+    s.mismatch_kl = NAN;
+    s.p95_abs_dlogp = s.p99_abs_dlogp = s.max_abs_dlogp = NAN;
+    s.status = DRIFT_ENOACTIVE;
+  } else {
+    const double dn = (double)a.n;
+    s.ratio0 = a.s_exp / dn;
+    s.approx_kl0 = a.s_kl / dn;
+    s.clipfrac0 = (double)(a.lo + a.hi) / dn;
+    s.mean_abs_dlogp = a.s_abs / dn;
+    s.mean_dlogp = a.s_d / dn;
+    s.mismatch_kl = -s.mean_dlogp;  // k1: mean of log pi_rollout - log pi_train
+    s.max_abs_dlogp = __uint_as_float((unsigned int)(a.best >> 32));
+    s.argmax_row = (long long)(0xffffffffu - (unsigned int)(a.best & 0xffffffffull));
+    s.status = a.nf ? DRIFT_ENONFINITE : DRIFT_OK;
+  }
+  if (lp) {
+    const int lst = header_status(lp->magic, lp->err_bits);
+    if (lst != DRIFT_OK) s.status = lst;
+  }
+}
+
+__device__ __forceinline__ long long quantile_rank(int q, long long n) {
+  const long long k = (kQNum[q] * n + 99) / 100;  // ceil(q * n), exact
+  return k < 1 ? 1 : (k > n ? n : k);
+}
+
 __global__ void __launch_bounds__(kDiagThreads) diag_tile(DiagParams p) {
   __shared__ unsigned int s_hist[kBins];
-  __shared__ double s_sum[4][kDiagThreads / 64];
-  __shared__ long long s_cnt[4][kDiagThreads / 64];
-  __shared__ unsigned long long s_best[kDiagThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const DiagLayout lay = DiagLayout::make(p.N);
   for (int b = tid; b < kBins; b += kDiagThreads) s_hist[b] = 0;
   __syncthreads();
   const double lo_edge = 1.0 - p.eps_low, hi_edge = 1.0 + p.eps_high;
-  double s_abs = 0, s_exp = 0, s_kl = 0, s_d = 0;
-  long long n = 0, lo = 0, hi = 0, nf = 0;
-  unsigned long long best = 0;
+  RowStats acc = {};
   const int64_t tile0 = (int64_t)blockIdx.x * kDiagTile;
 #pragma unroll
   for (int j = 0; j < kRowsPerThread; ++j) {
     const int64_t r = tile0 + (int64_t)j * kDiagThreads + tid;
     if (r >= p.N || !p.active[r]) continue;
     const float df = p.d[r];
-    const double v = (double)df;
-    const double e = exp(v);
-    ++n;
-    s_abs += fabs(v);
-    s_exp += e;
-    s_kl += expm1(v) - v;
-    s_d += v;
-    if (e < lo_edge) ++lo;
-    else if (e > hi_edge) ++hi;
-    if (!isfinite(df)) ++nf;
-    const unsigned int key = key_of(df);
-    const unsigned long long cand =
-        ((unsigned long long)key << 32) | (unsigned long long)(0xffffffffu - (unsigned int)r);
-    best = cand > best ? cand : best;
-    atomicAdd(&s_hist[key >> kShift[0]], 1u);
+    add_row(acc, df, r, lo_edge, hi_edge);
+    atomicAdd(&s_hist[key_of(df) >> kShift[0]], 1u);
   }
-  s_abs = wave_sum(s_abs);
-  s_exp = wave_sum(s_exp);
-  s_kl = wave_sum(s_kl);
-  s_d = wave_sum(s_d);
-  n = wave_sum(n);
-  lo = wave_sum(lo);
-  hi = wave_sum(hi);
-  nf = wave_sum(nf);
-  best = wave_max(best);
-  if (lane == 0) {
-    s_sum[0][wave] = s_abs;
-    s_sum[1][wave] = s_exp;
-    s_sum[2][wave] = s_kl;
-    s_sum[3][wave] = s_d;
-    s_cnt[0][wave] = n;
-    s_cnt[1][wave] = lo;
-    s_cnt[2][wave] = hi;
-    s_cnt[3][wave] = nf;
-    s_best[wave] = best;
-  }
-  __syncthreads();
+  const RowStats t = block_reduce(acc);
   TilePartial* tp = (TilePartial*)(p.ws + lay.partial_off);
   if (tid == 0) {
-    TilePartial t = {};
-    for (int w = 0; w < kDiagThreads / 64; ++w) {
-      t.s_abs += s_sum[0][w];
-      t.s_exp += s_sum[1][w];
-      t.s_kl += s_sum[2][w];
-      t.s_d += s_sum[3][w];
-      t.n += s_cnt[0][w];
-      t.lo += s_cnt[1][w];
-      t.hi += s_cnt[2][w];
-      t.nonfinite += s_cnt[3][w];
-      t.best = s_best[w] > t.best ? s_best[w] : t.best;
-    }
-    tp[blockIdx.x] = t;
+    TilePartial o = {};
+    o.s_abs = t.s_abs;
+    o.s_exp = t.s_exp;
+    o.s_kl = t.s_kl;
+    o.s_d = t.s_d;
+    o.n = t.n;
+    o.lo = t.lo;
+    o.hi = t.hi;
+    o.nonfinite = t.nf;
+    o.best = t.best;
+    tp[blockIdx.x] = o;
   }
   flush_hist(s_hist, hist_of(p, 0, 0), kBins);
   SelState* st = (SelState*)p.ws;
@@ -253,75 +321,110 @@ __global__ void __launch_bounds__(kDiagThreads) diag_tile(DiagParams p) {
   // last tile: lane j of wave 0 folds tiles j, j + 64, ... in order; thread 0 then folds
   // the 64 lane results in lane order (a tree fixed by the tile count)
   __shared__ long long s_n;
-  __shared__ TilePartial s_lane[64];
+  __shared__ RowStats s_lane[64];
   if (wave == 0) {
-    TilePartial a = {};
+    RowStats a = {};
     for (int g = lane; g < lay.G; g += 64) {
       const TilePartial b = tp[g];
-      a.s_abs += b.s_abs;
-      a.s_exp += b.s_exp;
-      a.s_kl += b.s_kl;
-      a.s_d += b.s_d;
-      a.n += b.n;
-      a.lo += b.lo;
-      a.hi += b.hi;
-      a.nonfinite += b.nonfinite;
-      a.best = b.best > a.best ? b.best : a.best;
+      const RowStats bs = {b.s_abs, b.s_exp, b.s_kl, b.s_d, b.n, b.lo, b.hi, b.nonfinite, b.best};
+      add_stats(a, bs);
     }
     s_lane[lane] = a;
   }
   __syncthreads();
   if (tid == 0) {
-    double a_abs = 0, a_exp = 0, a_kl = 0, a_d = 0;
-    long long an = 0, alo = 0, ahi = 0, anf = 0;
-    unsigned long long abest = 0;
-    for (int g = 0; g < 64; ++g) {
-      a_abs += s_lane[g].s_abs;
-      a_exp += s_lane[g].s_exp;
-      a_kl += s_lane[g].s_kl;
-      a_d += s_lane[g].s_d;
-      an += s_lane[g].n;
-      alo += s_lane[g].lo;
-      ahi += s_lane[g].hi;
-      anf += s_lane[g].nonfinite;
-      abest = s_lane[g].best > abest ? s_lane[g].best : abest;
-    }
-    drift_stats& s = st->stats;
-    s.n_active = an;
-    s.n_clip_low = alo;
-    s.n_clip_high = ahi;
-    s.n_nonfinite = anf;
-    st->n = an;
-    if (an == 0) {
-      s.argmax_row = -1;
-      s.ratio0 = s.clipfrac0 = s.approx_kl0 = s.mean_abs_dlogp = s.mean_dlogp = NAN;
-      s.p95_abs_dlogp = s.p99_abs_dlogp = s.max_abs_dlogp = NAN;
-      s.status = DRIFT_ENOACTIVE;
-    } else {
-      const double dn = (double)an;
-      s.ratio0 = a_exp / dn;
-      s.approx_kl0 = a_kl / dn;
-      s.clipfrac0 = (double)(alo + ahi) / dn;
-      s.mean_abs_dlogp = a_abs / dn;
-      s.mean_dlogp = a_d / dn;
-      s.max_abs_dlogp = __uint_as_float((unsigned int)(abest >> 32));
-      s.argmax_row = (long long)(0xffffffffu - (unsigned int)(abest & 0xffffffffull));
-      s.status = anf ? DRIFT_ENONFINITE : DRIFT_OK;
-    }
-    if (p.lp) {  // the logprob call's own status outranks the diagnostics status
-      const int lst = header_status(p.lp->magic, p.lp->err_bits);
-      if (lst != DRIFT_OK) s.status = lst;
-    }
+    RowStats a = {};
+    for (int g = 0; g < 64; ++g) add_stats(a, s_lane[g]);
+    finish_stats(st->stats, a, p.lp);
+    st->n = a.n;
     for (int q = 0; q < kNumQ; ++q) {
-      const long long k = (kQNum[q] * an + 99) / 100;  // ceil(q * n), exact
-      st->rank[q] = k < 1 ? 1 : (k > an ? an : k);
+      st->rank[q] = quantile_rank(q, a.n);
       st->prefix[q] = 0;
     }
-    s_n = an;
+    s_n = a.n;
   }
   __syncthreads();
   if (s_n == 0) return;  // block-uniform
   select_digit(st, p, 0);
+}
+
+// Per-segment statistics ("Diagnostics" table, per-sequence and per-rank views): one block
+// per segment [off[s], off[s+1]) does the sums, counts and the whole three-digit radix
+// select in LDS, reading the segment's rows once per digit. Thread t takes rows lo + t,
+// lo + t + 256, ..., so the fixed-order sums depend only on the segment's own rows.
+__global__ void __launch_bounds__(kDiagThreads) diag_segments(SegParams p) {
+  __shared__ unsigned int s_hist[kNumQ][kBins];
+  __shared__ long long s_rank[kNumQ];
+  __shared__ unsigned int s_prefix[kNumQ];
+  __shared__ long long s_n;
+  const int tid = threadIdx.x;
+  const int64_t seg = blockIdx.x;
+  const int64_t lo = p.off[seg], hi = p.off[seg + 1];
+  drift_stats* out = p.out + seg;
+  if (!(0 <= lo && lo <= hi && hi <= p.N)) {  // bad segment metadata
+    if (tid == 0) {
+      const RowStats none = {};
+      finish_stats(*out, none, nullptr);
+      out->status = DRIFT_EMASK;
+    }
+    return;
+  }
+  const double lo_edge = 1.0 - p.eps_low, hi_edge = 1.0 + p.eps_high;
+  for (int b = tid; b < kBins; b += kDiagThreads) s_hist[0][b] = 0;
+  __syncthreads();
+  RowStats acc = {};
+  for (int64_t r = lo + tid; r < hi; r += kDiagThreads) {
+    if (!p.active[r]) continue;
+    const float df = p.d[r];
+    add_row(acc, df, r, lo_edge, hi_edge);
+    atomicAdd(&s_hist[0][key_of(df) >> kShift[0]], 1u);
+  }
+  const RowStats t = block_reduce(acc);
+  drift_stats s;
+  if (tid == 0) {
+    finish_stats(s, t, p.lp);
+    for (int q = 0; q < kNumQ; ++q) {
+      s_rank[q] = quantile_rank(q, t.n);
+      s_prefix[q] = 0;
+    }
+    s_n = t.n;
+  }
+  __syncthreads();
+  if (s_n == 0) {  // block-uniform
+    if (tid == 0) *out = s;
+    return;
+  }
+  for (int pass = 0; pass < 3; ++pass) {
+    if (pass > 0) {  // histogram of this digit among keys that match the digits so far
+      for (int b = tid; b < kNumQ * kBins; b += kDiagThreads) (&s_hist[0][0])[b] = 0;
+      __syncthreads();
+      const int hi_shift = kShift[pass - 1], shift = kShift[pass];
+      const unsigned int mask = (1u << kBitsOf[pass]) - 1u;
+      const unsigned int pre0 = s_prefix[0] >> hi_shift, pre1 = s_prefix[1] >> hi_shift;
+      for (int64_t r = lo + tid; r < hi; r += kDiagThreads) {
+        if (!p.active[r]) continue;
+        const unsigned int key = key_of(p.d[r]);
+        if ((key >> hi_shift) == pre0) atomicAdd(&s_hist[0][(key >> shift) & mask], 1u);
+        if ((key >> hi_shift) == pre1) atomicAdd(&s_hist[1][(key >> shift) & mask], 1u);
+      }
+      __syncthreads();
+    }
+    for (int q = 0; q < kNumQ; ++q) {
+      int digit;
+      long long below;
+      pick_digit(s_hist[pass == 0 ? 0 : q], 1 << kBitsOf[pass], s_rank[q], digit, below);
+      if (tid == 0) {
+        s_prefix[q] |= (unsigned int)digit << kShift[pass];
+        s_rank[q] -= below;
+      }
+      __syncthreads();
+    }
+  }
+  if (tid == 0) {
+    s.p95_abs_dlogp = __uint_as_float(s_prefix[0]);
+    s.p99_abs_dlogp = __uint_as_float(s_prefix[1]);
+    *out = s;
+  }
 }
 
 __global__ void __launch_bounds__(kDiagThreads) diag_hist(DiagParams p, int pass) {
@@ -361,6 +464,12 @@ __global__ void __launch_bounds__(kDiagThreads) diag_hist(DiagParams p, int pass
 
 size_t diag_ws_bytes(int64_t N) { return DiagLayout::make(N).total; }
 size_t diag_stats_offset() { return offsetof(SelState, stats); }
+
+hipError_t launch_segment_diagnostics(const SegParams& p, hipStream_t s) {
+  if (p.S == 0) return hipSuccess;
+  hipLaunchKernelGGL(diag_segments, dim3((unsigned)p.S), dim3(kDiagThreads), 0, s, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_diagnostics(const DiagParams& p, hipStream_t s) {
   const DiagLayout lay = DiagLayout::make(p.N);
