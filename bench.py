@@ -15,6 +15,7 @@ Two further legs are reported beside the main line, outside its timed region: `t
 same batch) and `lmhead` (the fused LM-head selected logprob).
 """
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -37,10 +38,27 @@ WORKLOAD_TEXT = {
 }
 
 
-SCORE_SOURCES = ("logprob.hip", "classify.h", "lse.h", "common.h", "rowio.h")
+SCORE_SOURCES = ("logprob.hip", "classify.h", "lse.h", "rowio.h", "common.h:score")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "score_rows_bf16_qwen8b.md")
-DLOGITS_SOURCES = ("dlogits.hip", "classify.h", "common.h", "rowio.h")
+DLOGITS_SOURCES = ("dlogits.hip", "classify.h", "rowio.h", "common.h:score",
+                   "common.h:dlogits")
 DLOGITS_PROFILE = os.path.join(ROOT, "profiles", "dlogits_rows_bf16_qwen8b.md")
+
+
+def _source_text(name):
+    """A source file of the library, or the part of common.h that a kernel compiles
+    against ("common.h:score": everything up to the scoring launcher's declaration;
+    "common.h:dlogits": the dlogits parameter block)."""
+    fname, _, part = name.partition(":")
+    with open(os.path.join(ROOT, "train_rollout_logprob_amd", "csrc", fname), "rb") as fh:
+        text = fh.read()
+    if part == "score":
+        end = text.index(b"hipError_t launch_score(")
+        return text[:end]
+    if part == "dlogits":
+        start = text.index(b"struct DlogitsParams {")
+        return text[start:text.index(b"hipError_t launch_dlogits(", start)]
+    return text
 
 
 def source_hash(files=SCORE_SOURCES):
@@ -49,8 +67,7 @@ def source_hash(files=SCORE_SOURCES):
 
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "train_rollout_logprob_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        h.update(_source_text(f))
     return h.hexdigest()[:16]
 
 
@@ -136,6 +153,40 @@ def lmhead_leg(steps=5, warmup=2):
             "active_tokens_per_s": case.T / (ms * 1e-3), "tflops": tflops,
             "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS, "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
             "flop_per_call": flop}
+
+
+def segments_leg(case, d, active, logprob_ws, steps=20):
+    """Per-sequence statistics of the timed batch (drift_segment_diagnostics): one segment
+    per sequence (batch row, or packed sequence by cu_seqlens); events around `steps`
+    asynchronous calls on the launch stream."""
+    import torch
+
+    from train_rollout_logprob_amd import binding as B
+
+    dev = d.device
+    if case.cu_seqlens is not None:
+        offs = torch.as_tensor(case.cu_seqlens, dtype=torch.int32, device=dev)
+    else:
+        offs = torch.arange(case.B + 1, dtype=torch.int32, device=dev) * case.L
+    S = offs.numel() - 1
+    out = torch.empty(S * ctypes.sizeof(B.drift_stats), dtype=torch.uint8, device=dev)
+    call = (lambda: B.drift_segment_diagnostics(d, active, case.N, offs, S, case.eps_low,
+                                                case.eps_high, logprob_ws, out))
+    for _ in range(3):
+        assert call() == B.DRIFT_OK
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    worst = max(B.segment_diagnostics(d, active, offs, case.eps_low, case.eps_high),
+                key=lambda s_: s_["max_abs_dlogp"])
+    return {"kernel": "diag_segments", "segments": S, "us_per_call": us,
+            "rows_per_s": case.N / (us * 1e-6),
+            "worst_segment": {"argmax_row": worst["argmax_row"],
+                              "max_abs_dlogp": worst["max_abs_dlogp"]}}
 
 
 def training_leg(case, ids, att, act, cu, steps=10, warmup=2):
@@ -340,6 +391,11 @@ def main():
                      "bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
     }
+    stats = {k: getattr(runner.stats, k) for k in (
+        "ratio0", "clipfrac0", "approx_kl0", "mismatch_kl", "mean_abs_dlogp",
+        "p95_abs_dlogp", "p99_abs_dlogp", "max_abs_dlogp", "argmax_row")}
+    line["diagnostics"] = stats
+    line["segments"] = segments_leg(case, runner.out[2], runner.out[3], runner.ws)
     del runner
     if not args.no_training and args.xf == "none":
         log("[bench] training-state leg (entropy, lse, dlogits)")

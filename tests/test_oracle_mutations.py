@@ -9,7 +9,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PIN_TESTS = ["tests/test_oracle_logprob.py", "tests/test_oracle_diagnostics.py",
-             "tests/test_oracle_lmhead.py", "tests/test_oracle_training.py"]
+             "tests/test_oracle_lmhead.py", "tests/test_oracle_training.py",
+             "tests/test_oracle_sharding.py"]
 
 MUTATIONS = [
     ("logprob.py", "lpt = xt - lt", "lpt = lt - xt"),                          # sign
@@ -44,6 +45,10 @@ MUTATIONS = [
     ("diagnostics.py", "math.fsum(-v for v in vals) / n", "math.fsum(vals) / n"),  # kl sign
     ("diagnostics.py", 'st["argmax_row"] += lo', 'st["argmax_row"] += 0'),         # local row
     ("diagnostics.py", "if not 0 <= lo <= hi <= N:", "if not 0 <= lo <= N:"),       # bounds
+    ("sharding.py", "z * math.exp(m - M) for m, z in live", "z for m, z in live"),   # rescale
+    ("sharding.py", "if boundaries[s] <= y < boundaries[s + 1]:",
+     "if boundaries[s] <= y <= boundaries[s + 1]:"),                              # owner
+    ("sharding.py", "return M + math.log(", "return math.log("),                  # max term
     ("lmhead.py", "z[i, int(ids[r])]", "z[i, int(ids[i])]"),
     ("lmhead.py", "z = h @ weight_f64", "z = (h[:, ::-1] @ weight_f64)"),        # reversed K
 ]
