@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define DRIFT_ABI_VERSION 4
+#define DRIFT_ABI_VERSION 5
 
 /* ---- status codes ---------------------------------------------------------------- */
 #define DRIFT_OK          0
@@ -77,6 +77,31 @@ typedef struct drift_transform {
   int32_t op[DRIFT_MAX_TRANSFORMS];    /* DRIFT_XF_*, applied in index order             */
   float value[DRIFT_MAX_TRANSFORMS];   /* finite; > 0 for TEMPERATURE and SOFTCAP        */
 } drift_transform;
+
+/* ---- reduction of the log-sum-exp ("[WS2] Framework for ablation experiment", LogProb
+ *      knobs rows 4-5: reduction topology and merge order) ------------------------------ */
+#define DRIFT_REDUCE_TREE  0  /* fp64 partials merged in a tree fixed by V (fastest)      */
+#define DRIFT_REDUCE_EXACT 1  /* exact integer sums of per-group values: the same bits for
+                                 any split of the vocabulary into shards and any merge
+                                 order (the tp-partition control)                         */
+
+/* One side's log-sum-exp partial of one row over one vocabulary shard, in the exact
+ * form: the row's value sum_v exp(z_v) over the shard's columns is
+ * (bin[0] * 2^64 + bin[1] * 2^32 + bin[2]) * 2^(32 * (top - 2)), accumulated from groups
+ * of 8 columns (4 for fp32 logits) aligned in the global column index. Partials of any
+ * shards add exactly (bin-wise after aligning `top`), so their merge does not depend on
+ * how the vocabulary was split or in which order they are combined. */
+typedef struct drift_lse_partial {
+  uint64_t bin[3];  /* bins top, top-1, top-2                                       */
+  int32_t top;      /* bin index of bin[0]; -2^28 when the shard saw no column      */
+  uint32_t flags;   /* DRIFT_PART_* bits                                            */
+  float x_sel;      /* the selected logit after the transforms, if this shard owns it */
+  float reserved;
+} drift_lse_partial;
+#define DRIFT_PART_SCORED  1u  /* the row is active with a valid id                      */
+#define DRIFT_PART_OWNER   2u  /* the selected id lies in this shard's columns           */
+#define DRIFT_PART_BAD     4u  /* a NaN / +inf logit or |logit| >= 1.16e7 in the shard    */
+#define DRIFT_MAX_SHARDS  64
 
 /* ---- operations (for drift_workspace_size) ---------------------------------------- */
 #define DRIFT_OP_SELECTED_LOGPROB 0
@@ -116,6 +141,8 @@ typedef struct drift_transform {
  *  transforms      [0] train side, [1] rollout side: ordered logit transforms applied to
  *                  every logit of that side (the selected one included) before the
  *                  softmax (LogProb knobs row 7). count = 0 on both sides = none.
+ *  reduction       DRIFT_REDUCE_TREE or DRIFT_REDUCE_EXACT (see above); entropy needs
+ *                  DRIFT_REDUCE_TREE.
  *  entropy         optional outputs ([0] train, [1] rollout; NULL = not computed): fp32
  *                  [N] device arrays, the entropy -sum_v p_v log p_v of the row's softmax
  *                  (after the transforms, over the vocab_real columns), from the same pass
@@ -132,7 +159,7 @@ typedef struct drift_logprob_args {
   int32_t logits_dtype;
   int32_t ids_dtype;
   int32_t layout;
-  int32_t reserved0;           /* must be 0 */
+  int32_t reduction;           /* DRIFT_REDUCE_TREE (0) or DRIFT_REDUCE_EXACT */
   int64_t num_rows;
   int64_t vocab;
   int64_t row_stride;
@@ -209,6 +236,37 @@ typedef struct drift_backend_desc {
  * otherwise. Returns 0 for invalid arguments. Host only. */
 size_t drift_workspace_size(int op, int64_t num_rows, int64_t vocab, int64_t hidden_dim,
                             int dtype);
+
+/* Vocabulary-parallel scoring, one shard's part ("[WS2] Framework for ablation
+ * experiment", LogProb knobs rows 3-5 and 8; the allgather_partials_fixed_merge
+ * topology). `local` describes this shard's logits: train/rollout_logits point to the
+ * [N, row_stride] rows of its `vocab` columns, which are the global columns
+ * [vocab_start, vocab_start + vocab); ids, masks and layout are the global ones, and
+ * local->vocab_real is the global count of real columns (0 = vocab_global). Requires
+ * vocab_start % 8 == 0, vocab_start + vocab <= vocab_global, no entropy / lse outputs.
+ * Writes one exact partial per row and side ([N] each; rows that are not scored get
+ * flags 0) and the owner's selected logit. Errors of the logical inputs are recorded in
+ * `ws` as for drift_selected_logprob. Asynchronous. */
+int drift_shard_partials(const drift_logprob_args* local, int64_t vocab_start,
+                         int64_t vocab_global, drift_lse_partial* train_part,
+                         drift_lse_partial* rollout_part, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* Merge of gathered shard partials in global shard order, then the same finalization as
+ * drift_selected_logprob with DRIFT_REDUCE_EXACT: for every shard split the outputs are
+ * bitwise those of the unsharded exact call (the tp-partition control).
+ *   global        the unsharded arguments (N, vocab = vocab_global, vocab_real, ids, masks,
+ *                 layout, lse outputs); logits pointers are not read
+ *   train_parts, rollout_parts   device [num_shards][N] partials (an all-gather result)
+ *   shard_bounds  host int64 [num_shards + 1]: 0 = b_0 <= b_1 <= ... <= b_S = vocab,
+ *                 shard s owns [b_s, b_{s+1}); 1 <= num_shards <= DRIFT_MAX_SHARDS
+ * A selected id whose owner shard did not flag it gives EMASK (inconsistent shard
+ * metadata). Outputs and status as drift_selected_logprob. Asynchronous. */
+int drift_merge_shards(const drift_logprob_args* global, const drift_lse_partial* train_parts,
+                       const drift_lse_partial* rollout_parts, int num_shards,
+                       const int64_t* shard_bounds, float* train_logp, float* rollout_logp,
+                       float* dlogp, uint8_t* active, void* ws, size_t ws_bytes,
+                       void* stream);
 
 /* Per-row selected-token logprobs of both sides and their drift
  * ("Measurement Contract"). Outputs, each [N] device arrays:

@@ -21,6 +21,7 @@ def test_header_declares_the_boundary():
     assert names == sorted(["drift_workspace_size", "drift_selected_logprob",
                             "drift_get_status", "drift_diagnostics", "drift_lmhead_logprob",
                             "drift_dlogits", "drift_segment_diagnostics",
+                            "drift_shard_partials", "drift_merge_shards",
                             "drift_backend_descriptor", "drift_strerror"])
 
 
@@ -42,12 +43,13 @@ def test_struct_layouts_match_header():
     assert B.drift_logprob_args.entropy.offset == 208 and B.drift_logprob_args.lse.offset == 224
     assert ctypes.sizeof(B.drift_stats) == 5 * 8 + 5 * 8 + 3 * 4 + 4 + 8
     assert B.drift_stats.mismatch_kl.offset == 96
+    assert ctypes.sizeof(B.drift_lse_partial) == 40
 
 
 def test_descriptor_and_strerror():
     from train_rollout_logprob_amd import binding as B
     d = B.drift_backend_descriptor()
-    assert d["abi_version"] == 4 and d["archs"] == "gfx950"
+    assert d["abi_version"] == 5 and d["archs"] == "gfx950"
     assert "batch composition" in d["determinism"]
     assert d["lse_domain"] == "natural log"
     assert d["build_fingerprint"].startswith("src:")
@@ -152,3 +154,30 @@ def test_segment_diagnostics_host_checks():
     assert f(None, None, 10, None, 2, 0.2, 0.2, None, None, None) == B.DRIFT_EINVAL
     assert f(None, None, -1, None, 0, 0.2, 0.2, None, None, None) == B.DRIFT_EINVAL
     assert f(None, None, 10, None, 0, 0.2, 1.0, None, None, None) == B.DRIFT_EINVAL
+
+
+def test_shard_and_merge_host_checks():
+    from train_rollout_logprob_amd import binding as B
+    a = B.drift_logprob_args()
+    a.logits_dtype, a.ids_dtype, a.layout = B.DRIFT_BF16, B.DRIFT_I32, B.DRIFT_PAD_RIGHT
+    a.num_rows, a.vocab, a.row_stride, a.batch, a.seq_len = 0, 16, 16, 0, 1
+    sp = B.lib.drift_shard_partials
+    assert sp(ctypes.byref(a), 4, 64, None, None, None, 0, None) == B.DRIFT_EINVAL    # % 8
+    assert sp(ctypes.byref(a), 56, 64, None, None, None, 0, None) == B.DRIFT_EINVAL   # past end
+    assert sp(ctypes.byref(a), 48, 64, None, None, None, 0, None) == B.DRIFT_EWORKSPACE
+    a.reduction = 3
+    assert sp(ctypes.byref(a), 48, 64, None, None, None, 0, None) == B.DRIFT_EINVAL
+    a.reduction = 0
+    mg = B.lib.drift_merge_shards
+    b = (ctypes.c_int64 * 3)(0, 8, 16)
+    assert mg(ctypes.byref(a), None, None, 0, b, None, None, None, None, None, 0, None) == B.DRIFT_EINVAL
+    assert mg(ctypes.byref(a), None, None, 65, b, None, None, None, None, None, 0, None) == B.DRIFT_EINVAL
+    bad = (ctypes.c_int64 * 3)(0, 9, 15)                                    # does not end at V
+    assert mg(ctypes.byref(a), None, None, 2, bad, None, None, None, None, None, 0, None) == B.DRIFT_EINVAL
+    assert mg(ctypes.byref(a), None, None, 2, b, None, None, None, None, None, 0, None) == B.DRIFT_EWORKSPACE
+    # exact reduction does not carry the entropy moment
+    a.reduction = B.DRIFT_REDUCE_EXACT
+    e = ctypes.c_void_p(256)
+    a.entropy[0] = e
+    assert B.lib.drift_selected_logprob(ctypes.byref(a), None, None, None, None, None, 0,
+                                        None) == B.DRIFT_EINVAL

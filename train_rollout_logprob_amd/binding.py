@@ -34,12 +34,16 @@ LAYOUTS = {"right": DRIFT_PAD_RIGHT, "left": DRIFT_PAD_LEFT, "packed": DRIFT_PAC
 DRIFT_OP_SELECTED_LOGPROB, DRIFT_OP_DIAGNOSTICS, DRIFT_OP_LMHEAD = 0, 1, 2
 DRIFT_XF_SCALE, DRIFT_XF_TEMPERATURE, DRIFT_XF_SOFTCAP = 1, 2, 3
 DRIFT_MAX_TRANSFORMS = 4
+DRIFT_REDUCE_TREE, DRIFT_REDUCE_EXACT = 0, 1
+REDUCTIONS = {"tree": DRIFT_REDUCE_TREE, "exact": DRIFT_REDUCE_EXACT}
+DRIFT_PART_SCORED, DRIFT_PART_OWNER, DRIFT_PART_BAD = 1, 2, 4
+DRIFT_MAX_SHARDS = 64
 XF_CODES = {"scale": DRIFT_XF_SCALE, "temperature": DRIFT_XF_TEMPERATURE,
             "softcap": DRIFT_XF_SOFTCAP}
 
 EXPORTS = ("drift_workspace_size", "drift_selected_logprob", "drift_get_status",
            "drift_diagnostics", "drift_segment_diagnostics", "drift_lmhead_logprob",
-           "drift_dlogits",
+           "drift_dlogits", "drift_shard_partials", "drift_merge_shards",
            "drift_backend_descriptor", "drift_strerror")
 
 
@@ -50,7 +54,7 @@ class drift_transform(ctypes.Structure):
 
 class drift_logprob_args(ctypes.Structure):
     _fields_ = [("logits_dtype", ctypes.c_int32), ("ids_dtype", ctypes.c_int32),
-                ("layout", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("layout", ctypes.c_int32), ("reduction", ctypes.c_int32),
                 ("num_rows", ctypes.c_int64), ("vocab", ctypes.c_int64),
                 ("row_stride", ctypes.c_int64), ("train_logits", ctypes.c_void_p),
                 ("rollout_logits", ctypes.c_void_p), ("target_ids", ctypes.c_void_p),
@@ -60,6 +64,11 @@ class drift_logprob_args(ctypes.Structure):
                 ("prof_events", ctypes.c_void_p * 2), ("vocab_real", ctypes.c_int64),
                 ("transforms", drift_transform * 2), ("entropy", ctypes.c_void_p * 2),
                 ("lse", ctypes.c_void_p * 2)]
+
+
+class drift_lse_partial(ctypes.Structure):
+    _fields_ = [("bin", ctypes.c_uint64 * 3), ("top", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("x_sel", ctypes.c_float), ("reserved", ctypes.c_float)]
 
 
 class drift_stats(ctypes.Structure):
@@ -107,6 +116,12 @@ def _load():
     lib.drift_dlogits.argtypes = [ctypes.POINTER(drift_logprob_args), ctypes.c_int, vp, vp, vp,
                                   ctypes.c_int, vp, i64, vp]
     lib.drift_dlogits.restype = ctypes.c_int
+    lib.drift_shard_partials.argtypes = [ctypes.POINTER(drift_logprob_args), i64, i64, vp, vp, vp,
+                                         sz, vp]
+    lib.drift_shard_partials.restype = ctypes.c_int
+    lib.drift_merge_shards.argtypes = [ctypes.POINTER(drift_logprob_args), vp, vp, ctypes.c_int,
+                                       ctypes.POINTER(i64), vp, vp, vp, vp, vp, sz, vp]
+    lib.drift_merge_shards.restype = ctypes.c_int
     lib.drift_backend_descriptor.argtypes = []
     lib.drift_backend_descriptor.restype = ctypes.POINTER(drift_backend_desc)
     lib.drift_strerror.argtypes = [ctypes.c_int]
@@ -168,6 +183,23 @@ def drift_dlogits(args: drift_logprob_args, side: int, lse, active, grad_logp, o
                                  _stream(stream)))
 
 
+def drift_shard_partials(local: drift_logprob_args, vocab_start: int, vocab_global: int,
+                         train_part, rollout_part, ws, ws_bytes: int, stream=None) -> int:
+    return int(lib.drift_shard_partials(ctypes.byref(local), vocab_start, vocab_global,
+                                        _ptr(train_part), _ptr(rollout_part), _ptr(ws),
+                                        ws_bytes, _stream(stream)))
+
+
+def drift_merge_shards(glob: drift_logprob_args, train_parts, rollout_parts, num_shards: int,
+                       shard_bounds, train_logp, rollout_logp, dlogp, active, ws,
+                       ws_bytes: int, stream=None) -> int:
+    b = (ctypes.c_int64 * (num_shards + 1))(*[int(x) for x in shard_bounds])
+    return int(lib.drift_merge_shards(ctypes.byref(glob), _ptr(train_parts),
+                                      _ptr(rollout_parts), num_shards, b, _ptr(train_logp),
+                                      _ptr(rollout_logp), _ptr(dlogp), _ptr(active), _ptr(ws),
+                                      ws_bytes, _stream(stream)))
+
+
 def drift_backend_descriptor() -> dict:
     d = lib.drift_backend_descriptor().contents
     out = {"abi_version": d.abi_version}
@@ -227,12 +259,12 @@ def set_chain(t: drift_transform, chain):
 
 def make_args(train, rollout, ids, attention=None, action=None, layout="right", batch=0,
               seq_len=0, cu_seqlens=None, vocab=None, events=None, vocab_real=None,
-              transforms=(None, None), entropy=(None, None), lse=(None, None)
-              ) -> drift_logprob_args:
+              transforms=(None, None), entropy=(None, None), lse=(None, None),
+              reduction="tree") -> drift_logprob_args:
     """Describe torch tensors to the C ABI (no copies, no conversions). `vocab_real`:
     leading columns that enter the log-sum-exp (None = all); `transforms`: (train chain,
     rollout chain), each [(kind, value), ...]; `entropy` / `lse`: optional per-side
-    output tensors (fp32 / fp64 [N])."""
+    output tensors (fp32 / fp64 [N]); `reduction`: "tree" or "exact"."""
     if train.dtype != rollout.dtype or train.shape != rollout.shape:
         raise ValueError("train and rollout logits must share dtype and shape")
     if train.stride(1) != 1 or rollout.stride(0) != train.stride(0):
@@ -241,7 +273,7 @@ def make_args(train, rollout, ids, attention=None, action=None, layout="right", 
     a.logits_dtype = {torch.float32: DRIFT_F32, torch.bfloat16: DRIFT_BF16}.get(train.dtype, 99)
     a.ids_dtype = {torch.int32: DRIFT_I32, torch.int64: DRIFT_I64}.get(ids.dtype, 99)
     a.layout = LAYOUTS[layout]
-    a.reserved0 = 0
+    a.reduction = REDUCTIONS[reduction]
     a.num_rows = train.shape[0]
     a.vocab = vocab if vocab is not None else train.shape[1]
     a.row_stride = train.stride(0)
@@ -274,7 +306,7 @@ def make_args(train, rollout, ids, attention=None, action=None, layout="right", 
 def selected_logprob(train, rollout, ids, attention=None, action=None, layout="right",
                      batch=0, seq_len=0, cu_seqlens=None, ws=None, out=None, stream=None,
                      events=None, check=False, vocab_real=None, transforms=(None, None),
-                     entropy=(None, None), lse=(None, None)):
+                     entropy=(None, None), lse=(None, None), reduction="tree"):
     """Allocate outputs (and a workspace unless given) and call drift_selected_logprob.
     Returns (train_logp, rollout_logp, dlogp, active, ws). With check=True, synchronizes
     and raises DriftError on a data-dependent status. `entropy` / `lse`: optional output
@@ -283,7 +315,7 @@ def selected_logprob(train, rollout, ids, attention=None, action=None, layout="r
     dev = train.device
     args = make_args(train, rollout, ids, attention, action, layout, batch, seq_len,
                      cu_seqlens, events=events, vocab_real=vocab_real, transforms=transforms,
-                     entropy=entropy, lse=lse)
+                     entropy=entropy, lse=lse, reduction=reduction)
     if ws is None:
         ws = workspace(DRIFT_OP_SELECTED_LOGPROB, N, args.vocab, args.logits_dtype, dev)
     if out is None:
@@ -310,6 +342,67 @@ def diagnostics(dlogp, active, eps_low=0.2, eps_high=0.2, logprob_ws=None, ws=No
     st, s = drift_diagnostics(dlogp, active, N, eps_low, eps_high, logprob_ws, ws, ws.numel(),
                               stream)
     return st, s.as_dict()
+
+
+def shard_partials(train_local, rollout_local, ids, vocab_start, vocab_global, attention=None,
+                   action=None, layout="right", batch=0, seq_len=0, cu_seqlens=None,
+                   vocab_real=None, transforms=(None, None), out=None, ws=None, stream=None,
+                   events=None):
+    """Call drift_shard_partials on one shard's logits (the [N, width] columns
+    [vocab_start, vocab_start + width) of the global vocabulary). Returns
+    (train_partials, rollout_partials, ws): uint8 tensors holding [N] drift_lse_partial."""
+    args = make_args(train_local, rollout_local, ids, attention, action, layout, batch, seq_len,
+                     cu_seqlens, events=events, vocab_real=vocab_real, transforms=transforms)
+    N = int(args.num_rows)
+    dev = train_local.device
+    if ws is None:
+        ws = workspace(DRIFT_OP_SELECTED_LOGPROB, N, max(int(args.vocab), 1), args.logits_dtype,
+                       dev)
+    if out is None:
+        nb = max(N, 1) * ctypes.sizeof(drift_lse_partial)
+        out = (torch.empty(nb, dtype=torch.uint8, device=dev),
+               torch.empty(nb, dtype=torch.uint8, device=dev))
+    st = drift_shard_partials(args, vocab_start, vocab_global, out[0], out[1], ws, ws.numel(),
+                              stream)
+    if st != DRIFT_OK:
+        raise DriftError(st, "drift_shard_partials")
+    return out[0], out[1], ws
+
+
+def merge_shards(train_parts, rollout_parts, shard_bounds, ids, vocab, num_rows,
+                 attention=None, action=None, layout="right", batch=0, seq_len=0,
+                 cu_seqlens=None, vocab_real=None, lse=(None, None), out=None, ws=None,
+                 stream=None):
+    """Call drift_merge_shards on gathered partials (uint8 tensors holding
+    [S][N] drift_lse_partial). Returns (train_logp, rollout_logp, dlogp, active, ws)."""
+    dev = train_parts.device
+    S = len(shard_bounds) - 1
+    a = drift_logprob_args()
+    a.logits_dtype, a.layout = DRIFT_F32, LAYOUTS[layout]
+    a.ids_dtype = {torch.int32: DRIFT_I32, torch.int64: DRIFT_I64}.get(ids.dtype, 99)
+    a.reduction = DRIFT_REDUCE_EXACT
+    a.num_rows, a.vocab, a.row_stride = num_rows, vocab, vocab
+    a.target_ids = ids.data_ptr()
+    a.attention_mask = attention.data_ptr() if attention is not None else None
+    a.action_mask = action.data_ptr() if action is not None else None
+    a.batch, a.seq_len = batch, seq_len
+    a.cu_seqlens = cu_seqlens.data_ptr() if cu_seqlens is not None else None
+    a.num_seqs = (cu_seqlens.numel() - 1) if cu_seqlens is not None else 0
+    a.vocab_real = 0 if vocab_real is None else int(vocab_real)
+    for side in (0, 1):
+        a.lse[side] = lse[side].data_ptr() if lse[side] is not None else None
+    if ws is None:
+        ws = workspace(DRIFT_OP_SELECTED_LOGPROB, num_rows, vocab, DRIFT_F32, dev)
+    if out is None:
+        out = (torch.empty(num_rows, dtype=torch.float32, device=dev),
+               torch.empty(num_rows, dtype=torch.float32, device=dev),
+               torch.empty(num_rows, dtype=torch.float32, device=dev),
+               torch.empty(num_rows, dtype=torch.uint8, device=dev))
+    st = drift_merge_shards(a, train_parts, rollout_parts, S, shard_bounds, *out, ws, ws.numel(),
+                            stream)
+    if st != DRIFT_OK:
+        raise DriftError(st, "drift_merge_shards")
+    return (*out, ws)
 
 
 def dlogits(train, rollout, ids, side, lse, active, grad_logp=None, out_dtype=torch.float32,

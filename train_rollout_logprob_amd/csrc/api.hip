@@ -75,23 +75,32 @@ size_t drift_workspace_size(int op, int64_t num_rows, int64_t vocab, int64_t hid
   }
 }
 
-int drift_selected_logprob(const drift_logprob_args* a, float* train_logp, float* rollout_logp,
-                           float* dlogp, uint8_t* active, void* ws, size_t ws_bytes,
-                           void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks the logical inputs of `a` (ids, masks, layout, chains, vocab_real against
+// `vocab_ids`, the global column count) and, with `logits`, the logits description; fills
+// the common part of the scoring parameters. Returns a status.
+int prepare(const drift_logprob_args* a, bool logits, int64_t vocab_ids, ScoreParams& sp,
+            int64_t min_vocab = 1) {
   if (!a) return DRIFT_EINVAL;
   if (a->logits_dtype != DRIFT_F32 && a->logits_dtype != DRIFT_BF16) return DRIFT_EDTYPE;
   if (a->ids_dtype != DRIFT_I32 && a->ids_dtype != DRIFT_I64) return DRIFT_EDTYPE;
-  if (a->reserved0 != 0) return DRIFT_EINVAL;
+  if (a->reduction != DRIFT_REDUCE_TREE && a->reduction != DRIFT_REDUCE_EXACT)
+    return DRIFT_EINVAL;
   const int64_t N = a->num_rows, V = a->vocab;
-  if (N < 0 || N > INT32_MAX || V < 1 || V > INT32_MAX || a->row_stride < V) return DRIFT_EINVAL;
+  if (N < 0 || N > INT32_MAX || V < min_vocab || V > INT32_MAX || a->row_stride < V)
+    return DRIFT_EINVAL;
+  if (vocab_ids < 1 || vocab_ids > INT32_MAX) return DRIFT_EINVAL;
   const size_t esz = a->logits_dtype == DRIFT_F32 ? 4 : 2;
   const size_t isz = a->ids_dtype == DRIFT_I32 ? 4 : 8;
   if (N > 0) {
-    if (!a->train_logits || !a->rollout_logits || !a->target_ids) return DRIFT_EINVAL;
-    if (!train_logp || !rollout_logp || !dlogp || !active) return DRIFT_EINVAL;
-    if (!aligned(a->train_logits, esz) || !aligned(a->rollout_logits, esz) ||
-        !aligned(a->target_ids, isz) || !aligned(train_logp, 4) ||
-        !aligned(rollout_logp, 4) || !aligned(dlogp, 4))
+    if (!a->target_ids || !aligned(a->target_ids, isz)) return DRIFT_EINVAL;
+    // an empty shard (V = 0) reads no logits; its pointers may be null
+    if (logits && V > 0 &&
+        (!a->train_logits || !a->rollout_logits || !aligned(a->train_logits, esz) ||
+         !aligned(a->rollout_logits, esz)))
       return DRIFT_EINVAL;
   }
   switch (a->layout) {
@@ -107,18 +116,17 @@ int drift_selected_logprob(const drift_logprob_args* a, float* train_logp, float
     default:
       return DRIFT_EINVAL;
   }
-  if (a->vocab_real < 0 || a->vocab_real > V) return DRIFT_EINVAL;
-  const int64_t Vr = a->vocab_real == 0 ? V : a->vocab_real;
+  if (a->vocab_real < 0 || a->vocab_real > vocab_ids) return DRIFT_EINVAL;
   if (!chain_ok(a->transforms[0]) || !chain_ok(a->transforms[1])) return DRIFT_EINVAL;
   for (int side = 0; side < 2; ++side) {
     if ((a->entropy[side] && !aligned(a->entropy[side], 4)) ||
         (a->lse[side] && !aligned(a->lse[side], 8)))
       return DRIFT_EINVAL;
   }
-  if (!ws || !aligned(ws, 256) || ws_bytes < kLogprobWsBytes) return DRIFT_EWORKSPACE;
-  ScoreParams sp;
+  sp = ScoreParams{};
   sp.N = N;
-  sp.V = Vr;
+  sp.Vid = a->vocab_real == 0 ? vocab_ids : a->vocab_real;
+  sp.V = sp.Vid < V ? sp.Vid : V;
   sp.xf[0] = make_chain(a->transforms[0]);
   sp.xf[1] = make_chain(a->transforms[1]);
   sp.stride = a->row_stride;
@@ -133,6 +141,31 @@ int drift_selected_logprob(const drift_logprob_args* a, float* train_logp, float
   sp.att = a->attention_mask;
   sp.act = a->action_mask;
   sp.cu = a->cu_seqlens;
+  sp.vstart = 0;
+  return DRIFT_OK;
+}
+
+int check_outputs(int64_t N, float* t, float* r, float* d, uint8_t* act) {
+  if (N > 0 && (!t || !r || !d || !act || !aligned(t, 4) || !aligned(r, 4) || !aligned(d, 4)))
+    return DRIFT_EINVAL;
+  return DRIFT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int drift_selected_logprob(const drift_logprob_args* a, float* train_logp, float* rollout_logp,
+                           float* dlogp, uint8_t* active, void* ws, size_t ws_bytes,
+                           void* stream) {
+  ScoreParams sp;
+  int st = prepare(a, true, a ? a->vocab : 0, sp);
+  if (st != DRIFT_OK) return st;
+  if ((st = check_outputs(a->num_rows, train_logp, rollout_logp, dlogp, active)) != DRIFT_OK)
+    return st;
+  const bool exact = a->reduction == DRIFT_REDUCE_EXACT;
+  if (exact && (a->entropy[0] || a->entropy[1])) return DRIFT_EINVAL;
+  if (!ws || !aligned(ws, 256) || ws_bytes < kLogprobWsBytes) return DRIFT_EWORKSPACE;
   sp.out_t = train_logp;
   sp.out_r = rollout_logp;
   sp.out_d = dlogp;
@@ -142,10 +175,70 @@ int drift_selected_logprob(const drift_logprob_args* a, float* train_logp, float
     sp.lse[side] = a->lse[side];
   }
   sp.ws = (char*)ws;
-  if (launch_score(sp, (hipStream_t)stream, (hipEvent_t)a->prof_events[0],
-                   (hipEvent_t)a->prof_events[1]) != hipSuccess)
-    return DRIFT_EHIP;
-  return DRIFT_OK;
+  const hipEvent_t e0 = (hipEvent_t)a->prof_events[0], e1 = (hipEvent_t)a->prof_events[1];
+  const hipError_t e = exact ? launch_score_exact(sp, (hipStream_t)stream, e0, e1)
+                             : launch_score(sp, (hipStream_t)stream, e0, e1);
+  return e == hipSuccess ? DRIFT_OK : DRIFT_EHIP;
+}
+
+int drift_shard_partials(const drift_logprob_args* local, int64_t vocab_start,
+                         int64_t vocab_global, drift_lse_partial* train_part,
+                         drift_lse_partial* rollout_part, void* ws, size_t ws_bytes,
+                         void* stream) {
+  ScoreParams sp;
+  int st = prepare(local, true, vocab_global, sp, 0);  // a shard may hold no column
+  if (st != DRIFT_OK) return st;
+  if (vocab_start < 0 || vocab_start % 8 != 0 || vocab_start + local->vocab > vocab_global)
+    return DRIFT_EINVAL;
+  if (local->entropy[0] || local->entropy[1] || local->lse[0] || local->lse[1])
+    return DRIFT_EINVAL;
+  if (local->num_rows > 0 && (!train_part || !rollout_part || !aligned(train_part, 8) ||
+                              !aligned(rollout_part, 8)))
+    return DRIFT_EINVAL;
+  if (!ws || !aligned(ws, 256) || ws_bytes < kLogprobWsBytes) return DRIFT_EWORKSPACE;
+  // columns of this shard that enter the log-sum-exp
+  const int64_t in = sp.Vid - vocab_start;
+  sp.V = in < 0 ? 0 : (in < local->vocab ? in : local->vocab);
+  sp.vstart = vocab_start;
+  sp.part[0] = train_part;
+  sp.part[1] = rollout_part;
+  sp.ws = (char*)ws;
+  const hipEvent_t e0 = (hipEvent_t)local->prof_events[0], e1 = (hipEvent_t)local->prof_events[1];
+  return launch_score_exact(sp, (hipStream_t)stream, e0, e1) == hipSuccess ? DRIFT_OK
+                                                                          : DRIFT_EHIP;
+}
+
+int drift_merge_shards(const drift_logprob_args* global, const drift_lse_partial* train_parts,
+                       const drift_lse_partial* rollout_parts, int num_shards,
+                       const int64_t* shard_bounds, float* train_logp, float* rollout_logp,
+                       float* dlogp, uint8_t* active, void* ws, size_t ws_bytes,
+                       void* stream) {
+  MergeParams m;
+  int st = prepare(global, false, global ? global->vocab : 0, m.p);
+  if (st != DRIFT_OK) return st;
+  if ((st = check_outputs(global->num_rows, train_logp, rollout_logp, dlogp, active)) != DRIFT_OK)
+    return st;
+  if (global->entropy[0] || global->entropy[1]) return DRIFT_EINVAL;
+  if (num_shards < 1 || num_shards > kMaxShards || !shard_bounds) return DRIFT_EINVAL;
+  if (shard_bounds[0] != 0 || shard_bounds[num_shards] != global->vocab) return DRIFT_EINVAL;
+  for (int s = 0; s < num_shards; ++s)
+    if (shard_bounds[s + 1] < shard_bounds[s]) return DRIFT_EINVAL;
+  if (global->num_rows > 0 && (!train_parts || !rollout_parts || !aligned(train_parts, 8) ||
+                               !aligned(rollout_parts, 8)))
+    return DRIFT_EINVAL;
+  if (!ws || !aligned(ws, 256) || ws_bytes < kLogprobWsBytes) return DRIFT_EWORKSPACE;
+  m.p.out_t = train_logp;
+  m.p.out_r = rollout_logp;
+  m.p.out_d = dlogp;
+  m.p.active = active;
+  m.p.lse[0] = global->lse[0];
+  m.p.lse[1] = global->lse[1];
+  m.p.ws = (char*)ws;
+  m.part[0] = train_parts;
+  m.part[1] = rollout_parts;
+  m.S = num_shards;
+  for (int s = 0; s <= kMaxShards; ++s) m.bound[s] = s <= num_shards ? shard_bounds[s] : 0;
+  return launch_merge_shards(m, (hipStream_t)stream) == hipSuccess ? DRIFT_OK : DRIFT_EHIP;
 }
 
 int drift_get_status(const void* ws, void* stream, int64_t* first_bad_row) {
@@ -282,7 +375,7 @@ const drift_backend_desc* drift_backend_descriptor(void) {
   static const drift_backend_desc d = {
       DRIFT_ABI_VERSION,
       "drift.gfx950.v1",
-      "selected_token_logprob,dlogp,entropy,lse,drift_diagnostics,segment_diagnostics,mismatch_kl,lmhead_selected_logprob,dlogits",
+      "selected_token_logprob,dlogp,entropy,lse,exact_reduction,vocab_shard_partials,shard_merge,drift_diagnostics,segment_diagnostics,mismatch_kl,lmhead_selected_logprob,dlogits",
       "gfx950",
       "logits:f32,bf16;ids:i32,i64;lmhead:bf16",
       "pad_right,pad_left,packed(cu_seqlens);logits row-major [N,row_stride]",

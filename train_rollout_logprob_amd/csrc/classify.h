@@ -51,7 +51,7 @@ __device__ __forceinline__ RowClass classify_row(const ScoreParams& p, int64_t r
   c.y = -1;
   if (c.active) {
     c.y = load_id(p.ids, r, p.ids_i64);
-    if (c.y < 0 || c.y >= p.V) {
+    if (c.y < 0 || c.y >= p.Vid) {
       c.err |= 1u << kErrToken;
     } else {
       c.score = true;

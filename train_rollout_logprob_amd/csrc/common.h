@@ -36,7 +36,8 @@ __device__ __forceinline__ void record_error(WsHeader* h, ErrClass c, int64_t ro
 
 // ---- launchers (each defined next to its kernels) --------------------------------
 struct ScoreParams {
-  int64_t N, V, stride, L, nseq;  // V: columns that enter the log-sum-exp
+  int64_t N, V, stride, L, nseq;  // V: columns of the row that enter the log-sum-exp
+  int64_t Vid;                    // selected ids must lie in [0, Vid)
   int32_t dtype, ids_i64, layout;
   Chain xf[2];                    // transform chain per side (train, rollout)
   const void* train;
@@ -52,10 +53,26 @@ struct ScoreParams {
   float* ent[2];   // optional per-row entropy of each side's softmax
   double* lse[2];  // optional per-row natural-log LSE of each side
   char* ws;
+  // exact mode / vocab shards: global column of the row's first column, and (shard
+  // export) the per-side partial outputs; null = finalize the row here
+  int64_t vstart;
+  drift_lse_partial* part[2];
 };
 // Launches the header initialisation and the scoring kernel; `ev` (nullable) are recorded
 // right before and after the scoring kernel.
 hipError_t launch_score(const ScoreParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+// The exact-mode scoring kernel (order-independent sums), finalizing or exporting shard
+// partials.
+hipError_t launch_score_exact(const ScoreParams& p, hipStream_t s, hipEvent_t ev0,
+                              hipEvent_t ev1);
+constexpr int kMaxShards = 64;
+struct MergeParams {
+  ScoreParams p;  // classification inputs and the outputs
+  const drift_lse_partial* part[2];  // [S][N] per side
+  int32_t S;
+  int64_t bound[kMaxShards + 1];     // shard s owns global columns [bound[s], bound[s+1])
+};
+hipError_t launch_merge_shards(const MergeParams& m, hipStream_t s);
 
 struct DiagParams {
   int64_t N;

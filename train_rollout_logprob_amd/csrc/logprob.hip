@@ -30,6 +30,7 @@
 
 #include "classify.h"
 #include "common.h"
+#include "exact.h"
 #include "lse.h"
 #include "rowio.h"
 
@@ -103,6 +104,24 @@ __device__ __forceinline__ void push(A& a, const float (&x)[VEC]) {
   }
   a.s += (double)t;
   if constexpr (ENT) a.s2 += (double)t2;
+}
+
+// Exact mode: one group's integer pieces into the lane's bins. The window top is raised
+// for the whole wave at once (ballot + max), as k is in the fixed-tree mode.
+template <int VEC>
+__device__ __forceinline__ void push(AccX& a, const float (&x)[VEC]) {
+  const GroupPiece g = group_piece<VEC>(x);
+  const int32_t need = g.live ? g.bin + 1 : kEmptyTop;
+  if (__ballot(need > a.top)) {
+    int32_t T = need;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const int32_t u = __shfl_xor(T, o);
+      T = u > T ? u : T;
+    }
+    accx_shift(a, T);
+  }
+  accx_add(a, g);
 }
 
 // Lane `tid` owns the 16-byte groups g = tid, tid + NT, tid + 2NT, ... of the row and
@@ -319,6 +338,196 @@ __global__ void __launch_bounds__(NT) score_rows(ScoreParams p) {
   }
 }
 
+// ---- exact mode (order-independent sums) and vocabulary shards ----------------------
+
+__device__ __forceinline__ AccX shfl_xor_acc(const AccX& a, int o) {
+  AccX b;
+  b.top = __shfl_xor(a.top, o);
+  b.bad = __shfl_xor(a.bad, o);
+  b.b2 = __shfl_xor(a.b2, o);
+  b.b1 = __shfl_xor(a.b1, o);
+  b.b0 = __shfl_xor(a.b0, o);
+  return b;
+}
+
+__device__ __forceinline__ AccX from_partial(const drift_lse_partial& q) {
+  AccX a;
+  a.top = q.top;
+  a.bad = (q.flags & DRIFT_PART_BAD) ? 1u : 0u;
+  a.b2 = q.bin[0];
+  a.b1 = q.bin[1];
+  a.b0 = q.bin[2];
+  return a;
+}
+
+// Outputs of one scored row from its two exact sums and selected logits; shared by the
+// unsharded exact kernel and the shard merge, so both give the same bits.
+__device__ __forceinline__ void finish_row_exact(const ScoreParams& p, WsHeader* h, int64_t r,
+                                                 const AccX& T_, const AccX& R_, float xty,
+                                                 float xry) {
+  const double lse_t = T_.bad ? (double)NAN : accx_log2(T_) * kLn2;
+  const double lse_r = R_.bad ? (double)NAN : accx_log2(R_) * kLn2;
+  p.out_t[r] = (float)((double)xty - lse_t);
+  p.out_r[r] = (float)((double)xry - lse_r);
+  p.out_d[r] = (float)(((double)xty - (double)xry) - (lse_t - lse_r));
+  if (p.lse[0]) p.lse[0][r] = lse_t;
+  if (p.lse[1]) p.lse[1][r] = lse_r;
+  const bool ok = isfinite(lse_t) && isfinite(lse_r) && (xty > -INFINITY) && (xry > -INFINITY);
+  if (!ok) record_error(h, kErrNonfinite, r);
+}
+
+__device__ __forceinline__ void unscored_outputs(const ScoreParams& p, int64_t r, bool active) {
+  const float f = active ? NAN : 0.0f;
+  p.out_t[r] = f;
+  p.out_r[r] = f;
+  p.out_d[r] = f;
+#pragma unroll
+  for (int side = 0; side < 2; ++side) {
+    if (p.lse[side]) p.lse[side][r] = (double)f;
+  }
+}
+
+// One block per row, as score_rows, with the exact accumulator. The row holds the global
+// columns [vstart, vstart + V); with p.part set it writes the shard partials instead of
+// finalizing.
+template <typename T, int NT, int U, bool XF>
+__global__ void __launch_bounds__(NT) score_rows_exact(ScoreParams p) {
+  constexpr int NW = NT / 64;
+  __shared__ AccX s_acc[2][NW];
+  __shared__ int64_t s_y;
+  WsHeader* h = (WsHeader*)p.ws;
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const bool shard = p.part[0] != nullptr;
+  if (tid == 0) {
+    int64_t end = p.N;
+    if (p.layout == DRIFT_PACKED) {
+      end = (int64_t)p.cu[p.nseq];
+      end = end < 0 ? 0 : (end > p.N ? p.N : end);
+    }
+    const RowClass c = classify_row(p, r, end);
+    if (p.active) p.active[r] = c.active ? 1 : 0;
+    if (c.err & (1u << kErrMask)) record_error(h, kErrMask, r);
+    if (c.err & (1u << kErrToken)) record_error(h, kErrToken, r);
+    if (!c.score) {
+      if (shard) {
+        for (int side = 0; side < 2; ++side) {
+          drift_lse_partial& q = p.part[side][r];
+          q.bin[0] = q.bin[1] = q.bin[2] = 0;
+          q.top = kEmptyTop;
+          q.flags = 0;
+          q.x_sel = 0.0f;
+          q.reserved = 0.0f;
+        }
+      } else {
+        unscored_outputs(p, r, c.active);
+      }
+    }
+    s_y = c.score ? c.y : -1;
+  }
+  __syncthreads();
+  const int64_t y = s_y;
+  if (y < 0) return;  // block-uniform
+
+  const size_t off = (size_t)r * (size_t)p.stride * sizeof(T);
+  const char* rt = (const char*)p.train + off;
+  const char* rr = (const char*)p.rollout + off;
+  AccX at = accx_empty(), ar = accx_empty();
+  if ((((uintptr_t)rt | (uintptr_t)rr) & 15) == 0) {
+    stream_row<T, NT, U, true, XF>(rt, rr, p.V, tid, at, ar, p);
+  } else {
+    stream_row<T, NT, U, false, XF>(rt, rr, p.V, tid, at, ar, p);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    at = merge(at, shfl_xor_acc(at, o));
+    ar = merge(ar, shfl_xor_acc(ar, o));
+  }
+  const int lane = tid & 63, wave = tid >> 6;
+  if (lane == 0) {
+    s_acc[0][wave] = at;
+    s_acc[1][wave] = ar;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    AccX T_ = s_acc[0][0], R_ = s_acc[1][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      T_ = merge(T_, s_acc[0][w]);
+      R_ = merge(R_, s_acc[1][w]);
+    }
+    const bool owner = y >= p.vstart && y < p.vstart + p.V;
+    float xty = 0.0f, xry = 0.0f;
+    if (owner) {  // single owner: the selected logit goes through the same chain
+      float one[1] = {Elem<T>::load1(rt, y - p.vstart)};
+      if constexpr (XF) apply_chain<1>(one, p.xf[0]);
+      xty = one[0];
+      one[0] = Elem<T>::load1(rr, y - p.vstart);
+      if constexpr (XF) apply_chain<1>(one, p.xf[1]);
+      xry = one[0];
+    }
+    if (shard) {
+      auto put = [&](drift_lse_partial& q, const AccX& a, float xs) {
+        q.bin[0] = a.b2;
+        q.bin[1] = a.b1;
+        q.bin[2] = a.b0;
+        q.top = a.top;
+        q.flags = DRIFT_PART_SCORED | (owner ? DRIFT_PART_OWNER : 0u) |
+                  (a.bad ? DRIFT_PART_BAD : 0u);
+        q.x_sel = xs;
+        q.reserved = 0.0f;
+      };
+      put(p.part[0][r], T_, xty);
+      put(p.part[1][r], R_, xry);
+    } else {
+      finish_row_exact(p, h, r, T_, R_, xty, xry);
+    }
+  }
+}
+
+// Shard merge: one thread per row classifies it, folds the S partials of each side in
+// shard order and takes the selected logit from the owner shard.
+__global__ void __launch_bounds__(256) merge_shards(MergeParams m) {
+  const ScoreParams& p = m.p;
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= p.N) return;
+  WsHeader* h = (WsHeader*)p.ws;
+  int64_t end = p.N;
+  if (p.layout == DRIFT_PACKED) {
+    end = (int64_t)p.cu[p.nseq];
+    end = end < 0 ? 0 : (end > p.N ? p.N : end);
+  }
+  const RowClass c = classify_row(p, r, end);
+  p.active[r] = c.active ? 1 : 0;
+  if (c.err & (1u << kErrMask)) record_error(h, kErrMask, r);
+  if (c.err & (1u << kErrToken)) record_error(h, kErrToken, r);
+  if (!c.score) {
+    unscored_outputs(p, r, c.active);
+    return;
+  }
+  AccX T_ = accx_empty(), R_ = accx_empty();
+  bool consistent = true;
+  float xty = 0.0f, xry = 0.0f;
+  for (int s = 0; s < m.S; ++s) {
+    const drift_lse_partial qt = m.part[0][(int64_t)s * p.N + r];
+    const drift_lse_partial qr = m.part[1][(int64_t)s * p.N + r];
+    consistent = consistent && (qt.flags & DRIFT_PART_SCORED) && (qr.flags & DRIFT_PART_SCORED);
+    T_ = merge(T_, from_partial(qt));
+    R_ = merge(R_, from_partial(qr));
+    if (c.y >= m.bound[s] && c.y < m.bound[s + 1]) {
+      consistent = consistent && (qt.flags & DRIFT_PART_OWNER) && (qr.flags & DRIFT_PART_OWNER);
+      xty = qt.x_sel;
+      xry = qr.x_sel;
+    }
+  }
+  if (!consistent) {  // a shard did not score the row or does not hold its selected id
+    record_error(h, kErrMask, r);
+    unscored_outputs(p, r, true);
+    return;
+  }
+  finish_row_exact(p, h, r, T_, R_, xty, xry);
+}
+
 // Block shapes of the scoring kernel, per logits dtype (measured on MI355X: bf16 rows
 // stream best with 256 threads x 8 groups in flight, fp32 rows with 512 x 4). The
 // per-row reduction tree depends on the block width, so a build fixes it once; the unroll
@@ -369,6 +578,38 @@ hipError_t launch_score(const ScoreParams& p, hipStream_t s, hipEvent_t ev0, hip
   }
   if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
   return hipSuccess;
+}
+
+hipError_t launch_score_exact(const ScoreParams& p, hipStream_t s, hipEvent_t ev0,
+                              hipEvent_t ev1) {
+  hipLaunchKernelGGL(init_header, dim3(1), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
+  if (p.N > 0) {
+    const dim3 grid((unsigned)p.N);
+    const bool xf = p.xf[0].n > 0 || p.xf[1].n > 0;
+    constexpr int NB = DRIFT_SCORE_THREADS_BF16, UB = DRIFT_SCORE_UNROLL_BF16;
+    constexpr int NF = DRIFT_SCORE_THREADS_F32, UF = DRIFT_SCORE_UNROLL_F32;
+    if (p.dtype == DRIFT_BF16) {
+      if (xf) hipLaunchKernelGGL((score_rows_exact<uint16_t, NB, UB, true>), grid, dim3(NB), 0, s, p);
+      else hipLaunchKernelGGL((score_rows_exact<uint16_t, NB, UB, false>), grid, dim3(NB), 0, s, p);
+    } else {
+      if (xf) hipLaunchKernelGGL((score_rows_exact<float, NF, UF, true>), grid, dim3(NF), 0, s, p);
+      else hipLaunchKernelGGL((score_rows_exact<float, NF, UF, false>), grid, dim3(NF), 0, s, p);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
+  return hipSuccess;
+}
+
+hipError_t launch_merge_shards(const MergeParams& m, hipStream_t s) {
+  hipLaunchKernelGGL(init_header, dim3(1), dim3(256), 0, s, m.p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || m.p.N == 0) return e;
+  hipLaunchKernelGGL(merge_shards, dim3((unsigned)((m.p.N + 255) / 256)), dim3(256), 0, s, m);
+  return hipGetLastError();
 }
 
 }  // namespace drift
