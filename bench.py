@@ -10,9 +10,11 @@ kernel): algorithmic bytes = active rows x V x 2 bytes x 2 sides, divided by its
 duration measured with HIP events recorded by the library around that kernel on the launch
 stream. `cpu_baseline` is the fp64 CPU oracle timed on a bounded sample of the same rows.
 
-Two further legs are reported beside the main line, outside its timed region: `training`
-(the scoring kernel with per-row entropy and LSE written, and the dlogits kernel on the
-same batch) and `lmhead` (the fused LM-head selected logprob).
+Further legs are reported beside the main line, outside its timed region: `segments`
+(per-sequence diagnostics), `training` (the scoring kernel with per-row entropy and LSE
+written, and the dlogits kernel on the same batch), `exact` (the order-independent
+reduction, unsharded and as vocabulary shards merged in shard order) and `lmhead` (the
+fused LM-head selected logprob).
 """
 import argparse
 import ctypes
@@ -189,6 +191,76 @@ def segments_leg(case, d, active, logprob_ws, steps=20):
                               "max_abs_dlogp": worst["max_abs_dlogp"]}}
 
 
+def exact_leg(case, ids, att, act, cu, shards=8, steps=10, warmup=2):
+    """Order-independent (exact) reduction on the same batch: the unsharded exact scoring
+    kernel, then the batch split into `shards` vocabulary shards (column views, as
+    tensor-parallel ranks hold them): per-shard partial kernels plus the shard-order merge,
+    whose outputs are checked bitwise against the unsharded exact call."""
+    import torch
+
+    from train_rollout_logprob_amd import binding as B
+
+    dev = case.train.device
+    N, V, esz = case.N, case.V, case.elem_bytes
+    n_active = case.n_active()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    out = None
+    for i in range(warmup + steps):
+        evs = (ev[2 * (i - warmup)].cuda_event, ev[2 * (i - warmup) + 1].cuda_event) \
+            if i >= warmup else None
+        out = B.selected_logprob(case.train, case.rollout, ids, att, act, case.layout, case.B,
+                                 case.L, cu, ws=out[4] if out else None,
+                                 out=out[:4] if out else None, events=evs, reduction="exact")
+    torch.cuda.synchronize()
+    st, _ = B.drift_get_status(out[4])
+    if st != B.DRIFT_OK:
+        raise RuntimeError(f"exact scoring: status {B.STATUS_NAMES[st]}")
+    ex_ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)) / steps
+    ex_bytes = n_active * V * esz * 2
+    width = (V // shards) // 8 * 8
+    bounds = [width * s for s in range(shards)] + [V]
+    nb = N * ctypes.sizeof(B.drift_lse_partial)
+    tparts = torch.empty(shards * nb, dtype=torch.uint8, device=dev)
+    rparts = torch.empty(shards * nb, dtype=torch.uint8, device=dev)
+    wss = [B.workspace(B.DRIFT_OP_SELECTED_LOGPROB, N, 1, B.DRIFT_BF16, dev) for _ in range(shards)]
+    args = [B.make_args(case.train[:, bounds[s]:bounds[s + 1]],
+                        case.rollout[:, bounds[s]:bounds[s + 1]], ids, att, act, case.layout,
+                        case.B, case.L, cu) for s in range(shards)]
+
+    def sharded():
+        for s in range(shards):
+            assert B.drift_shard_partials(args[s], bounds[s], V, tparts[s * nb:],
+                                          rparts[s * nb:], wss[s], wss[s].numel()) == B.DRIFT_OK
+        return B.merge_shards(tparts, rparts, bounds, ids, V, N, att, act, case.layout, case.B,
+                              case.L, cu)
+
+    for _ in range(warmup):
+        res = sharded()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        res = sharded()
+    e1.record()
+    torch.cuda.synchronize()
+    sh_ms = e0.elapsed_time(e1) / steps
+    same = all(torch.equal(a.view(torch.int32), b.view(torch.int32))
+               for a, b in zip(res[:3], out[:3]))
+    return {
+        "workload": f"same batch; exact reduction unsharded, then {shards} vocabulary shards "
+                    f"of {width} columns (column views) + shard-order merge",
+        "exact": {"kernel": f"score_rows_exact<{case.dtype}>", "kernel_ms": ex_ms,
+                  "bytes_per_launch": ex_bytes,
+                  "achieved_gbs": ex_bytes / (ex_ms * 1e-3) / 1e9,
+                  "frac": ex_bytes / (ex_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "sharded": {"shards": shards, "ms_all_shards_and_merge": sh_ms,
+                    "achieved_gbs": ex_bytes / (sh_ms * 1e-3) / 1e9,
+                    "bitwise_equal_to_unsharded": bool(same)},
+    }
+
+
 def training_leg(case, ids, att, act, cu, steps=10, warmup=2):
     """Training-only state on the same batch: the scoring kernel with per-row entropy and
     LSE written for both sides (kernel time from events on the launch stream), then
@@ -265,6 +337,8 @@ def main():
                     help="scoring workload (the benchmark line is quoted on qwen8b)")
     ap.add_argument("--no-training", action="store_true",
                     help="skip the entropy / dlogits leg reported beside the main line")
+    ap.add_argument("--no-exact", action="store_true",
+                    help="skip the exact-reduction / vocabulary-shard leg")
     ap.add_argument("--no-lmhead", action="store_true",
                     help="skip the fused LM-head leg reported beside the main line")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
@@ -401,6 +475,10 @@ def main():
         log("[bench] training-state leg (entropy, lse, dlogits)")
         torch.cuda.empty_cache()
         line["training"] = training_leg(case, ids, att, act, cu)
+    if not args.no_exact and args.xf == "none":
+        log("[bench] exact-reduction leg (unsharded and vocabulary shards)")
+        torch.cuda.empty_cache()
+        line["exact"] = exact_leg(case, ids, att, act, cu)
     if not args.no_lmhead and args.workload == "qwen8b" and args.xf == "none":
         torch.cuda.empty_cache()
         log("[bench] fused LM-head leg")
