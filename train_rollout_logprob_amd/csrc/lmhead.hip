@@ -9,11 +9,11 @@
 //   lm_transpose_w   W [H, V] -> WT [Vp, Hp] (K contiguous, zero padded) in the workspace,
 //                    so both MFMA operands load as 16-byte K-contiguous vectors;
 //   lm_pad_hidden    (only when T or H is not a tile multiple) hidden -> [Tp, Hp], zero pad;
-//   lm_gemm_lse      C^T tiles: 256 vocab rows x 256 tokens per block, K = H in steps of 64
-//                    through double-buffered LDS with global loads two stages ahead,
-//                    v_mfma_f32_32x32x16_bf16 with fp32
-//                    accumulation. The epilogue turns each token's 256 logits into a (k, s)
-//                    log-sum-exp partial and records z[t, y_t] from the single owning lane;
+//   lm_gemm_lse      C^T tiles: 256 vocab rows x 256 tokens per block, 4 waves of 128 x 128,
+//                    K = H in steps of 64 through two LDS buffers filled by direct-to-LDS
+//                    loads, v_mfma_f32_32x32x16_bf16 with fp32 accumulation. The epilogue
+//                    turns each token's 256 logits into a (k, s) log-sum-exp partial and
+//                    records z[t, y_t] from the single owning lane;
 //   lm_merge         per token, the partials of all vocab tiles in ascending tile order.
 // The K order of every product is fixed (k-tiles ascending, 16-wide MFMA steps ascending)
 // and independent of T, of the token's position in its tile and of the launch, so a
@@ -31,30 +31,25 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Block tile and wave grid. Two waves per SIMD (8 waves) let one wave's MFMAs cover the
-// other's LDS and global-load waits. The K order of the products does not depend on
-// these shapes; the epilogue tree depends only on the vocab-wave split (2).
-#ifndef DRIFT_LM_WAVES_T
-#define DRIFT_LM_WAVES_T 4
-#endif
+// Block tile and its schedule over the chip. The K order of the products does not depend
+// on these shapes; the epilogue tree depends only on the vocab-wave split (2).
 constexpr int kBV = 256;        // vocab rows per block (MFMA M)
 constexpr int kBT = 256;        // tokens per block (MFMA N)
 constexpr int kBK = 64;         // K per LDS stage
-constexpr int kPitch = kBK + 8; // LDS row pitch in bf16 (144 B: conflict-free 16-B reads)
-constexpr int kWavesV = 2;
-constexpr int kWavesT = DRIFT_LM_WAVES_T;
-constexpr int kThreads = 64 * kWavesV * kWavesT;
-constexpr int kWV = kBV / kWavesV;  // vocab rows per wave (128)
-constexpr int kWT = kBT / kWavesT;  // tokens per wave
-constexpr int kTM = kWV / 32;       // 32x32 MFMA tiles per wave along vocab
-constexpr int kTN = kWT / 32;       // ... along tokens
-// Stage loads: each thread moves 64 contiguous bytes (half a row's K slice) per pass, so
-// its four 16-byte loads share one address register (immediate offsets).
-constexpr int kRowsPerPass = kThreads / 2;
-constexpr int kPasses = kBV / kRowsPerPass;
-static_assert(kTN >= 1 && kPasses >= 1 && kBV == kBT && kBK == 64, "tile shape");
-constexpr int kGroupV = 16;     // vocab tiles per scheduling group
-constexpr int kGroupT = 16;     // token tiles per scheduling chunk
+constexpr int kPW = 128;        // rows (vocab) and tokens per wave: a 2 x 2 wave grid
+constexpr int kPT = kPW / 32;   // 32x32 MFMA tiles per wave along each side
+constexpr int kPThreads = 256;
+static_assert(kBV == kBT && kBK == 64 && kBV == 2 * kPW, "tile shape");
+#ifndef DRIFT_LM_GROUP_V
+#define DRIFT_LM_GROUP_V 16
+#endif
+#ifndef DRIFT_LM_GROUP_T
+#define DRIFT_LM_GROUP_T 16
+#endif
+constexpr int kGroupV = DRIFT_LM_GROUP_V;  // vocab tiles per scheduling group
+constexpr int kGroupT = DRIFT_LM_GROUP_T;  // token tiles per scheduling chunk
+static_assert(kGroupV * kGroupT == 256 && kGroupV % 4 == 0 && kGroupT % 2 == 0,
+              "one chunk = one block per CU, 8 XCD sub-grids");
 
 struct Partial {  // 16 bytes
   float k;
@@ -145,16 +140,17 @@ __global__ void __launch_bounds__(256) lm_pad_hidden(const uint16_t* __restrict_
 // Block id -> (vocab tile, token tile). Groups of kGroupV vocab tiles are walked in order;
 // inside a group, chunks of kGroupT token tiles; inside a chunk (256 blocks = one block
 // per CU), the 32 blocks that the dispatcher sends to one XCD (ids equal mod 8) form a
-// 4 x 8 sub-grid, so they share operand panels in that XCD's L2. Ids past the end map
-// outside the grid and exit.
+// (kGroupV / 4) x (kGroupT / 2) sub-grid, so they share operand panels in that XCD's L2.
+// Ids past the end map outside the grid and exit.
 __device__ __forceinline__ void tile_of(int64_t b, int64_t nVt_pad, int64_t nTt_pad,
                                         int64_t& vt, int64_t& tt) {
   const int64_t per_group = (int64_t)kGroupV * nTt_pad;
   const int64_t g = b / per_group, j = b % per_group;
   const int64_t chunk = j / (kGroupV * kGroupT), jj = j % (kGroupV * kGroupT);
+  constexpr int SV = kGroupV / 4, ST = kGroupT / 2;  // one XCD's sub-grid: SV x ST
   const int xcd = (int)(jj % 8), s = (int)(jj / 8);
-  vt = g * kGroupV + 4 * (xcd % 4) + (s % 4);
-  tt = chunk * kGroupT + 8 * (xcd / 4) + (s / 4);
+  vt = g * kGroupV + SV * (xcd % 4) + (s % SV);
+  tt = chunk * kGroupT + ST * (xcd / 4) + (s / SV);
 }
 
 struct GemmArgs {
@@ -166,124 +162,30 @@ struct GemmArgs {
   float* zsel;          // [Tp]
 };
 
-__global__ void __launch_bounds__(kThreads, 1) lm_gemm_lse(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBV][kPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBT][kPitch];
-  __shared__ float s_k[kWavesT][kWT];
-  __shared__ double s_s[kWavesT][kWT];
-  int64_t vt, tt;
-  tile_of(blockIdx.x, a.nVt_pad, a.nTt_pad, vt, tt);
-  if (vt >= a.nVt || tt >= a.nTt) return;  // block-uniform
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wv = wave / kWavesT, wt = wave % kWavesT;
-  const int lr = lane & 31, lh = lane >> 5;
-  const int64_t v0 = vt * kBV, t0 = tt * kBT;
-  const uint16_t* gA = a.wt + v0 * a.Hp;
-  const uint16_t* gB = a.hid + t0 * a.Hp;
-
-  // Two register sets of stage loads are in flight (stage j lives in set j % 2); LDS is
-  // double buffered (stage j in buffer j % 2).
-  const int lrow = tid >> 1, lcol = (tid & 1) * 32;
-  const uint16_t* pa = gA + (int64_t)lrow * a.Hp + lcol;
-  const uint16_t* pb = gB + (int64_t)lrow * a.Hp + lcol;
-  struct Set {
-    u32x4 a[kPasses][4], b[kPasses][4];
-  };
-  Set s0, s1;
-  auto load = [&](Set& R, int64_t k0) {
-#pragma unroll
-    for (int ps = 0; ps < kPasses; ++ps) {
-      const uint16_t* qa = pa + (int64_t)ps * kRowsPerPass * a.Hp + k0;
-      const uint16_t* qb = pb + (int64_t)ps * kRowsPerPass * a.Hp + k0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        R.a[ps][i] = *(const u32x4*)(qa + 8 * i);
-        R.b[ps][i] = *(const u32x4*)(qb + 8 * i);
-      }
-    }
-  };
-  auto store = [&](const Set& R, int buf) {
-#pragma unroll
-    for (int ps = 0; ps < kPasses; ++ps)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        *(u32x4*)&sA[buf][ps * kRowsPerPass + lrow][lcol + 8 * i] = R.a[ps][i];
-        *(u32x4*)&sB[buf][ps * kRowsPerPass + lrow][lcol + 8 * i] = R.b[ps][i];
-      }
-  };
-
-  f32x16 acc[kTM][kTN];
-#pragma unroll
-  for (int im = 0; im < kTM; ++im)
-#pragma unroll
-    for (int in = 0; in < kTN; ++in)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[im][in][r] = 0.0f;
-
-  auto compute = [&](int buf) {
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      __builtin_amdgcn_sched_barrier(0);  // keep the K steps in order (register pressure)
-      const int koff = kk * 16 + lh * 8;
-      bf16x8 fb[kTN];
-#pragma unroll
-      for (int in = 0; in < kTN; ++in)
-        fb[in] = *(const bf16x8*)&sB[buf][kWT * wt + 32 * in + lr][koff];
-#pragma unroll
-      for (int im = 0; im < kTM; ++im) {
-        const bf16x8 fa = *(const bf16x8*)&sA[buf][kWV * wv + 32 * im + lr][koff];
-#pragma unroll
-        for (int in = 0; in < kTN; ++in)
-          acc[im][in] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb[in], acc[im][in], 0, 0, 0);
-      }
-    }
-  };
-
-  const int64_t nk = a.Hp / kBK;
-  load(s0, 0);
-  if (nk > 1) load(s1, kBK);
-  store(s0, 0);
-  __syncthreads();
-  // Stage j is loaded into set j % 2 two stages ahead and computed from buffer j % 2.
-  // Per pair of stages (kt, kt + 1): load kt+2 into s0, compute buffer 0, move s1 (stage
-  // kt+1) into buffer 1, barrier; load kt+3 into s1, compute buffer 1, move s0 (stage
-  // kt+2) into buffer 0, barrier. An odd last stage is computed from buffer 0.
-  const int64_t nk2 = nk & ~(int64_t)1;
-  for (int64_t kt = 0; kt < nk2; kt += 2) {
-    if (kt + 2 < nk) load(s0, (kt + 2) * kBK);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(0);
-    __builtin_amdgcn_sched_barrier(0);
-    store(s1, 1);
-    __syncthreads();
-    if (kt + 3 < nk) load(s1, (kt + 3) * kBK);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(1);
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + 2 < nk) store(s0, 0);
-    __syncthreads();
-  }
-  if (nk & 1) {
-    compute(0);
-    __syncthreads();
-  }
-
-  // Epilogue. Lane (lr, lh) of wave (wv, wt) holds, for token t = t0 + kWT wt + 32 in + lr,
-  // the logits of vocab rows vb + 32 im + 8 (r / 4) + (r % 4), vb = v0 + kWV wv + 4 lh.
-  // Row tests compare the compile-time offset 32 im + 8 (r / 4) + (r % 4) against
-  // per-lane limits, so no per-element index is materialised.
-  const int64_t vb = v0 + kWV * wv + 4 * lh;
+// Epilogue of the GEMM kernels: each token's logits of this block become one (k, s)
+// log-sum-exp partial; the single owner of z[t, y_t] records it. Lane (lr, lh) of wave
+// (wv, wt) holds, for token t = t0 + WT wt + 32 in + lr, the logits of vocab rows
+// vb + 32 im + 8 (r / 4) + (r % 4), vb = v0 + WV wv + 4 lh. Row tests compare the
+// compile-time offset 32 im + 8 (r / 4) + (r % 4) against per-lane limits, so no
+// per-element index is materialised. The two vocab waves of a token merge through LDS
+// (wave wv = 1 writes, wv = 0 merges and stores).
+template <int TM, int TN, int WV, int WT>
+__device__ __forceinline__ void lse_epilogue(const f32x16 (&acc)[TM][TN], const GemmArgs& a,
+                                             int64_t vt, int64_t v0, int64_t t0, int wv, int wt,
+                                             int lr, int lh, float (*s_k)[WT],
+                                             double (*s_s)[WT]) {
+  const int64_t vb = v0 + WV * wv + 4 * lh;
   const int64_t vlim64 = a.V - vb;  // offsets below this are real vocab rows
-  const int vlim = vlim64 > kWV ? kWV : (int)vlim64;
+  const int vlim = vlim64 > WV ? WV : (int)vlim64;
 #pragma unroll
-  for (int in = 0; in < kTN; ++in) {
-    const int64_t t = t0 + kWT * wt + 32 * in + lr;
+  for (int in = 0; in < TN; ++in) {
+    const int64_t t = t0 + WT * wt + 32 * in + lr;
     const int64_t y = (t < a.T) ? (int64_t)a.ids[t] : -1;
     const int64_t yr64 = y - vb;
-    const int yrel = (y >= 0 && yr64 >= 0 && yr64 < kWV) ? (int)yr64 : -1;
+    const int yrel = (y >= 0 && yr64 >= 0 && yr64 < WV) ? (int)yr64 : -1;
     float m = -INFINITY;
 #pragma unroll
-    for (int im = 0; im < kTM; ++im)
+    for (int im = 0; im < TM; ++im)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int off = 32 * im + 8 * (r / 4) + (r % 4);
@@ -300,7 +202,7 @@ __global__ void __launch_bounds__(kThreads, 1) lm_gemm_lse(GemmArgs a) {
       } else {
         const float nk = -k;
 #pragma unroll
-        for (int im = 0; im < kTM; ++im)
+        for (int im = 0; im < TM; ++im)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int off = 32 * im + 8 * (r / 4) + (r % 4);
@@ -333,6 +235,149 @@ __global__ void __launch_bounds__(kThreads, 1) lm_gemm_lse(GemmArgs a) {
     }
     __syncthreads();
   }
+}
+
+// The head GEMM with its LSE epilogue. 4 waves (one per SIMD) in a 2 x 2 grid each compute
+// 128 vocab rows x 128 tokens (4 x 4 MFMA tiles, accumulators in the AGPRs). Within a K
+// stage the four 16-wide steps are interleaved by hand with the memory work: the MFMAs of
+// a step run while the next step's fragments are read from LDS into the other register
+// set. The stage tiles move from global memory into
+// LDS with global_load_lds_dwordx4 (lane l of an instruction fills bytes [16 l, 16 l + 16)
+// of a 1 KB LDS span, checked on the GPU), so no VGPRs hold them and the LDS fills count
+// on vmcnt while the fragment reads alone count on lgkmcnt. Rows are 128 bytes without
+// padding; the 16-byte chunk c of row r is stored at chunk c ^ ((r >> 1) & 7), which makes
+// the fragment reads (16 lanes = 16 consecutive rows at one logical chunk) hit 16 distinct
+// 4-bank groups. The four buffers (A and B, two stages) are separate LDS arrays and the
+// stage loop is unrolled by two, so every access names its buffer at compile time.
+constexpr int kDRowBytes = kBK * 2;  // 128
+__global__ void __launch_bounds__(kPThreads, 1) lm_gemm_lse(GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint16_t sA0[kBV * kBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA1[kBV * kBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB0[kBT * kBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB1[kBT * kBK];
+  __shared__ float s_k[2][kPW];
+  __shared__ double s_s[2][kPW];
+  int64_t vt, tt;
+  tile_of(blockIdx.x, a.nVt_pad, a.nTt_pad, vt, tt);
+  if (vt >= a.nVt || tt >= a.nTt) return;  // block-uniform
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wv = wave >> 1, wt = wave & 1;
+  const int lr = lane & 31, lh = lane >> 5;
+  const int64_t v0 = vt * kBV, t0 = tt * kBT;
+  const uint16_t* gA = a.wt + v0 * a.Hp;
+  const uint16_t* gB = a.hid + t0 * a.Hp;
+  if (a.T < 0) {  // never taken; keeps the LDS arrays from being treated as never written
+    sA0[tid] = sA1[tid] = sB0[tid] = sB1[tid] = 0;
+  }
+
+  // LDS fills: wave w moves the 8-row blocks 8w .. 8w + 7 of both tiles. Lane l of an
+  // instruction for rows r0 .. r0 + 7 takes row r0 + l / 8 and stored chunk l % 8, i.e.
+  // logical chunk (l % 8) ^ ((r0 / 2 + l / 16) & 7).
+  // The stored chunk of a lane depends on the 8-row block only through its parity (r0 / 2
+  // is a multiple of 4), so two per-lane byte offsets serve every instruction; the rest of
+  // the address is wave-uniform.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t lane_off[2] = {
+      (uint32_t)(((lane >> 3) * a.Hp + (((lane & 7) ^ ((lane >> 4) & 7)) * 8)) * 2),
+      (uint32_t)(((lane >> 3) * a.Hp + (((lane & 7) ^ ((4 + (lane >> 4)) & 7)) * 8)) * 2)};
+  auto fill = [&](uint16_t* dA, uint16_t* dB, int64_t k0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r0 = (wave_u * 8 + j) * 8;
+      const int64_t rowk = (int64_t)r0 * a.Hp + k0;
+      const char* srcA = (const char*)(gA + rowk) + lane_off[j & 1];
+      const char* srcB = (const char*)(gB + rowk) + lane_off[j & 1];
+      __builtin_amdgcn_global_load_lds(srcA, dA + r0 * kBK, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(srcB, dB + r0 * kBK, 16, 0, 0);
+    }
+  };
+
+  f32x16 acc[kPT][kPT];
+#pragma unroll
+  for (int i = 0; i < kPT; ++i)
+#pragma unroll
+    for (int j = 0; j < kPT; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  bf16x8 fa[2][kPT], fb[2][kPT];
+  const int swz = (lr >> 1) & 7;  // rows 128 wv + 32 i + lr share ((row >> 1) & 7)
+  auto fread = [&](const uint16_t* bA, const uint16_t* bB, int kk, int set) {
+    const int ch = (2 * kk + lh) ^ swz;
+#pragma unroll
+    for (int i = 0; i < kPT; ++i) {
+      fa[set][i] = *(const bf16x8*)(bA + (kPW * wv + 32 * i + lr) * kBK + ch * 8);
+      fb[set][i] = *(const bf16x8*)(bB + (kPW * wt + 32 * i + lr) * kBK + ch * 8);
+    }
+  };
+  auto mfmas = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < kPT; ++i)
+#pragma unroll
+      for (int j = 0; j < kPT; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j],
+                                                            0, 0, 0);
+  };
+  // the next step's fragment reads go out early in the step, one after each MFMA
+  auto interleave_reads = [&]() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Stage kt reads the buffers of parity kt % 2: steps 0-2 read the next step's fragments;
+  // then this wave's fills of stage kt + 1 (issued during stage kt - 1) are awaited and the
+  // block barrier makes every fill visible and every read of this stage's buffers done;
+  // step 3 reads the first fragments of stage kt + 1 and starts the fills of stage kt + 2
+  // into this stage's buffers (the last stages re-fill with the last stage's data, which
+  // nobody reads).
+  const int64_t nk = a.Hp / kBK;
+  auto stage = [&](const uint16_t* cA, const uint16_t* cB, uint16_t* nA, uint16_t* nB,
+                   int64_t kt) {
+    const int64_t k2 = (kt + 2 < nk ? kt + 2 : nk - 1) * kBK;
+    fread(cA, cB, 1, 1);
+    mfmas(0);
+    interleave_reads();
+    fread(cA, cB, 2, 0);
+    mfmas(1);
+    interleave_reads();
+    fread(cA, cB, 3, 1);
+    mfmas(0);
+    interleave_reads();
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's fills of stage kt + 1
+    __syncthreads();
+    fread(nA, nB, 0, 0);
+    fill(const_cast<uint16_t*>(cA), const_cast<uint16_t*>(cB), k2);
+    mfmas(1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  fill(sA0, sB0, 0);
+  fill(sA1, sB1, nk > 1 ? kBK : 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  fread(sA0, sB0, 0, 0);
+  int64_t kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    stage(sA0, sB0, sA1, sB1, kt);
+    stage(sA1, sB1, sA0, sB0, kt + 1);
+  }
+  if (kt < nk) stage(sA0, sB0, sA1, sB1, kt);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+
+  lse_epilogue<kPT, kPT, kPW, kPW>(acc, a, vt, v0, t0, wv, wt, lr, lh, s_k, s_s);
 }
 
 // Four lanes per token: lane q folds the vocab tiles [q*c, (q+1)*c) in ascending order
@@ -429,7 +474,7 @@ hipError_t launch_lmhead(const LmheadParams& p, hipStream_t s) {
   g.part = (Partial*)(p.ws + l.part_off);
   g.zsel = (float*)(p.ws + l.zsel_off);
   const int64_t nblocks = g.nVt_pad * g.nTt_pad;
-  hipLaunchKernelGGL(lm_gemm_lse, dim3((unsigned)nblocks), dim3(kThreads), 0, s, g);
+  hipLaunchKernelGGL(lm_gemm_lse, dim3((unsigned)nblocks), dim3(kPThreads), 0, s, g);
   hipLaunchKernelGGL(lm_merge, dim3((unsigned)((p.T * kMergeSplit + 255) / 256)), dim3(256), 0, s,
                      g.part,
                      g.zsel, p.ids, p.active, p.logp, p.T, l.Tp, p.V, l.nVt, p.ws);
