@@ -76,7 +76,7 @@ __device__ __forceinline__ AccX merge(AccX a, AccX b) {
 
 // The integer pieces of one group: value = hi * 2^(32 (bin + 1)) + lo * 2^(32 bin).
 struct GroupPiece {
-  int32_t bin;    // meaningless when live == 0
+  int32_t bin;    // meaningless when live == 0 (the pieces are 0 then)
   uint32_t hi, lo;
   uint32_t live;  // 0: every logit of the group is -inf (adds nothing)
   uint32_t bad;
@@ -85,15 +85,11 @@ struct GroupPiece {
 template <int VEC>
 __device__ __forceinline__ GroupPiece group_piece(const float (&x)[VEC]) {
   GroupPiece g;
-  g.hi = g.lo = 0;
-  g.bin = 0;
   float m = x[0];
 #pragma unroll
   for (int i = 1; i < VEC; ++i) m = fmaxf(m, x[i]);  // NaN-ignoring
-  g.live = m != -INFINITY;
-  g.bad = 0;
-  if (!g.live) return g;
-  const float n = ceilf(m * kLog2e);
+  const bool live = m != -INFINITY;
+  const float n = live ? ceilf(m * kLog2e) : 0.0f;
   float e[VEC];
 #pragma unroll
   for (int i = 0; i < VEC; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(x[i], kLog2e, -n));
@@ -105,36 +101,28 @@ __device__ __forceinline__ GroupPiece group_piece(const float (&x)[VEC]) {
   const float G = e[0];
   // G >= 2^-2 for a finite group (its largest term is about 1); NaN, +inf or a huge
   // exponent fail closed
-  if (!(fabsf(n) <= kMaxGroupExp) || !(G >= 0.125f && G <= 64.0f)) {
-    g.bad = 1;
-    g.live = 0;
-    return g;
-  }
+  const bool ok = fabsf(n) <= kMaxGroupExp && G >= 0.125f && G <= 64.0f;
+  g.bad = (live && !ok) ? 1u : 0u;
+  g.live = (live && ok) ? 1u : 0u;
   const uint32_t bits = __float_as_uint(G);
   const int32_t eg = (int32_t)((bits >> 23) & 0xffu) - 127;
   const uint64_t mant = (uint64_t)((bits & 0x7fffffu) | 0x800000u);
   const int32_t p = (int32_t)n + eg - 23;  // exponent of the mantissa's lowest bit
   g.bin = p >> 5;                          // floor(p / 32)
   const uint64_t v = mant << (uint32_t)(p & 31);
-  g.lo = (uint32_t)v;
-  g.hi = (uint32_t)(v >> 32);
+  g.lo = g.live ? (uint32_t)v : 0u;
+  g.hi = g.live ? (uint32_t)(v >> 32) : 0u;
   return g;
 }
 
-// Adds a group's pieces to an accumulator whose window already reaches bin + 1.
+// Adds a group's pieces to an accumulator whose window already reaches bin + 1 (a group
+// that is not live has zero pieces). Branch-free: each bin takes the piece that lands in it.
 __device__ __forceinline__ void accx_add(AccX& a, const GroupPiece& g) {
   a.bad |= g.bad;
-  if (!g.live) return;
   const int32_t rel = a.top - (g.bin + 1);
-  if (rel == 0) {
-    a.b2 += g.hi;
-    a.b1 += g.lo;
-  } else if (rel == 1) {
-    a.b1 += g.hi;
-    a.b0 += g.lo;
-  } else if (rel == 2) {
-    a.b0 += g.hi;
-  }
+  a.b2 += (uint64_t)(rel == 0 ? g.hi : 0u);
+  a.b1 += (uint64_t)(rel == 0 ? g.lo : (rel == 1 ? g.hi : 0u));
+  a.b0 += (uint64_t)(rel == 1 ? g.lo : (rel == 2 ? g.hi : 0u));
 }
 
 // log2 of the accumulated value (-inf when empty). The three bins are combined into one
