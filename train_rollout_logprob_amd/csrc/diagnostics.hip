@@ -13,6 +13,10 @@
 //   diag_hist 1,2  histogram of the next digit among keys whose upper digits match the
 //                  ones chosen so far, one histogram per quantile; the last tile picks the
 //                  digit, and after the third digit the keys are exact.
+// diag_segments (drift_segment_diagnostics) computes the same statistics per segment of
+// rows (per sequence, per batch row or per rank) in one launch, one block per segment.
+// Every statistics record also carries mismatch_kl = -mean(d), the k1 estimator of
+// KL(rollout || train) ("Attention Debug Matrix", Metrics); approx_kl0 is its k3 form.
 // Keys are the IEEE bit patterns of |d| (fabs clears the sign bit), whose unsigned order
 // is the order of the values, so the selection is an MSB-first radix select with digits
 // of 11, 11 and 10 bits. Counts and digit choices are integer work whose result does not

@@ -142,8 +142,8 @@ __global__ void __launch_bounds__(256) lm_pad_hidden(const uint16_t* __restrict_
 // per CU), the 32 blocks that the dispatcher sends to one XCD (ids equal mod 8) form a
 // (kGroupV / 4) x (kGroupT / 2) sub-grid, so they share operand panels in that XCD's L2.
 // Ids past the end map outside the grid and exit.
-__device__ __forceinline__ void tile_of(int64_t b, int64_t nVt_pad, int64_t nTt_pad,
-                                        int64_t& vt, int64_t& tt) {
+__device__ __forceinline__ void tile_of(int64_t b, int64_t nTt_pad, int64_t& vt,
+                                        int64_t& tt) {
   const int64_t per_group = (int64_t)kGroupV * nTt_pad;
   const int64_t g = b / per_group, j = b % per_group;
   const int64_t chunk = j / (kGroupV * kGroupT), jj = j % (kGroupV * kGroupT);
@@ -249,7 +249,6 @@ __device__ __forceinline__ void lse_epilogue(const f32x16 (&acc)[TM][TN], const 
 // the fragment reads (16 lanes = 16 consecutive rows at one logical chunk) hit 16 distinct
 // 4-bank groups. The four buffers (A and B, two stages) are separate LDS arrays and the
 // stage loop is unrolled by two, so every access names its buffer at compile time.
-constexpr int kDRowBytes = kBK * 2;  // 128
 __global__ void __launch_bounds__(kPThreads, 1) lm_gemm_lse(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[kBV * kBK];
   __shared__ __attribute__((aligned(1024))) uint16_t sA1[kBV * kBK];
@@ -258,7 +257,7 @@ __global__ void __launch_bounds__(kPThreads, 1) lm_gemm_lse(GemmArgs a) {
   __shared__ float s_k[2][kPW];
   __shared__ double s_s[2][kPW];
   int64_t vt, tt;
-  tile_of(blockIdx.x, a.nVt_pad, a.nTt_pad, vt, tt);
+  tile_of(blockIdx.x, a.nTt_pad, vt, tt);
   if (vt >= a.nVt || tt >= a.nTt) return;  // block-uniform
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wv = wave >> 1, wt = wave & 1;

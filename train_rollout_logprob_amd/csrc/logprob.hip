@@ -24,6 +24,12 @@
 //     (Attention knobs row 6, LSE domain); logp and dlogp are formed in fp64 and rounded
 //     once to fp32.
 // The selected logit is read once by its single owner (LogProb knobs row 8).
+//
+// The same file holds the kernels of the optional outputs and modes, which share the row
+// streaming above: the entropy instantiation of score_rows (a second fp64 moment per
+// partial, LogProb knobs row 11), and score_rows_exact with merge_shards, the
+// order-independent reduction (exact.h) used unsharded or for vocabulary shards whose
+// partials are merged in global shard order (LogProb knobs rows 3-5).
 #include <math.h>
 
 #include <type_traits>
