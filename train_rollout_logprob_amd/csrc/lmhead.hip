@@ -168,7 +168,8 @@ struct GemmArgs {
 // vb + 32 im + 8 (r / 4) + (r % 4), vb = v0 + WV wv + 4 lh. Row tests compare the
 // compile-time offset 32 im + 8 (r / 4) + (r % 4) against per-lane limits, so no
 // per-element index is materialised. The two vocab waves of a token merge through LDS
-// (wave wv = 1 writes, wv = 0 merges and stores).
+// (wave wv = 1 writes the partials of all its tokens, one barrier, wave wv = 0 merges and
+// stores).
 template <int TM, int TN, int WV, int WT>
 __device__ __forceinline__ void lse_epilogue(const f32x16 (&acc)[TM][TN], const GemmArgs& a,
                                              int64_t vt, int64_t v0, int64_t t0, int wv, int wt,
@@ -177,6 +178,7 @@ __device__ __forceinline__ void lse_epilogue(const f32x16 (&acc)[TM][TN], const 
   const int64_t vb = v0 + WV * wv + 4 * lh;
   const int64_t vlim64 = a.V - vb;  // offsets below this are real vocab rows
   const int vlim = vlim64 > WV ? WV : (int)vlim64;
+  Acc pt[TN];  // this lane's merged partial of each of its tokens
 #pragma unroll
   for (int in = 0; in < TN; ++in) {
     const int64_t t = t0 + WT * wt + 32 * in + lr;
@@ -219,21 +221,24 @@ __device__ __forceinline__ void lse_epilogue(const f32x16 (&acc)[TM][TN], const 
     Acc o;
     o.k = __shfl_xor(p.k, 32);
     o.s = __shfl_xor(p.s, 32);
-    p = merge(p, o);
+    pt[in] = merge(p, o);
     if (wv == 1 && lh == 0) {
-      s_k[wt][32 * in + lr] = p.k;
-      s_s[wt][32 * in + lr] = p.s;
+      s_k[wt][32 * in + lr] = pt[in].k;
+      s_s[wt][32 * in + lr] = pt[in].s;
     }
-    __syncthreads();
-    if (wv == 0 && lh == 0) {
-      const Acc q = merge(p, Acc{s_k[wt][32 * in + lr], s_s[wt][32 * in + lr]});
+  }
+  __syncthreads();  // one exchange for all the wave's tokens
+  if (wv == 0 && lh == 0) {
+#pragma unroll
+    for (int in = 0; in < TN; ++in) {
+      const int64_t t = t0 + WT * wt + 32 * in + lr;
+      const Acc q = merge(pt[in], Acc{s_k[wt][32 * in + lr], s_s[wt][32 * in + lr]});
       Partial out;
       out.k = q.k;
       out.pad = 0.0f;
       out.s = q.s;
       a.part[vt * a.Tp + t] = out;
     }
-    __syncthreads();
   }
 }
 
