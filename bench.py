@@ -96,6 +96,46 @@ def recorded_traffic(profile=TRAFFIC_PROFILE, files=SCORE_SOURCES):
         return None
 
 
+def read_ceiling(case, reps=10, warmup=2):
+    """Pure-read rate (GB/s) of the same logits tensors with the scoring kernels' access
+    pattern: every row pair, one block per pair, 16-byte nontemporal loads
+    (libdrift_ceiling.so, measurement only). HIP events on the launch stream, median."""
+    import torch
+
+    from train_rollout_logprob_amd import build as Bd
+
+    if not os.path.exists(Bd.CEILING_LIB):
+        raise RuntimeError(f"{Bd.CEILING_LIB} is missing: run __graft_entry__.build()")
+    lib = ctypes.CDLL(Bd.CEILING_LIB)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.drift_read_ceiling.argtypes = [vp, vp, i64, i64, i64, vp, vp]
+    lib.drift_read_ceiling.restype = ctypes.c_int
+    esz = case.train.element_size()
+    rows = case.train.shape[0]
+    row_bytes = case.train.shape[1] * esz // 16 * 16
+    stride = case.train.stride(0) * esz
+    sink = torch.empty(rows * 4, dtype=torch.int32, device=case.train.device)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        st = lib.drift_read_ceiling(case.train.data_ptr(), case.rollout.data_ptr(), rows,
+                                    row_bytes, stride, sink.data_ptr(), stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"drift_read_ceiling: status {st}")
+
+    for _ in range(warmup):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[reps // 2]
+    return 2 * rows * row_bytes / (ms * 1e-3) / 1e9, ms
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -438,6 +478,9 @@ def main():
         f"({achieved:.0f} GB/s), {value / 1e6:.3f} M active tok/s")
 
     cpu = None
+    ceiling_gbs, ceiling_ms = read_ceiling(case)
+    log(f"[bench] pure-read ceiling of the same tensors: {ceiling_gbs:.0f} GB/s "
+        f"({ceiling_ms:.3f} ms); scoring kernel at {achieved / ceiling_gbs:.3f} of it")
 
     line = {
         "metric": METRIC,
@@ -462,7 +505,10 @@ def main():
                      "traffic": recorded_traffic()
                      if args.workload == "qwen8b" and args.xf == "none" else None,
                      "kernel": f"score_rows<{case.dtype}>", "kernel_ms": kern_avg,
-                     "bytes_per_launch": alg_bytes},
+                     "bytes_per_launch": alg_bytes,
+                     "ceiling_gbs": ceiling_gbs, "frac_of_ceiling": achieved / ceiling_gbs,
+                     "ceiling_kernel": "read_rows: pure 16-byte nontemporal reads of every "
+                                       "row pair of the same tensors, one block per pair"},
         "cpu_baseline": cpu,
     }
     stats = {k: getattr(runner.stats, k) for k in (

@@ -181,3 +181,47 @@ def test_shard_and_merge_host_checks():
     a.entropy[0] = e
     assert B.lib.drift_selected_logprob(ctypes.byref(a), None, None, None, None, None, 0,
                                         None) == B.DRIFT_EINVAL
+
+
+CEILING_HEADER = os.path.join(ROOT, "include", "drift_ceiling.h")
+
+
+def _ceiling_lib():
+    from train_rollout_logprob_amd import build as Bd
+    if not os.path.exists(Bd.CEILING_LIB):
+        pytest.skip("libdrift_ceiling.so is not built")
+    lib = ctypes.CDLL(Bd.CEILING_LIB)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.drift_read_ceiling.argtypes = [vp, vp, i64, i64, i64, vp, vp]
+    lib.drift_read_ceiling.restype = ctypes.c_int
+    return lib
+
+
+def test_ceiling_library_exports_its_declared_symbol():
+    src = re.sub(r"/\*.*?\*/", "", open(CEILING_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(drift_[a-z_]+)\s*\(", src)))
+    assert names == ["drift_read_ceiling"]
+    lib = _ceiling_lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_ceiling_host_checks_fail_before_launch():
+    lib = _ceiling_lib()
+    good = 1 << 20                                     # an aligned address, never dereferenced
+    EINVAL = -1
+    assert lib.drift_read_ceiling(None, None, 0, 16, 16, None, None) == 0   # nothing to read
+    cases = [
+        (good, good, -1, 16, 16, good),                # negative rows
+        (good, good, 1 << 31, 16, 16, good),           # rows beyond a grid
+        (good, good, 1, 0, 16, good),                  # empty rows
+        (good, good, 1, 24, 32, good),                 # row bytes not a multiple of 16
+        (good, good, 1, 32, 16, good),                 # stride below the row
+        (good, good, 1, 16, 24, good),                 # stride not a multiple of 16
+        (None, good, 1, 16, 16, good),                 # null input
+        (good, good, 1, 16, 16, None),                 # null sink
+        (good + 8, good, 1, 16, 16, good),             # misaligned input
+        (good, good, 1, 16, 16, good + 2),             # misaligned sink
+    ]
+    for a, b, rows, rb, st, sink in cases:
+        assert lib.drift_read_ceiling(a, b, rows, rb, st, sink, None) == EINVAL, (rows, rb, st)

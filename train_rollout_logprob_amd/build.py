@@ -1,4 +1,5 @@
-"""Compile the HIP sources into the in-tree shared library ``libdrift.so`` (gfx950)."""
+"""Compile the HIP sources into the in-tree shared library ``libdrift.so`` (gfx950), and the
+measurement-only read kernel into ``libdrift_ceiling.so``."""
 from __future__ import annotations
 
 import hashlib
@@ -16,6 +17,8 @@ LIB = os.path.join(PKG, "libdrift.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 SOURCES = ["api.hip", "logprob.hip", "diagnostics.hip", "lmhead.hip", "dlogits.hip"]
 HEADERS = ["common.h", "classify.h", "lse.h", "rowio.h"]
+CEILING_LIB = os.path.join(PKG, "libdrift_ceiling.so")
+CEILING_SOURCE = "ceiling.hip"
 
 ARCH = "gfx950"
 FLAGS = [
@@ -80,5 +83,19 @@ def build(verbose: bool = False, defines=(), out: str = LIB, build_dir: str = BU
     return out
 
 
+def build_ceiling(out: str = CEILING_LIB) -> str:
+    """Compile and link the measurement-only read kernel (no part of the drift library)."""
+    hipcc = _hipcc()
+    tmp = out + ".tmp"
+    cmd = [hipcc, *FLAGS, f"-I{INCLUDE}", "-shared", "-o", tmp, os.path.join(CSRC, CEILING_SOURCE)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
+        raise RuntimeError(f"hipcc failed on {CEILING_SOURCE}:\n{msg}")
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_ceiling())
