@@ -8,8 +8,9 @@
 // split of a row into pieces, reduced in any order and merged in any order, gives the
 // same bits:
 //   * a group of VEC consecutive columns (aligned to VEC in the global column index) gives
-//     one value G * 2^n, with n = ceil(max x * log2 e) of the group and
-//     G = sum of exp2(x * log2 e - n) in fp32, pairwise: a function of the group alone;
+//     one value G * 2^n, with n = ceil(x * log2 e) of the group's first logit (of its
+//     largest where the first does not serve, group_piece) and G = sum of
+//     exp2(x * log2 e - n) in fp32, pairwise: a function of the group alone;
 //   * the value's 24 mantissa bits are cut at absolute bit positions that are multiples
 //     of 32 ("bins") and added as integers into the bins;
 //   * an accumulator keeps the three highest bins it has seen (top, top-1, top-2) in
@@ -82,14 +83,9 @@ struct GroupPiece {
   uint32_t bad;
 };
 
+// sum of exp2(x * log2e - n) over the group in fp32, pairwise
 template <int VEC>
-__device__ __forceinline__ GroupPiece group_piece(const float (&x)[VEC]) {
-  GroupPiece g;
-  float m = x[0];
-#pragma unroll
-  for (int i = 1; i < VEC; ++i) m = fmaxf(m, x[i]);  // NaN-ignoring
-  const bool live = m != -INFINITY;
-  const float n = live ? ceilf(m * kLog2e) : 0.0f;
+__device__ __forceinline__ float group_exp_sum(const float (&x)[VEC], float n) {
   float e[VEC];
 #pragma unroll
   for (int i = 0; i < VEC; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(x[i], kLog2e, -n));
@@ -98,10 +94,33 @@ __device__ __forceinline__ GroupPiece group_piece(const float (&x)[VEC]) {
 #pragma unroll
     for (int i = 0; i + st < VEC; i += 2 * st) e[i] = e[i] + e[i + st];
   }
-  const float G = e[0];
-  // G >= 2^-2 for a finite group (its largest term is about 1); NaN, +inf or a huge
-  // exponent fail closed
-  const bool ok = fabsf(n) <= kMaxGroupExp && G >= 0.125f && G <= 64.0f;
+  return e[0];
+}
+
+// The group's exponent n is taken from its first logit: that term is then in (1/2, 1], so
+// G >= 1/2, and G stays finite while no logit of the group exceeds the first by more than
+// about 88. Otherwise (first logit -inf or out of range, G overflowing, a NaN or +inf
+// logit) n comes from the group's maximum, where G is in [1, 8] for finite logits. Either
+// way G * 2^n is a function of the group alone. Only the maximum-based exponent decides
+// failure: the first-logit path requires |n| <= 2^24 - 128, and a finite G there bounds
+// the maximum's exponent by n + 128.
+template <int VEC>
+__device__ __forceinline__ GroupPiece group_piece(const float (&x)[VEC]) {
+  GroupPiece g;
+  float n = ceilf(x[0] * kLog2e);
+  float G = group_exp_sum<VEC>(x, n);
+  bool live = true;
+  bool ok = fabsf(n) <= kMaxGroupExp - 128.0f && G <= 3.4028235e38f;  // false for NaN
+  if (!ok) {
+    float m = x[0];
+#pragma unroll
+    for (int i = 1; i < VEC; ++i) m = fmaxf(m, x[i]);  // NaN-ignoring
+    live = m != -INFINITY;
+    n = live ? ceilf(m * kLog2e) : 0.0f;
+    G = group_exp_sum<VEC>(x, n);
+    // NaN, +inf or a huge exponent fail closed
+    ok = fabsf(n) <= kMaxGroupExp && G >= 0.125f && G <= 64.0f;
+  }
   g.bad = (live && !ok) ? 1u : 0u;
   g.live = (live && ok) ? 1u : 0u;
   const uint32_t bits = __float_as_uint(G);

@@ -47,7 +47,11 @@ constexpr float kRaise = 16.0f;  // a group sum at or above this raises the wave
 
 // exp2 terms of one group in fp32, summed pairwise; with ENT also the first moment of
 // the exponent, sum of 2^a * a over the group (a = x*log2e - k) as a chain of fp32 FMAs in
-// element order; -inf exponents contribute 0.
+// element order; -inf exponents contribute 0. The moment is first taken without a guard: a
+// -inf exponent then gives 0 * -inf = NaN, and only such groups (masked or -inf columns)
+// take it again with the exponent clamped to -1e30. Both give the same bits wherever the
+// first is not NaN (a term with a below -1e30 has 2^a = 0 and adds a signed zero to the
+// chain either way).
 template <int VEC, bool ENT>
 __device__ __forceinline__ void group_sums(const float (&x)[VEC], float nk, float& t, float& t2) {
   float e[VEC];
@@ -56,7 +60,14 @@ __device__ __forceinline__ void group_sums(const float (&x)[VEC], float nk, floa
   for (int i = 0; i < VEC; ++i) {
     const float a = fmaf(x[i], kLog2e, nk);
     e[i] = __builtin_amdgcn_exp2f(a);
-    if constexpr (ENT) w = fmaf(e[i], fmaxf(a, -1.0e30f), w);
+    if constexpr (ENT) w = fmaf(e[i], a, w);
+  }
+  if constexpr (ENT) {
+    if (w != w) {
+      w = 0.0f;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) w = fmaf(e[i], fmaxf(fmaf(x[i], kLog2e, nk), -1.0e30f), w);
+    }
   }
 #pragma unroll
   for (int st = 1; st < VEC; st *= 2) {
