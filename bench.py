@@ -258,7 +258,8 @@ def exact_leg(case, ids, att, act, cu, shards=8, steps=10, warmup=2):
     st, _ = B.drift_get_status(out[4])
     if st != B.DRIFT_OK:
         raise RuntimeError(f"exact scoring: status {B.STATUS_NAMES[st]}")
-    ex_ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)) / steps
+    ex_all = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps))
+    ex_ms = sum(ex_all) / steps
     ex_bytes = n_active * V * esz * 2
     width = (V // shards) // 8 * 8
     bounds = [width * s for s in range(shards)] + [V]
@@ -292,6 +293,7 @@ def exact_leg(case, ids, att, act, cu, shards=8, steps=10, warmup=2):
         "workload": f"same batch; exact reduction unsharded, then {shards} vocabulary shards "
                     f"of {width} columns (column views) + shard-order merge",
         "exact": {"kernel": f"score_rows_exact<{case.dtype}>", "kernel_ms": ex_ms,
+                  "kernel_ms_median": ex_all[steps // 2], "kernel_ms_min": ex_all[0],
                   "bytes_per_launch": ex_bytes,
                   "achieved_gbs": ex_bytes / (ex_ms * 1e-3) / 1e9,
                   "frac": ex_bytes / (ex_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
@@ -330,7 +332,8 @@ def training_leg(case, ids, att, act, cu, steps=10, warmup=2):
     st, _ = B.drift_get_status(out[4])
     if st != B.DRIFT_OK:
         raise RuntimeError(f"scoring with entropy: status {B.STATUS_NAMES[st]}")
-    ent_ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)) / steps
+    ent_all = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps))
+    ent_ms = sum(ent_all) / steps
     ent_bytes = n_active * V * esz * 2
     active = out[3]
     g = torch.randn(N, dtype=torch.float32, device=dev, generator=torch.Generator(
@@ -353,7 +356,8 @@ def training_leg(case, ids, att, act, cu, steps=10, warmup=2):
         "workload": "same batch; entropy + LSE of both sides from the scoring pass, then "
                     "dlogits of the train side (bf16 out, upstream gradient per row)",
         "score_with_entropy": {"kernel": f"score_rows<{case.dtype}, entropy>",
-                               "kernel_ms": ent_ms, "bytes_per_launch": ent_bytes,
+                               "kernel_ms": ent_ms, "kernel_ms_median": ent_all[steps // 2],
+                               "kernel_ms_min": ent_all[0], "bytes_per_launch": ent_bytes,
                                "achieved_gbs": ent_bytes / (ent_ms * 1e-3) / 1e9,
                                "frac": ent_bytes / (ent_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "dlogits": {"kernel": f"dlogits_rows<{case.dtype}, bf16>", "kernel_ms": dl_ms,
