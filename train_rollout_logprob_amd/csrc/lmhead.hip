@@ -165,16 +165,20 @@ struct GemmArgs {
 // Epilogue of the GEMM kernels: each token's logits of this block become one (k, s)
 // log-sum-exp partial; the single owner of z[t, y_t] records it. Lane (lr, lh) of wave
 // (wv, wt) holds, for token t = t0 + WT wt + 32 in + lr, the logits of vocab rows
-// vb + 32 im + 8 (r / 4) + (r % 4), vb = v0 + WV wv + 4 lh. Row tests compare the
-// compile-time offset 32 im + 8 (r / 4) + (r % 4) against per-lane limits, so no
-// per-element index is materialised. The two vocab waves of a token merge through LDS
-// (wave wv = 1 writes the partials of all its tokens, one barrier, wave wv = 0 merges and
-// stores).
-template <int TM, int TN, int WV, int WT>
+// vb + 32 im + 8 (r / 4) + (r % 4), vb = v0 + WV wv + 4 lh, i.e. the offsets from vb whose
+// bit 2 is clear. FULL (every vocab row of the block is real: all tiles but the last) drops
+// the per-row range tests; otherwise they compare the compile-time offset against a
+// per-lane limit. The owner of y (offset y - vb in [0, WV) with bit 2 clear) takes z[t, y]
+// out of its 64 values with a select tree on the offset's bits and stores it once. The two
+// vocab waves of a token merge through LDS (wave wv = 1 writes the partials of all its
+// tokens, one barrier, wave wv = 0 merges and stores).
+template <int TM, int TN, int WV, int WT, bool FULL>
 __device__ __forceinline__ void lse_epilogue(const f32x16 (&acc)[TM][TN], const GemmArgs& a,
                                              int64_t vt, int64_t v0, int64_t t0, int wv, int wt,
                                              int lr, int lh, float (*s_k)[WT],
                                              double (*s_s)[WT]) {
+  static_assert(TM == 4 && WV == 128, "the select tree covers 4 x 16 values per token");
+  constexpr int NZ = TM * 16;
   const int64_t vb = v0 + WV * wv + 4 * lh;
   const int64_t vlim64 = a.V - vb;  // offsets below this are real vocab rows
   const int vlim = vlim64 > WV ? WV : (int)vlim64;
@@ -185,16 +189,33 @@ __device__ __forceinline__ void lse_epilogue(const f32x16 (&acc)[TM][TN], const 
     const int64_t y = (t < a.T) ? (int64_t)a.ids[t] : -1;
     const int64_t yr64 = y - vb;
     const int yrel = (y >= 0 && yr64 >= 0 && yr64 < WV) ? (int)yr64 : -1;
+    // value i = 16 im + r sits at offset 32 im + 8 (r / 4) + (r % 4); rows past V are -inf
+    float z[NZ];
+#pragma unroll
+    for (int i = 0; i < NZ; ++i) {
+      const int off = 32 * (i >> 4) + 8 * ((i & 15) >> 2) + (i & 3);
+      z[i] = (FULL || off < vlim) ? acc[i >> 4][in][i & 15] : -INFINITY;
+    }
+    if (yrel >= 0 && (yrel & 4) == 0) {
+      // the owner: i = 16 (bits 5-6) + 4 (bits 3-4) + (bits 0-1) of the offset, picked by a
+      // select tree on i's bits (all-ones / zero lane masks, no branches)
+      const uint32_t i_sel = (uint32_t)(((yrel >> 5) << 4) | (((yrel >> 3) & 3) << 2) | (yrel & 3));
+      uint32_t u[NZ / 2];
+      const uint32_t m0 = 0u - (i_sel & 1u);
+#pragma unroll
+      for (int q = 0; q < NZ / 2; ++q)
+        u[q] = (m0 & __float_as_uint(z[2 * q + 1])) | (~m0 & __float_as_uint(z[2 * q]));
+#pragma unroll
+      for (int b = 1, n = NZ / 4; n >= 1; ++b, n >>= 1) {
+        const uint32_t mb = 0u - ((i_sel >> b) & 1u);
+#pragma unroll
+        for (int q = 0; q < n; ++q) u[q] = (mb & u[2 * q + 1]) | (~mb & u[2 * q]);
+      }
+      a.zsel[t] = __uint_as_float(u[0]);
+    }
     float m = -INFINITY;
 #pragma unroll
-    for (int im = 0; im < TM; ++im)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int off = 32 * im + 8 * (r / 4) + (r % 4);
-        const float z = acc[im][in][r];
-        if (off < vlim) m = fmaxf(m, z);
-        if (off == yrel) a.zsel[t] = z;  // the single owner of z[t, y_t]
-      }
+    for (int i = 0; i < NZ; ++i) m = fmaxf(m, z[i]);
     Acc p = {-INFINITY, 0.0};
     if (m > -INFINITY) {
       const float k = ceilf(m * kLog2e);
@@ -204,12 +225,7 @@ __device__ __forceinline__ void lse_epilogue(const f32x16 (&acc)[TM][TN], const 
       } else {
         const float nk = -k;
 #pragma unroll
-        for (int im = 0; im < TM; ++im)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int off = 32 * im + 8 * (r / 4) + (r % 4);
-            if (off < vlim) s += __builtin_amdgcn_exp2f(fmaf(acc[im][in][r], kLog2e, nk));
-          }
+        for (int i = 0; i < NZ; ++i) s += __builtin_amdgcn_exp2f(fmaf(z[i], kLog2e, nk));
       }
       p.k = (k == INFINITY) ? 0.0f : k;
       p.s = (double)s;
@@ -217,7 +233,7 @@ __device__ __forceinline__ void lse_epilogue(const f32x16 (&acc)[TM][TN], const 
       p.k = 0.0f;
       p.s = NAN;
     }
-    // the other half of the wave holds the other 4-row groups of the same token
+  // the other half of the wave holds the other 4-row groups of the same token
     Acc o;
     o.k = __shfl_xor(p.k, 32);
     o.s = __shfl_xor(p.s, 32);
@@ -381,7 +397,10 @@ __global__ void __launch_bounds__(kPThreads, 1) lm_gemm_lse(GemmArgs a) {
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
 
-  lse_epilogue<kPT, kPT, kPW, kPW>(acc, a, vt, v0, t0, wv, wt, lr, lh, s_k, s_s);
+  if (v0 + kBV <= a.V)  // block-uniform
+    lse_epilogue<kPT, kPT, kPW, kPW, true>(acc, a, vt, v0, t0, wv, wt, lr, lh, s_k, s_s);
+  else
+    lse_epilogue<kPT, kPT, kPW, kPW, false>(acc, a, vt, v0, t0, wv, wt, lr, lh, s_k, s_s);
 }
 
 // Four lanes per token: lane q folds the vocab tiles [q*c, (q+1)*c) in ascending order
