@@ -318,7 +318,7 @@ int drift_segment_diagnostics(const float* dlogp, const uint8_t* active, int64_t
 
 /* Fused LM-head selected logprob: logits z = hidden x W are formed tile by tile on the
  * matrix cores and never written to memory; logp[t] = z[t, y_t] - LSE(z[t]).
- *   hidden      bf16 [T, H] row-major (16-byte aligned rows: H % 8 == 0)
+ *   hidden      bf16 [T, H] row-major (16-byte aligned rows: H % 8 == 0; H <= 2^22)
  *   weight      bf16 [H, V] row-major, vocabulary contiguous (V % 8 == 0)
  *   target_ids  int32 [T]; active (nullable) uint8 [T]: inactive rows get 0.0
  *   logp        fp32 [T]

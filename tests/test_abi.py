@@ -103,6 +103,9 @@ def test_host_checks_fail_closed_without_launching():
                                  None) == B.DRIFT_EINVAL                # eps out of range
     assert lib.drift_lmhead_logprob(None, None, 4, 4100, 16, None, None, None, None, 0,
                                     None) == B.DRIFT_EINVAL             # H % 8 != 0
+    big = 1 << 20                                     # aligned addresses, never dereferenced
+    assert lib.drift_lmhead_logprob(big, big, 4, (1 << 22) + 8, 16, big, None, big, big, 1 << 40,
+                                    None) == B.DRIFT_EINVAL             # H above 2^22
     assert lib.drift_get_status(None, None, None) == B.DRIFT_EWORKSPACE
     # vocab_real and transform chains are checked before the workspace
     a.layout, a.num_rows, a.batch, a.seq_len, a.vocab, a.row_stride = B.DRIFT_PAD_RIGHT, 0, 0, 1, 10, 10

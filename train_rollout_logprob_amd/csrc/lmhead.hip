@@ -28,6 +28,8 @@ namespace drift {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -263,7 +265,7 @@ __device__ __forceinline__ void lse_epilogue(const f32x16 (&acc)[TM][TN], const 
 // stage the four 16-wide steps are interleaved by hand with the memory work: the MFMAs of
 // a step run while the next step's fragments are read from LDS into the other register
 // set. The stage tiles move from global memory into
-// LDS with global_load_lds_dwordx4 (lane l of an instruction fills bytes [16 l, 16 l + 16)
+// LDS with buffer_load_dwordx4 ... lds (lane l of an instruction fills bytes [16 l, 16 l + 16)
 // of a 1 KB LDS span, checked on the GPU), so no VGPRs hold them and the LDS fills count
 // on vmcnt while the fragment reads alone count on lgkmcnt. Rows are 128 bytes without
 // padding; the 16-byte chunk c of row r is stored at chunk c ^ ((r >> 1) & 7), which makes
@@ -300,15 +302,24 @@ __global__ void __launch_bounds__(kPThreads, 1) lm_gemm_lse(GemmArgs a) {
   const uint32_t lane_off[2] = {
       (uint32_t)(((lane >> 3) * a.Hp + (((lane & 7) ^ ((lane >> 4) & 7)) * 8)) * 2),
       (uint32_t)(((lane >> 3) * a.Hp + (((lane & 7) ^ ((4 + (lane >> 4)) & 7)) * 8)) * 2)};
+  // The fills go through buffer resources over the block's two operand panels (256 rows x
+  // Hp each; reads past a panel return 0): the per-lane byte offset is one of the two
+  // constants above and the rest is one scalar offset per instruction, so no address
+  // arithmetic or address registers are needed in the loop.
+  const uint32_t panel_bytes = (uint32_t)(kBV * a.Hp * 2);
+  const __amdgpu_buffer_rsrc_t rA =
+      __builtin_amdgcn_make_buffer_rsrc((void*)gA, (short)0, panel_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rB =
+      __builtin_amdgcn_make_buffer_rsrc((void*)gB, (short)0, panel_bytes, 0x00020000);
   auto fill = [&](uint16_t* dA, uint16_t* dB, int64_t k0) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int r0 = (wave_u * 8 + j) * 8;
-      const int64_t rowk = (int64_t)r0 * a.Hp + k0;
-      const char* srcA = (const char*)(gA + rowk) + lane_off[j & 1];
-      const char* srcB = (const char*)(gB + rowk) + lane_off[j & 1];
-      __builtin_amdgcn_global_load_lds(srcA, dA + r0 * kBK, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(srcB, dB + r0 * kBK, 16, 0, 0);
+      const uint32_t so = (uint32_t)(((int64_t)r0 * a.Hp + k0) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr)(dA + r0 * kBK), 16, lane_off[j & 1],
+                                               so, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr)(dB + r0 * kBK), 16, lane_off[j & 1],
+                                               so, 0, 0);
     }
   };
 
