@@ -2,17 +2,16 @@
 // Diagnostics table): ratio0, clipfrac0, approx_kl0, mean |dlogp|, and p95/p99/max
 // |dlogp| as exact nearest-rank order statistics (the ceil(q*n)-th smallest value).
 //
-// Four launches over tiles of kDiagTile rows (G tiles):
-//   diag_init      zeroes the three digit histograms and the tile tickets;
-//   diag_tile      per tile: fp64 sums of |d|, exp(d), expm1(d) - d and d in a fixed
-//                  order, the active / clipped / non-finite counts, the largest key with
-//                  its first row, and the histogram of the top 11 bits of the keys
-//                  (integer atomics into one global histogram). The last tile to finish
-//                  (atomic ticket) folds the tile partials in tile order into the
-//                  statistics, derives the nearest ranks and picks the top digit;
-//   diag_hist 1,2  histogram of the next digit among keys whose upper digits match the
-//                  ones chosen so far, one histogram per quantile; the last tile picks the
-//                  digit, and after the third digit the keys are exact.
+// Two launches:
+//   diag_tile      one block per tile of kDiagTile rows (G tiles): fp64 sums of |d|,
+//                  exp(d), expm1(d) - d and d in a fixed order, the active / clipped /
+//                  non-finite counts and the largest key with its first row, written as
+//                  one partial per tile;
+//   diag_select    one block of kSelThreads: folds the tile partials in a fixed order (lane
+//                  j of wave 0 takes tiles j, j + 64, ..., then the 64 lane results in lane
+//                  order) into the statistics, derives the nearest ranks and runs the
+//                  three-digit radix select over all keys with LDS histograms, one per
+//                  quantile, re-reading the keys once per digit (they stay in L2).
 // diag_segments (drift_segment_diagnostics) computes the same statistics per segment of
 // rows (per sequence, per batch row or per rank) in one launch, one block per segment.
 // Every statistics record also carries mismatch_kl = -mean(d), the k1 estimator of
@@ -45,23 +44,20 @@ struct TilePartial {
 };
 static_assert(sizeof(TilePartial) == 128, "partial size");
 
+constexpr int kSelThreads = 1024;                // the selection block
+
 struct SelState {
   drift_stats stats;                // the result copied to the host
-  unsigned int prefix[kNumQ];       // selected key bits so far
-  long long rank[kNumQ];            // remaining 1-based rank inside the current bucket
-  long long n;
-  unsigned int ticket[3];           // tiles finished, per pass
 };
 static_assert(sizeof(SelState) <= 512, "state size");
 
 struct DiagLayout {
-  size_t hist_off, partial_off, total;
+  size_t partial_off, total;
   int G;
   __host__ __device__ static DiagLayout make(int64_t N) {
     DiagLayout l;
     l.G = (int)((N + kDiagTile - 1) / kDiagTile);
-    l.hist_off = 512;
-    l.partial_off = l.hist_off + (size_t)3 * kNumQ * kBins * 4;
+    l.partial_off = 512;
     l.total = l.partial_off + align_up((size_t)(l.G > 0 ? l.G : 1) * sizeof(TilePartial), 256);
     return l;
   }
@@ -84,38 +80,15 @@ __device__ __forceinline__ unsigned long long wave_max(unsigned long long v) {
   return v;
 }
 
-__device__ __forceinline__ unsigned int* hist_of(const DiagParams& p, int pass, int q) {
-  return (unsigned int*)(p.ws + DiagLayout::make(p.N).hist_off) + ((size_t)pass * kNumQ + q) * kBins;
-}
-
-// Adds a block's LDS histogram into the global one (integer atomics; order-independent).
-__device__ __forceinline__ void flush_hist(const unsigned int* sh, unsigned int* gh, int nbins) {
-  for (int b = threadIdx.x; b < nbins; b += kDiagThreads)
-    if (sh[b]) atomicAdd(gh + b, sh[b]);
-}
-
-// Every block calls this after its global writes; returns true in the last block to
-// arrive, which then sees all of them.
-__device__ __forceinline__ bool last_block(unsigned int* ticket, unsigned int G) {
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicAdd(ticket, 1u) == G - 1);
-  __syncthreads();
-  if (!s_last) return false;
-  __threadfence();
-  return true;
-}
-
-// Block-cooperative: in histogram h (nbins <= kBins counts, global or LDS), finds the bin
-// holding the 1-based rank `rank`, i.e. the digit d with below < rank <= below + h[d],
-// where below counts the keys in bins before d. Each thread owns kBins / kDiagThreads
-// adjacent bins; an inclusive scan over threads locates the bin. Every thread gets the
-// result.
+// Block-cooperative (NT threads): in histogram h (nbins <= kBins counts, in LDS), finds the
+// bin holding the 1-based rank `rank`, i.e. the digit d with below < rank <= below + h[d],
+// where below counts the keys in bins before d. Each thread owns kBins / NT adjacent bins;
+// an inclusive scan over threads locates the bin. Every thread gets the result.
+template <int NT>
 __device__ void pick_digit(const unsigned int* h, int nbins, long long rank, int& digit,
                            long long& below) {
-  constexpr int PER = kBins / kDiagThreads;
-  __shared__ long long s_scan[kDiagThreads / 64];
+  constexpr int PER = kBins / NT;
+  __shared__ long long s_scan[NT / 64];
   __shared__ int s_digit;
   __shared__ long long s_below;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -149,45 +122,6 @@ __device__ void pick_digit(const unsigned int* h, int nbins, long long rank, int
   digit = s_digit;
   below = s_below;
   __syncthreads();  // s_scan / s_digit are reused by the next call
-}
-
-// Picks the digit of pass `pass` for both quantiles from the global histograms and
-// updates the selection state (read and written by thread 0).
-__device__ void select_digit(SelState* st, const DiagParams& p, int pass) {
-  __shared__ long long s_rank[kNumQ];
-  __shared__ unsigned int s_prefix[kNumQ];
-  const int tid = threadIdx.x;
-  if (tid == 0) {
-    for (int q = 0; q < kNumQ; ++q) {
-      s_rank[q] = st->rank[q];
-      s_prefix[q] = st->prefix[q];
-    }
-  }
-  __syncthreads();
-  const int nbins = 1 << kBitsOf[pass];
-  for (int q = 0; q < kNumQ; ++q) {
-    int digit;
-    long long below;
-    pick_digit(hist_of(p, pass, pass == 0 ? 0 : q), nbins, s_rank[q], digit, below);
-    if (tid == 0) {
-      s_prefix[q] |= (unsigned int)digit << kShift[pass];
-      s_rank[q] -= below;
-    }
-    __syncthreads();
-  }
-  if (tid == 0) {
-    for (int q = 0; q < kNumQ; ++q) {
-      st->prefix[q] = s_prefix[q];
-      st->rank[q] = s_rank[q];
-    }
-  }
-}
-
-__global__ void __launch_bounds__(1024) diag_init(DiagParams p) {
-  SelState* st = (SelState*)p.ws;
-  unsigned int* h = hist_of(p, 0, 0);
-  for (int i = threadIdx.x; i < 3 * kNumQ * kBins; i += 1024) h[i] = 0;
-  if (threadIdx.x < 3) st->ticket[threadIdx.x] = 0;
 }
 
 // Running statistics of a set of active rows. Thread partials are combined by
@@ -287,11 +221,8 @@ __device__ __forceinline__ long long quantile_rank(int q, long long n) {
 }
 
 __global__ void __launch_bounds__(kDiagThreads) diag_tile(DiagParams p) {
-  __shared__ unsigned int s_hist[kBins];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const DiagLayout lay = DiagLayout::make(p.N);
-  for (int b = tid; b < kBins; b += kDiagThreads) s_hist[b] = 0;
-  __syncthreads();
   const double lo_edge = 1.0 - p.eps_low, hi_edge = 1.0 + p.eps_high;
   RowStats acc = {};
   const int64_t tile0 = (int64_t)blockIdx.x * kDiagTile;
@@ -299,12 +230,9 @@ __global__ void __launch_bounds__(kDiagThreads) diag_tile(DiagParams p) {
   for (int j = 0; j < kRowsPerThread; ++j) {
     const int64_t r = tile0 + (int64_t)j * kDiagThreads + tid;
     if (r >= p.N || !p.active[r]) continue;
-    const float df = p.d[r];
-    add_row(acc, df, r, lo_edge, hi_edge);
-    atomicAdd(&s_hist[key_of(df) >> kShift[0]], 1u);
+    add_row(acc, p.d[r], r, lo_edge, hi_edge);
   }
   const RowStats t = block_reduce(acc);
-  TilePartial* tp = (TilePartial*)(p.ws + lay.partial_off);
   if (tid == 0) {
     TilePartial o = {};
     o.s_abs = t.s_abs;
@@ -316,16 +244,66 @@ __global__ void __launch_bounds__(kDiagThreads) diag_tile(DiagParams p) {
     o.hi = t.hi;
     o.nonfinite = t.nf;
     o.best = t.best;
-    tp[blockIdx.x] = o;
+    ((TilePartial*)(p.ws + lay.partial_off))[blockIdx.x] = o;
   }
-  flush_hist(s_hist, hist_of(p, 0, 0), kBins);
-  SelState* st = (SelState*)p.ws;
-  if (!last_block(&st->ticket[0], gridDim.x)) return;
+}
 
-  // last tile: lane j of wave 0 folds tiles j, j + 64, ... in order; thread 0 then folds
-  // the 64 lane results in lane order (a tree fixed by the tile count)
-  __shared__ long long s_n;
+// Block-cooperative (NT threads) three-digit radix select: the nearest-rank keys of both
+// quantiles among the active rows [lo, hi), given their 1-based ranks in s_rank (updated in
+// place); the keys end in s_prefix. With have_top the top-digit histogram is already in
+// s_hist[0]; otherwise it is built here. Each further digit re-reads the rows and counts,
+// per quantile, the keys whose upper digits match the ones chosen so far.
+template <int NT>
+__device__ void radix_select(const float* d, const uint8_t* active, int64_t lo, int64_t hi,
+                             bool have_top, unsigned int (*s_hist)[kBins], long long* s_rank,
+                             unsigned int* s_prefix) {
+  const int tid = threadIdx.x;
+  for (int pass = 0; pass < 3; ++pass) {
+    if (pass > 0 || !have_top) {
+      for (int b = tid; b < kNumQ * kBins; b += NT) (&s_hist[0][0])[b] = 0;
+      __syncthreads();
+      const int shift = kShift[pass];
+      const unsigned int mask = (1u << kBitsOf[pass]) - 1u;
+      if (pass == 0) {
+        for (int64_t r = lo + tid; r < hi; r += NT)
+          if (active[r]) atomicAdd(&s_hist[0][key_of(d[r]) >> shift], 1u);
+      } else {
+        const int hi_shift = kShift[pass - 1];
+        const unsigned int pre0 = s_prefix[0] >> hi_shift, pre1 = s_prefix[1] >> hi_shift;
+        for (int64_t r = lo + tid; r < hi; r += NT) {
+          if (!active[r]) continue;
+          const unsigned int key = key_of(d[r]);
+          if ((key >> hi_shift) == pre0) atomicAdd(&s_hist[0][(key >> shift) & mask], 1u);
+          if ((key >> hi_shift) == pre1) atomicAdd(&s_hist[1][(key >> shift) & mask], 1u);
+        }
+      }
+      __syncthreads();
+    }
+    for (int q = 0; q < kNumQ; ++q) {
+      int digit;
+      long long below;
+      pick_digit<NT>(s_hist[pass == 0 ? 0 : q], 1 << kBitsOf[pass], s_rank[q], digit, below);
+      if (tid == 0) {
+        s_prefix[q] |= (unsigned int)digit << kShift[pass];
+        s_rank[q] -= below;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// The whole batch after diag_tile: folds the tile partials, finishes the statistics and
+// selects p95 / p99.
+__global__ void __launch_bounds__(kSelThreads) diag_select(DiagParams p) {
+  __shared__ unsigned int s_hist[kNumQ][kBins];
+  __shared__ long long s_rank[kNumQ];
+  __shared__ unsigned int s_prefix[kNumQ];
   __shared__ RowStats s_lane[64];
+  __shared__ long long s_n;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const DiagLayout lay = DiagLayout::make(p.N);
+  const TilePartial* tp = (const TilePartial*)(p.ws + lay.partial_off);
+  SelState* st = (SelState*)p.ws;
   if (wave == 0) {
     RowStats a = {};
     for (int g = lane; g < lay.G; g += 64) {
@@ -340,16 +318,19 @@ __global__ void __launch_bounds__(kDiagThreads) diag_tile(DiagParams p) {
     RowStats a = {};
     for (int g = 0; g < 64; ++g) add_stats(a, s_lane[g]);
     finish_stats(st->stats, a, p.lp);
-    st->n = a.n;
     for (int q = 0; q < kNumQ; ++q) {
-      st->rank[q] = quantile_rank(q, a.n);
-      st->prefix[q] = 0;
+      s_rank[q] = quantile_rank(q, a.n);
+      s_prefix[q] = 0;
     }
     s_n = a.n;
   }
   __syncthreads();
   if (s_n == 0) return;  // block-uniform
-  select_digit(st, p, 0);
+  radix_select<kSelThreads>(p.d, p.active, 0, p.N, false, s_hist, s_rank, s_prefix);
+  if (tid == 0) {
+    st->stats.p95_abs_dlogp = __uint_as_float(s_prefix[0]);
+    st->stats.p99_abs_dlogp = __uint_as_float(s_prefix[1]);
+  }
 }
 
 // Per-segment statistics ("Diagnostics" table, per-sequence and per-rank views): one block
@@ -398,69 +379,11 @@ __global__ void __launch_bounds__(kDiagThreads) diag_segments(SegParams p) {
     if (tid == 0) *out = s;
     return;
   }
-  for (int pass = 0; pass < 3; ++pass) {
-    if (pass > 0) {  // histogram of this digit among keys that match the digits so far
-      for (int b = tid; b < kNumQ * kBins; b += kDiagThreads) (&s_hist[0][0])[b] = 0;
-      __syncthreads();
-      const int hi_shift = kShift[pass - 1], shift = kShift[pass];
-      const unsigned int mask = (1u << kBitsOf[pass]) - 1u;
-      const unsigned int pre0 = s_prefix[0] >> hi_shift, pre1 = s_prefix[1] >> hi_shift;
-      for (int64_t r = lo + tid; r < hi; r += kDiagThreads) {
-        if (!p.active[r]) continue;
-        const unsigned int key = key_of(p.d[r]);
-        if ((key >> hi_shift) == pre0) atomicAdd(&s_hist[0][(key >> shift) & mask], 1u);
-        if ((key >> hi_shift) == pre1) atomicAdd(&s_hist[1][(key >> shift) & mask], 1u);
-      }
-      __syncthreads();
-    }
-    for (int q = 0; q < kNumQ; ++q) {
-      int digit;
-      long long below;
-      pick_digit(s_hist[pass == 0 ? 0 : q], 1 << kBitsOf[pass], s_rank[q], digit, below);
-      if (tid == 0) {
-        s_prefix[q] |= (unsigned int)digit << kShift[pass];
-        s_rank[q] -= below;
-      }
-      __syncthreads();
-    }
-  }
+  radix_select<kDiagThreads>(p.d, p.active, lo, hi, true, s_hist, s_rank, s_prefix);
   if (tid == 0) {
     s.p95_abs_dlogp = __uint_as_float(s_prefix[0]);
     s.p99_abs_dlogp = __uint_as_float(s_prefix[1]);
     *out = s;
-  }
-}
-
-__global__ void __launch_bounds__(kDiagThreads) diag_hist(DiagParams p, int pass) {
-  __shared__ unsigned int s_hist[kNumQ][kBins];
-  const int tid = threadIdx.x;
-  SelState* st = (SelState*)p.ws;
-  if (st->n == 0) return;  // written by the previous launch; uniform
-  for (int b = tid; b < kNumQ * kBins; b += kDiagThreads) (&s_hist[0][0])[b] = 0;
-  __syncthreads();
-  const int hi_shift = kShift[pass - 1];
-  const int shift = kShift[pass];
-  const unsigned int mask = (1u << kBitsOf[pass]) - 1u;
-  unsigned int pre[kNumQ];
-#pragma unroll
-  for (int q = 0; q < kNumQ; ++q) pre[q] = st->prefix[q] >> hi_shift;
-  const int64_t tile0 = (int64_t)blockIdx.x * kDiagTile;
-#pragma unroll
-  for (int j = 0; j < kRowsPerThread; ++j) {
-    const int64_t r = tile0 + (int64_t)j * kDiagThreads + tid;
-    if (r >= p.N || !p.active[r]) continue;
-    const unsigned int key = key_of(p.d[r]);
-#pragma unroll
-    for (int q = 0; q < kNumQ; ++q)
-      if ((key >> hi_shift) == pre[q]) atomicAdd(&s_hist[q][(key >> shift) & mask], 1u);
-  }
-  __syncthreads();
-  for (int q = 0; q < kNumQ; ++q) flush_hist(s_hist[q], hist_of(p, pass, q), 1 << kBitsOf[pass]);
-  if (!last_block(&st->ticket[pass], gridDim.x)) return;
-  select_digit(st, p, pass);
-  if (pass == 2 && tid == 0) {
-    st->stats.p95_abs_dlogp = __uint_as_float(st->prefix[0]);
-    st->stats.p99_abs_dlogp = __uint_as_float(st->prefix[1]);
   }
 }
 
@@ -477,11 +400,9 @@ hipError_t launch_segment_diagnostics(const SegParams& p, hipStream_t s) {
 
 hipError_t launch_diagnostics(const DiagParams& p, hipStream_t s) {
   const DiagLayout lay = DiagLayout::make(p.N);
-  const int G = lay.G > 0 ? lay.G : 1;
-  hipLaunchKernelGGL(diag_init, dim3(1), dim3(1024), 0, s, p);
+  const int G = lay.G > 0 ? lay.G : 1;  // one (empty) tile when N = 0
   hipLaunchKernelGGL(diag_tile, dim3(G), dim3(kDiagThreads), 0, s, p);
-  for (int pass = 1; pass < 3; ++pass)
-    hipLaunchKernelGGL(diag_hist, dim3(G), dim3(kDiagThreads), 0, s, p, pass);
+  hipLaunchKernelGGL(diag_select, dim3(1), dim3(kSelThreads), 0, s, p);
   return hipGetLastError();
 }
 
