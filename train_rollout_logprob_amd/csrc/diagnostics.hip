@@ -11,7 +11,8 @@
 //                  j of wave 0 takes tiles j, j + 64, ..., then the 64 lane results in lane
 //                  order) into the statistics, derives the nearest ranks and runs the
 //                  three-digit radix select over all keys with LDS histograms, one per
-//                  quantile, re-reading the keys once per digit (they stay in L2).
+//                  quantile; the first 16 keys of each thread are read once into
+//                  registers, any further keys are re-read per digit (they stay in L2).
 // diag_segments (drift_segment_diagnostics) computes the same statistics per segment of
 // rows (per sequence, per batch row or per rank) in one launch, one block per segment.
 // Every statistics record also carries mismatch_kl = -mean(d), the k1 estimator of
@@ -80,48 +81,61 @@ __device__ __forceinline__ unsigned long long wave_max(unsigned long long v) {
   return v;
 }
 
-// Block-cooperative (NT threads): in histogram h (nbins <= kBins counts, in LDS), finds the
-// bin holding the 1-based rank `rank`, i.e. the digit d with below < rank <= below + h[d],
-// where below counts the keys in bins before d. Each thread owns kBins / NT adjacent bins;
-// an inclusive scan over threads locates the bin. Every thread gets the result.
-template <int NT>
-__device__ void pick_digit(const unsigned int* h, int nbins, long long rank, int& digit,
-                           long long& below) {
-  constexpr int PER = kBins / NT;
-  __shared__ long long s_scan[NT / 64];
-  __shared__ int s_digit;
-  __shared__ long long s_below;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  long long c[PER];
-  long long mine = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int b = tid * PER + i;
-    c[i] = b < nbins ? (long long)h[b] : 0;
-    mine += c[i];
-  }
-  long long inc = mine;
+// Wave 0 of the block: for each quantile q, finds in histogram h[q] (kBins counts in LDS;
+// bins past the digit's range are zero) the bin holding the 1-based rank s_rank[q], i.e.
+// the digit d with below < rank <= below + h[q][d], where below counts the keys in bins
+// before d; appends d to s_prefix[q] at bit `shift` and leaves rank - below in s_rank[q].
+// Two levels: lane l sums bins [32 l, 32 l + 32) and a wave scan of the sums finds the
+// block of 32 bins holding the rank; then lanes 0-31 take one bin each of that block and
+// a second wave scan finds the bin. Counts are 32-bit (a total never exceeds the number
+// of rows, below 2^31). The caller separates this from the histogram writes and from the
+// next reads of s_prefix / s_rank with block barriers.
+__device__ __forceinline__ unsigned int wave_incl_scan(unsigned int v, int lane) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const long long t = __shfl_up(inc, o);
-    if (lane >= o) inc += t;
+    const unsigned int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
   }
-  if (lane == 63) s_scan[wave] = inc;
-  __syncthreads();
-  long long run = inc - mine;
-  for (int w = 0; w < wave; ++w) run += s_scan[w];
+  return v;
+}
+
+__device__ void pick_digits(const unsigned int* h0, const unsigned int* h1, int shift,
+                            long long* s_rank, unsigned int* s_prefix) {
+  constexpr int PER = kBins / 64;
+  const int lane = threadIdx.x;
+  if (lane >= 64) return;
+  const unsigned int* h[kNumQ] = {h0, h1};
+  unsigned int mine[kNumQ], inc[kNumQ];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    if (run < rank && rank <= run + c[i]) {
-      s_digit = tid * PER + i;
-      s_below = run;
-    }
-    run += c[i];
+  for (int q = 0; q < kNumQ; ++q) {
+    unsigned int m = 0;
+    // rotated order: at step j the 32 lanes of a half-wave read 32 distinct banks
+#pragma unroll
+    for (int j = 0; j < PER; ++j) m += h[q][lane * PER + ((j + lane) & (PER - 1))];
+    mine[q] = m;
   }
-  __syncthreads();
-  digit = s_digit;
-  below = s_below;
-  __syncthreads();  // s_scan / s_digit are reused by the next call
+#pragma unroll
+  for (int q = 0; q < kNumQ; ++q) inc[q] = wave_incl_scan(mine[q], lane);
+  unsigned int rank[kNumQ], blk[kNumQ], cnt[kNumQ], inc2[kNumQ];
+#pragma unroll
+  for (int q = 0; q < kNumQ; ++q) {
+    const unsigned int rk = (unsigned int)s_rank[q];  // 1 <= rank <= total < 2^31
+    const unsigned int ex = inc[q] - mine[q];
+    const unsigned long long own = __ballot(ex < rk && rk <= inc[q]);  // exactly one lane
+    blk[q] = own ? (unsigned int)(__ffsll((long long)own) - 1) : 0u;
+    rank[q] = rk - (unsigned int)__shfl((int)ex, (int)blk[q]);
+    cnt[q] = lane < PER ? h[q][blk[q] * PER + lane] : 0u;
+  }
+#pragma unroll
+  for (int q = 0; q < kNumQ; ++q) inc2[q] = wave_incl_scan(cnt[q], lane);
+#pragma unroll
+  for (int q = 0; q < kNumQ; ++q) {
+    const unsigned int ex = inc2[q] - cnt[q];
+    if (ex < rank[q] && rank[q] <= inc2[q]) {  // exactly one lane below PER
+      s_prefix[q] |= (blk[q] * PER + (unsigned int)lane) << shift;
+      s_rank[q] = (long long)(rank[q] - ex);
+    }
+  }
 }
 
 // Running statistics of a set of active rows. Thread partials are combined by
@@ -248,47 +262,68 @@ __global__ void __launch_bounds__(kDiagThreads) diag_tile(DiagParams p) {
   }
 }
 
+constexpr unsigned int kNoKey = 0xffffffffu;  // no row (keys have bit 31 clear)
+constexpr int kSelBatch = 8;                  // rows per thread per batch of loads
+
 // Block-cooperative (NT threads) three-digit radix select: the nearest-rank keys of both
 // quantiles among the active rows [lo, hi), given their 1-based ranks in s_rank (updated in
-// place); the keys end in s_prefix. With have_top the top-digit histogram is already in
-// s_hist[0]; otherwise it is built here. Each further digit re-reads the rows and counts,
-// per quantile, the keys whose upper digits match the ones chosen so far.
-template <int NT>
+// place); the keys end in s_prefix (zero on entry). Rows lo + tid + k NT, k < KC, are read
+// once into registers; rows past lo + KC NT are re-read for every digit in batches of
+// kSelBatch per thread (all loads of a batch issued before any count). Digit h of a
+// quantile counts, in LDS, the keys whose upper digits match the ones chosen so far; the
+// first digit's histogram is shared by both quantiles.
+template <int NT, int KC>
 __device__ void radix_select(const float* d, const uint8_t* active, int64_t lo, int64_t hi,
-                             bool have_top, unsigned int (*s_hist)[kBins], long long* s_rank,
+                             unsigned int (*s_hist)[kBins], long long* s_rank,
                              unsigned int* s_prefix) {
   const int tid = threadIdx.x;
+  unsigned int ck[KC];
+  {
+    uint8_t a[KC];
+    float x[KC];
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      const int64_t r = lo + tid + (int64_t)k * NT;
+      a[k] = r < hi ? active[r] : (uint8_t)0;
+      x[k] = r < hi ? d[r] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < KC; ++k) ck[k] = a[k] ? key_of(x[k]) : kNoKey;
+  }
+  const int64_t rest = lo + (int64_t)KC * NT;
   for (int pass = 0; pass < 3; ++pass) {
-    if (pass > 0 || !have_top) {
-      for (int b = tid; b < kNumQ * kBins; b += NT) (&s_hist[0][0])[b] = 0;
-      __syncthreads();
-      const int shift = kShift[pass];
-      const unsigned int mask = (1u << kBitsOf[pass]) - 1u;
+    for (int b = tid; b < kNumQ * kBins; b += NT) (&s_hist[0][0])[b] = 0;
+    __syncthreads();
+    const int shift = kShift[pass];
+    const unsigned int mask = (1u << kBitsOf[pass]) - 1u;
+    const int hi_shift = pass > 0 ? kShift[pass - 1] : 31;
+    const unsigned int pre0 = s_prefix[0] >> hi_shift, pre1 = s_prefix[1] >> hi_shift;
+    auto count = [&](unsigned int key) {
+      if (key == kNoKey) return;
       if (pass == 0) {
-        for (int64_t r = lo + tid; r < hi; r += NT)
-          if (active[r]) atomicAdd(&s_hist[0][key_of(d[r]) >> shift], 1u);
+        atomicAdd(&s_hist[0][key >> shift], 1u);
       } else {
-        const int hi_shift = kShift[pass - 1];
-        const unsigned int pre0 = s_prefix[0] >> hi_shift, pre1 = s_prefix[1] >> hi_shift;
-        for (int64_t r = lo + tid; r < hi; r += NT) {
-          if (!active[r]) continue;
-          const unsigned int key = key_of(d[r]);
-          if ((key >> hi_shift) == pre0) atomicAdd(&s_hist[0][(key >> shift) & mask], 1u);
-          if ((key >> hi_shift) == pre1) atomicAdd(&s_hist[1][(key >> shift) & mask], 1u);
-        }
+        if ((key >> hi_shift) == pre0) atomicAdd(&s_hist[0][(key >> shift) & mask], 1u);
+        if ((key >> hi_shift) == pre1) atomicAdd(&s_hist[1][(key >> shift) & mask], 1u);
       }
-      __syncthreads();
-    }
-    for (int q = 0; q < kNumQ; ++q) {
-      int digit;
-      long long below;
-      pick_digit<NT>(s_hist[pass == 0 ? 0 : q], 1 << kBitsOf[pass], s_rank[q], digit, below);
-      if (tid == 0) {
-        s_prefix[q] |= (unsigned int)digit << kShift[pass];
-        s_rank[q] -= below;
+    };
+#pragma unroll
+    for (int k = 0; k < KC; ++k) count(ck[k]);
+    for (int64_t base = rest; base < hi; base += (int64_t)NT * kSelBatch) {
+      uint8_t a[kSelBatch];
+      float x[kSelBatch];
+#pragma unroll
+      for (int u = 0; u < kSelBatch; ++u) {
+        const int64_t r = base + tid + (int64_t)u * NT;
+        a[u] = r < hi ? active[r] : (uint8_t)0;
+        x[u] = r < hi ? d[r] : 0.0f;
       }
-      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kSelBatch; ++u) count(a[u] ? key_of(x[u]) : kNoKey);
     }
+    __syncthreads();
+    pick_digits(s_hist[0], s_hist[pass == 0 ? 0 : 1], shift, s_rank, s_prefix);
+    __syncthreads();
   }
 }
 
@@ -326,7 +361,7 @@ __global__ void __launch_bounds__(kSelThreads) diag_select(DiagParams p) {
   }
   __syncthreads();
   if (s_n == 0) return;  // block-uniform
-  radix_select<kSelThreads>(p.d, p.active, 0, p.N, false, s_hist, s_rank, s_prefix);
+  radix_select<kSelThreads, 16>(p.d, p.active, 0, p.N, s_hist, s_rank, s_prefix);
   if (tid == 0) {
     st->stats.p95_abs_dlogp = __uint_as_float(s_prefix[0]);
     st->stats.p99_abs_dlogp = __uint_as_float(s_prefix[1]);
@@ -355,14 +390,10 @@ __global__ void __launch_bounds__(kDiagThreads) diag_segments(SegParams p) {
     return;
   }
   const double lo_edge = 1.0 - p.eps_low, hi_edge = 1.0 + p.eps_high;
-  for (int b = tid; b < kBins; b += kDiagThreads) s_hist[0][b] = 0;
-  __syncthreads();
   RowStats acc = {};
   for (int64_t r = lo + tid; r < hi; r += kDiagThreads) {
     if (!p.active[r]) continue;
-    const float df = p.d[r];
-    add_row(acc, df, r, lo_edge, hi_edge);
-    atomicAdd(&s_hist[0][key_of(df) >> kShift[0]], 1u);
+    add_row(acc, p.d[r], r, lo_edge, hi_edge);
   }
   const RowStats t = block_reduce(acc);
   drift_stats s;
@@ -379,7 +410,7 @@ __global__ void __launch_bounds__(kDiagThreads) diag_segments(SegParams p) {
     if (tid == 0) *out = s;
     return;
   }
-  radix_select<kDiagThreads>(p.d, p.active, lo, hi, true, s_hist, s_rank, s_prefix);
+  radix_select<kDiagThreads, 8>(p.d, p.active, lo, hi, s_hist, s_rank, s_prefix);
   if (tid == 0) {
     s.p95_abs_dlogp = __uint_as_float(s_prefix[0]);
     s.p99_abs_dlogp = __uint_as_float(s_prefix[1]);
