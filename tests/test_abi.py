@@ -228,3 +228,11 @@ def test_ceiling_host_checks_fail_before_launch():
     ]
     for a, b, rows, rb, st, sink in cases:
         assert lib.drift_read_ceiling(a, b, rows, rb, st, sink, None) == EINVAL, (rows, rb, st)
+
+
+def test_build_fingerprint_covers_every_source():
+    """The descriptor's source hash must change with any kernel source or header the
+    library is compiled from."""
+    from train_rollout_logprob_amd import build as Bd
+    on_disk = {f for f in os.listdir(Bd.CSRC) if f.endswith((".hip", ".h"))}
+    assert on_disk - {Bd.CEILING_SOURCE} == set(Bd.SOURCES) | set(Bd.HEADERS)

@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdrift.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 SOURCES = ["api.hip", "logprob.hip", "diagnostics.hip", "lmhead.hip", "dlogits.hip"]
-HEADERS = ["common.h", "classify.h", "lse.h", "rowio.h"]
+HEADERS = ["common.h", "classify.h", "exact.h", "lse.h", "rowio.h"]
 CEILING_LIB = os.path.join(PKG, "libdrift_ceiling.so")
 CEILING_SOURCE = "ceiling.hip"
 
