@@ -27,7 +27,11 @@ def _oracle(case, rows):
     return oracle.lmhead_logprob(_bits(case.hidden), w64, case.ids, rows=rows)
 
 
-@pytest.mark.parametrize("T,H,V", [(300, 264, 1000), (128, 64, 128), (1, 8, 8), (77, 520, 4104)])
+# The last two shapes give the blocks of the persistent grid several tiles each: an even
+# number of K stages (H=256: 4 stages of 64) chains a tile's first fills into the previous
+# tile's last stages, an odd number (H=320: 5) drains and restarts them.
+@pytest.mark.parametrize("T,H,V", [(300, 264, 1000), (128, 64, 128), (1, 8, 8), (77, 520, 4104),
+                                   (2000, 256, 20008), (1537, 320, 20000)])
 def test_parity_ragged_shapes(T, H, V):
     from train_rollout_logprob_amd import binding as B
     print(f"[case] lmhead T={T} H={H} V={V}", flush=True)
