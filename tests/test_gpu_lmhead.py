@@ -27,9 +27,9 @@ def _oracle(case, rows):
     return oracle.lmhead_logprob(_bits(case.hidden), w64, case.ids, rows=rows)
 
 
-# The last two shapes give the blocks of the persistent grid several tiles each: an even
-# number of K stages (H=256: 4 stages of 64) chains a tile's first fills into the previous
-# tile's last stages, an odd number (H=320: 5) drains and restarts them.
+# The last two shapes span hundreds of tiles (more than one per compute unit) with ragged
+# token and vocabulary edges, with an even (H=256: 4 stages of 64) and an odd (H=320: 5)
+# number of K stages.
 @pytest.mark.parametrize("T,H,V", [(300, 264, 1000), (128, 64, 128), (1, 8, 8), (77, 520, 4104),
                                    (2000, 256, 20008), (1537, 320, 20000)])
 def test_parity_ragged_shapes(T, H, V):
