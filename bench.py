@@ -231,6 +231,28 @@ def segments_leg(case, d, active, logprob_ws, steps=20):
                               "max_abs_dlogp": worst["max_abs_dlogp"]}}
 
 
+def active_rows_leg(case, active, steps=20):
+    """The ascending active-row list of the timed batch (drift_active_rows, two small
+    launches): events around `steps` asynchronous calls on the launch stream."""
+    import torch
+
+    from train_rollout_logprob_amd import binding as B
+
+    rows, n, ws = B.active_rows(active)
+    call = (lambda: B.drift_active_rows(active, case.N, rows, n, ws, ws.numel()))
+    for _ in range(3):
+        assert call() == B.DRIFT_OK
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    return {"kernels": "compact_count + compact_scatter", "n_active": int(n.item()),
+            "us_per_call": us, "rows_per_s": case.N / (us * 1e-6)}
+
+
 def exact_leg(case, ids, att, act, cu, shards=8, steps=10, warmup=2):
     """Order-independent (exact) reduction on the same batch: the unsharded exact scoring
     kernel, then the batch split into `shards` vocabulary shards (column views, as
@@ -520,6 +542,8 @@ def main():
         "p95_abs_dlogp", "p99_abs_dlogp", "max_abs_dlogp", "argmax_row")}
     line["diagnostics"] = stats
     line["segments"] = segments_leg(case, runner.out[2], runner.out[3], runner.ws)
+    line["active_rows"] = active_rows_leg(case, runner.out[3])
+    assert line["active_rows"]["n_active"] == n_active
     del runner
     if not args.no_training and args.xf == "none":
         log("[bench] training-state leg (entropy, lse, dlogits)")

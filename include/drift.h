@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define DRIFT_ABI_VERSION 5
+#define DRIFT_ABI_VERSION 6
 
 /* ---- status codes ---------------------------------------------------------------- */
 #define DRIFT_OK          0
@@ -107,6 +107,7 @@ typedef struct drift_lse_partial {
 #define DRIFT_OP_SELECTED_LOGPROB 0
 #define DRIFT_OP_DIAGNOSTICS      1
 #define DRIFT_OP_LMHEAD           2
+#define DRIFT_OP_ACTIVE_ROWS      3
 
 /*
  * Arguments of drift_selected_logprob. Logical inputs follow "Measurement Contract"
@@ -315,6 +316,22 @@ int drift_segment_diagnostics(const float* dlogp, const uint8_t* active, int64_t
                               const int32_t* seg_offsets, int64_t num_segments,
                               double eps_low, double eps_high, const void* logprob_ws,
                               drift_stats* out_dev, void* stream);
+
+/* The active rows as an ascending list ("Measurement Contract": only active
+ * response/action tokens are compared), for callers that gather or scatter per-token
+ * results of the active rows.
+ *   active      uint8 [N] device, nonzero = active (e.g. the `active` output of
+ *               drift_selected_logprob)
+ *   rows        int32 [N] device, caller-owned: rows[0 .. n) receives the indices r with
+ *               active[r] != 0 in ascending order; entries from n on are not written
+ *   n_dev       int64 [1] device: receives n
+ *   ws          drift_workspace_size(DRIFT_OP_ACTIVE_ROWS, N, 1, 0, DRIFT_F32) bytes
+ *               (per-tile counts), 256-byte aligned
+ * Integer work only: the result is exact and independent of scheduling. Asynchronous;
+ * returns EINVAL / EWORKSPACE for bad arguments before any launch, EHIP if a launch
+ * fails. */
+int drift_active_rows(const uint8_t* active, int64_t num_rows, int32_t* rows, int64_t* n_dev,
+                      void* ws, size_t ws_bytes, void* stream);
 
 /* Fused LM-head selected logprob: logits z = hidden x W are formed tile by tile on the
  * matrix cores and never written to memory; logp[t] = z[t, y_t] - LSE(z[t]).

@@ -6,7 +6,8 @@ the benchmark use it. It shares no code, tables or helpers with the HIP library.
 
 It is a plain, slow, textbook implementation in float64 numpy / Python:
 
-* ``logprob``     - active-row rule, logical-input validation, two-pass log-sum-exp,
+* ``logprob``     - active-row rule and the ascending active-row list, logical-input
+                    validation, two-pass log-sum-exp,
                     selected-logit gather and dlogp (page "WS2 Cross-Config Logprob Drift
                     Contract", section "Measurement Contract"; page "[WS2] Framework for
                     ablation experiment", LogProb knobs rows 2, 6, 8), the vocab-padding
@@ -26,7 +27,8 @@ Each function is pinned by tests against closed forms, brute force at 50 decimal
 and textbook library routines; none is "parity unpinned".
 """
 from .logprob import (STATUS, widen, logsumexp_row, selected_logprob, validate_inputs,
-                      active_rows, score_row, score_rows, apply_transforms, TRANSFORMS)
+                      active_rows, active_row_list, score_row, score_rows, apply_transforms,
+                      TRANSFORMS)
 from .diagnostics import diagnostics, nearest_rank, segment_diagnostics
 from .lmhead import lmhead_logprob
 from .sharding import merge_partials, owner_of, shard_partial, sharded_score_rows
@@ -34,7 +36,7 @@ from .training import (chain_derivative, dlogits_row, dlogits_rows, entropy_row,
                        softmax_row)
 
 __all__ = ["STATUS", "widen", "logsumexp_row", "selected_logprob", "validate_inputs",
-           "active_rows", "score_row", "score_rows", "apply_transforms", "TRANSFORMS", "diagnostics", "nearest_rank", "segment_diagnostics", "lmhead_logprob",
+           "active_rows", "active_row_list", "score_row", "score_rows", "apply_transforms", "TRANSFORMS", "diagnostics", "nearest_rank", "segment_diagnostics", "lmhead_logprob",
            "shard_partial", "merge_partials", "owner_of", "sharded_score_rows",
            "entropy_row", "entropy_rows", "dlogits_row", "dlogits_rows", "chain_derivative",
            "softmax_row"]

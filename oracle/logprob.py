@@ -72,6 +72,13 @@ def active_rows(attention, action, N, layout, cu_seqlens=None) -> np.ndarray:
     return att & act
 
 
+def active_row_list(active) -> np.ndarray:
+    """The active rows as a list in ascending order (the compaction of the Measurement
+    Contract's active-token rule): every r with active[r] != 0, each once, smallest first."""
+    a = np.asarray(active)
+    return np.array([r for r in range(a.shape[0]) if a[r] != 0], dtype=np.int64)
+
+
 def validate_inputs(attention, action, ids, V, N, layout, B=0, L=0, cu_seqlens=None):
     """Logical-input checks that make a comparison invalid rather than noisy.
 

@@ -22,7 +22,8 @@ def test_header_declares_the_boundary():
                             "drift_get_status", "drift_diagnostics", "drift_lmhead_logprob",
                             "drift_dlogits", "drift_segment_diagnostics",
                             "drift_shard_partials", "drift_merge_shards",
-                            "drift_backend_descriptor", "drift_strerror"])
+                            "drift_active_rows", "drift_backend_descriptor",
+                            "drift_strerror"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -49,7 +50,7 @@ def test_struct_layouts_match_header():
 def test_descriptor_and_strerror():
     from train_rollout_logprob_amd import binding as B
     d = B.drift_backend_descriptor()
-    assert d["abi_version"] == 5 and d["archs"] == "gfx950"
+    assert d["abi_version"] == 6 and d["archs"] == "gfx950"
     assert "batch composition" in d["determinism"]
     assert d["lse_domain"] == "natural log"
     assert d["build_fingerprint"].startswith("src:")
@@ -236,3 +237,18 @@ def test_build_fingerprint_covers_every_source():
     from train_rollout_logprob_amd import build as Bd
     on_disk = {f for f in os.listdir(Bd.CSRC) if f.endswith((".hip", ".h"))}
     assert on_disk - {Bd.CEILING_SOURCE} == set(Bd.SOURCES) | set(Bd.HEADERS)
+
+
+def test_active_rows_host_checks():
+    from train_rollout_logprob_amd import binding as B
+    ok = ctypes.c_void_p(1 << 20)  # aligned stand-ins; no call below reaches a launch
+    ws = 1 << 16
+    need = B.drift_workspace_size(B.DRIFT_OP_ACTIVE_ROWS, 5000, 1, 0, B.DRIFT_F32)
+    assert need == 256  # one int32 count per tile of 4096 rows, rounded up to 256 bytes
+    f = B.lib.drift_active_rows
+    assert f(ok, -1, ok, ok, ws, need, None) == B.DRIFT_EINVAL
+    assert f(ok, 5000, ok, None, ws, need, None) == B.DRIFT_EINVAL          # no n
+    assert f(None, 5000, ok, ok, ws, need, None) == B.DRIFT_EINVAL          # no mask
+    assert f(ok, 5000, ctypes.c_void_p((1 << 20) + 2), ok, ws, need, None) == B.DRIFT_EINVAL
+    assert f(ok, 5000, ok, ok, ws, need - 1, None) == B.DRIFT_EWORKSPACE
+    assert f(ok, 5000, ok, ok, ws + 8, need, None) == B.DRIFT_EWORKSPACE

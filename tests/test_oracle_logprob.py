@@ -305,3 +305,20 @@ def test_per_side_transforms_make_drift():
     lp = lambda aa, bb: aa - math.log(math.exp(aa) + (V - 1) * math.exp(bb))
     want = lp(a, b) - lp(a / 2, b / 2)
     assert abs(out["dlogp"][0] - want) <= 1e-14
+
+
+def test_active_row_list_worked_example_and_properties():
+    """The ascending active-row list: a hand-worked example, the edge cases, and the
+    properties that define it (sorted, each active row once, nothing else)."""
+    assert oracle.active_row_list([0, 1, 1, 0, 1]).tolist() == [1, 2, 4]
+    assert oracle.active_row_list([]).tolist() == []
+    assert oracle.active_row_list([0, 0, 0]).tolist() == []
+    assert oracle.active_row_list([1, 1, 1]).tolist() == [0, 1, 2]
+    assert oracle.active_row_list(np.array([0, 2, 0, 255], np.uint8)).tolist() == [1, 3]
+    rng = np.random.default_rng(5)
+    a = (rng.random(5003) < 0.3).astype(np.uint8)
+    got = oracle.active_row_list(a)
+    assert np.all(np.diff(got) > 0)
+    assert len(got) == int(a.sum())
+    assert np.all(a[got] == 1)
+    assert np.array_equal(got, np.flatnonzero(a))

@@ -31,7 +31,7 @@ STATUS_NAMES = {DRIFT_OK: "OK", DRIFT_EINVAL: "EINVAL", DRIFT_EDTYPE: "EDTYPE",
 DRIFT_F32, DRIFT_BF16, DRIFT_I32, DRIFT_I64 = 0, 1, 2, 3
 DRIFT_PAD_RIGHT, DRIFT_PAD_LEFT, DRIFT_PACKED = 0, 1, 2
 LAYOUTS = {"right": DRIFT_PAD_RIGHT, "left": DRIFT_PAD_LEFT, "packed": DRIFT_PACKED}
-DRIFT_OP_SELECTED_LOGPROB, DRIFT_OP_DIAGNOSTICS, DRIFT_OP_LMHEAD = 0, 1, 2
+DRIFT_OP_SELECTED_LOGPROB, DRIFT_OP_DIAGNOSTICS, DRIFT_OP_LMHEAD, DRIFT_OP_ACTIVE_ROWS = 0, 1, 2, 3
 DRIFT_XF_SCALE, DRIFT_XF_TEMPERATURE, DRIFT_XF_SOFTCAP = 1, 2, 3
 DRIFT_MAX_TRANSFORMS = 4
 DRIFT_REDUCE_TREE, DRIFT_REDUCE_EXACT = 0, 1
@@ -44,7 +44,7 @@ XF_CODES = {"scale": DRIFT_XF_SCALE, "temperature": DRIFT_XF_TEMPERATURE,
 EXPORTS = ("drift_workspace_size", "drift_selected_logprob", "drift_get_status",
            "drift_diagnostics", "drift_segment_diagnostics", "drift_lmhead_logprob",
            "drift_dlogits", "drift_shard_partials", "drift_merge_shards",
-           "drift_backend_descriptor", "drift_strerror")
+           "drift_active_rows", "drift_backend_descriptor", "drift_strerror")
 
 
 class drift_transform(ctypes.Structure):
@@ -111,6 +111,8 @@ def _load():
     lib.drift_segment_diagnostics.argtypes = [vp, vp, i64, vp, i64, ctypes.c_double,
                                               ctypes.c_double, vp, vp, vp]
     lib.drift_segment_diagnostics.restype = ctypes.c_int
+    lib.drift_active_rows.argtypes = [vp, i64, vp, vp, vp, sz, vp]
+    lib.drift_active_rows.restype = ctypes.c_int
     lib.drift_lmhead_logprob.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]
     lib.drift_lmhead_logprob.restype = ctypes.c_int
     lib.drift_dlogits.argtypes = [ctypes.POINTER(drift_logprob_args), ctypes.c_int, vp, vp, vp,
@@ -167,6 +169,12 @@ def drift_segment_diagnostics(dlogp, active, num_rows: int, seg_offsets, num_seg
                                              _ptr(seg_offsets), num_segments, eps_low,
                                              eps_high, _ptr(logprob_ws), _ptr(out_dev),
                                              _stream(stream)))
+
+
+def drift_active_rows(active, num_rows: int, rows, n_dev, ws, ws_bytes: int,
+                      stream=None) -> int:
+    return int(lib.drift_active_rows(_ptr(active), num_rows, _ptr(rows), _ptr(n_dev), _ptr(ws),
+                                     ws_bytes, _stream(stream)))
 
 
 def drift_lmhead_logprob(hidden, weight, T: int, H: int, V: int, target_ids, active, logp, ws,
@@ -425,6 +433,26 @@ def dlogits(train, rollout, ids, side, lse, active, grad_logp=None, out_dtype=to
     if st != DRIFT_OK:
         raise DriftError(st, "drift_dlogits")
     return out
+
+
+def active_rows(active, rows=None, n=None, ws=None, stream=None):
+    """Call drift_active_rows on a uint8 device tensor [N]. Returns (rows, n, ws): rows is an
+    int32 tensor [N] whose first n entries are the active row indices in ascending order,
+    n an int64 device tensor [1] (read it with .item(), which synchronizes)."""
+    N = active.shape[0]
+    dev = active.device
+    if active.dtype != torch.uint8 or active.dim() != 1:
+        raise ValueError("active must be a uint8 vector")
+    if ws is None:
+        ws = workspace(DRIFT_OP_ACTIVE_ROWS, N, 1, DRIFT_F32, dev)
+    if rows is None:
+        rows = torch.empty(max(N, 1), dtype=torch.int32, device=dev)
+    if n is None:
+        n = torch.empty(1, dtype=torch.int64, device=dev)
+    st = drift_active_rows(active, N, rows, n, ws, ws.numel(), stream)
+    if st != DRIFT_OK:
+        raise DriftError(st, "drift_active_rows")
+    return rows, n, ws
 
 
 def segment_diagnostics(dlogp, active, seg_offsets, eps_low=0.2, eps_high=0.2, logprob_ws=None,

@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdrift.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ["api.hip", "logprob.hip", "diagnostics.hip", "lmhead.hip", "dlogits.hip"]
+SOURCES = ["api.hip", "logprob.hip", "diagnostics.hip", "lmhead.hip", "dlogits.hip",
+           "compact.hip"]
 HEADERS = ["common.h", "classify.h", "exact.h", "lse.h", "rowio.h"]
 CEILING_LIB = os.path.join(PKG, "libdrift_ceiling.so")
 CEILING_SOURCE = "ceiling.hip"

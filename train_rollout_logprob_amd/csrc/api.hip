@@ -70,6 +70,8 @@ size_t drift_workspace_size(int op, int64_t num_rows, int64_t vocab, int64_t hid
     case DRIFT_OP_LMHEAD:
       if (dtype != DRIFT_BF16 || hidden_dim < 1 || hidden_dim % 8 || vocab % 8) return 0;
       return lmhead_ws_bytes(num_rows, hidden_dim, vocab);
+    case DRIFT_OP_ACTIVE_ROWS:
+      return compact_ws_bytes(num_rows);
     default:
       return 0;
   }
@@ -304,6 +306,18 @@ int drift_segment_diagnostics(const float* dlogp, const uint8_t* active, int64_t
   return DRIFT_OK;
 }
 
+int drift_active_rows(const uint8_t* active, int64_t num_rows, int32_t* rows, int64_t* n_dev,
+                      void* ws, size_t ws_bytes, void* stream) {
+  if (num_rows < 0 || num_rows > INT32_MAX) return DRIFT_EINVAL;
+  if (!n_dev || !aligned(n_dev, 8)) return DRIFT_EINVAL;
+  if (num_rows > 0 && (!active || !rows || !aligned(rows, 4))) return DRIFT_EINVAL;
+  if (!ws || !aligned(ws, 256) || ws_bytes < compact_ws_bytes(num_rows)) return DRIFT_EWORKSPACE;
+  return launch_compact(active, num_rows, rows, n_dev, (char*)ws, (hipStream_t)stream) ==
+                 hipSuccess
+             ? DRIFT_OK
+             : DRIFT_EHIP;
+}
+
 int drift_lmhead_logprob(const void* hidden, const void* weight, int64_t T, int64_t H, int64_t V,
                          const int32_t* target_ids, const uint8_t* active, float* logp,
                          void* ws, size_t ws_bytes, void* stream) {
@@ -375,7 +389,7 @@ const drift_backend_desc* drift_backend_descriptor(void) {
   static const drift_backend_desc d = {
       DRIFT_ABI_VERSION,
       "drift.gfx950.v1",
-      "selected_token_logprob,dlogp,entropy,lse,exact_reduction,vocab_shard_partials,shard_merge,drift_diagnostics,segment_diagnostics,mismatch_kl,lmhead_selected_logprob,dlogits",
+      "selected_token_logprob,dlogp,entropy,lse,exact_reduction,vocab_shard_partials,shard_merge,drift_diagnostics,segment_diagnostics,mismatch_kl,active_rows,lmhead_selected_logprob,dlogits",
       "gfx950",
       "logits:f32,bf16;ids:i32,i64;lmhead:bf16",
       "pad_right,pad_left,packed(cu_seqlens);logits row-major [N,row_stride]",

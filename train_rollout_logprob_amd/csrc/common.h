@@ -130,4 +130,9 @@ struct DlogitsParams {
 };
 hipError_t launch_dlogits(const DlogitsParams& p, hipStream_t s);
 
+int64_t compact_tiles(int64_t N);
+size_t compact_ws_bytes(int64_t N);
+hipError_t launch_compact(const uint8_t* active, int64_t N, int32_t* rows, int64_t* n_out,
+                          char* ws, hipStream_t s);
+
 }  // namespace drift
