@@ -97,6 +97,9 @@ def test_host_checks_fail_closed_without_launching():
     a.layout, a.num_rows, a.batch, a.seq_len = B.DRIFT_PAD_LEFT, 6, 2, 4  # B*L != N
     assert lib.drift_selected_logprob(ctypes.byref(a), None, None, None, None, None, 0,
                                       None) == B.DRIFT_EINVAL
+    a.num_rows, a.batch, a.seq_len = 0, 1 << 32, 1 << 32       # B*L wraps to 0 in 64 bits
+    assert lib.drift_selected_logprob(ctypes.byref(a), None, None, None, None, None, 0,
+                                      None) == B.DRIFT_EINVAL
     st = B.drift_stats()
     assert lib.drift_diagnostics(None, None, 5, 0.2, 0.2, None, ctypes.byref(st), None, 0,
                                  None) == B.DRIFT_EINVAL

@@ -108,7 +108,9 @@ int prepare(const drift_logprob_args* a, bool logits, int64_t vocab_ids, ScorePa
   switch (a->layout) {
     case DRIFT_PAD_RIGHT:
     case DRIFT_PAD_LEFT:
-      if (a->batch < 0 || a->seq_len < 1 || a->batch * a->seq_len != N) return DRIFT_EINVAL;
+      if (a->batch < 0 || a->seq_len < 1 || a->batch > INT32_MAX || a->seq_len > INT32_MAX ||
+          a->batch * a->seq_len != N)  // both below 2^31: the product cannot overflow
+        return DRIFT_EINVAL;
       break;
     case DRIFT_PACKED:
       if (!a->cu_seqlens || a->num_seqs < 0 || a->num_seqs > INT32_MAX - 1 ||
