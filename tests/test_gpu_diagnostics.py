@@ -125,3 +125,20 @@ def test_pipeline_gate_a_and_gate_b(key):
         assert abs(s[k] - want_b[k]) <= 1e-5 * abs(want_b[k]), k
     for k in ("p95_abs_dlogp", "p99_abs_dlogp", "max_abs_dlogp"):
         assert abs(s[k] - want_b[k]) <= 2e-5, k
+
+
+@pytest.mark.parametrize("n", [4099, 100003])
+def test_unaligned_views_take_the_scalar_loads(n):
+    """dlogp and active as views one element in (4-byte but not 16-byte aligned): the
+    select reads the rows one by one instead of four at a time; same statistics."""
+    from train_rollout_logprob_amd import binding as B
+    rng = np.random.default_rng(n + 1)
+    d = (rng.standard_normal(n + 1) * 5e-3).astype(np.float32)
+    act = (rng.random(n + 1) < 0.7).astype(np.uint8)
+    dd = torch.as_tensor(d, device="cuda")[1:]
+    aa = torch.as_tensor(act, device="cuda")[1:]
+    assert dd.data_ptr() % 16 != 0 and aa.data_ptr() % 4 != 0
+    st, got = B.diagnostics(dd, aa, 0.2, 0.2)
+    want = oracle.diagnostics(d[1:], act[1:], 0.2, 0.2)
+    assert status_name(st) == want["status"] == "OK"
+    assert_stats_exact(got, want)

@@ -65,6 +65,7 @@ struct DiagLayout {
 };
 
 __device__ __forceinline__ unsigned int key_of(float d) { return __float_as_uint(fabsf(d)); }
+constexpr unsigned int kNoKey = 0xffffffffu;  // no row (keys have bit 31 clear)
 
 template <typename V>
 __device__ __forceinline__ V wave_sum(V v) {
@@ -262,23 +263,56 @@ __global__ void __launch_bounds__(kDiagThreads) diag_tile(DiagParams p) {
   }
 }
 
-constexpr unsigned int kNoKey = 0xffffffffu;  // no row (keys have bit 31 clear)
 constexpr int kSelBatch = 8;                  // rows per thread per batch of loads
+
+// Keys of rows r0 .. r0 + 3 (kNoKey for inactive rows and rows past hi): one 16-byte load
+// of d and one 4-byte load of the mask when all four rows exist; d and active must then be
+// 16- and 4-byte aligned at r0.
+__device__ __forceinline__ void keys4(const float* d, const uint8_t* active, int64_t r0,
+                                      int64_t hi, unsigned int (&k)[4]) {
+  if (r0 + 3 < hi) {
+    const float4 v = *(const float4*)(d + r0);
+    const uint32_t a = *(const uint32_t*)(active + r0);
+    k[0] = (a & 0xffu) ? key_of(v.x) : kNoKey;
+    k[1] = (a & 0xff00u) ? key_of(v.y) : kNoKey;
+    k[2] = (a & 0xff0000u) ? key_of(v.z) : kNoKey;
+    k[3] = (a & 0xff000000u) ? key_of(v.w) : kNoKey;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t r = r0 + e;
+      k[e] = (r < hi && active[r]) ? key_of(d[r]) : kNoKey;
+    }
+  }
+}
 
 // Block-cooperative (NT threads) three-digit radix select: the nearest-rank keys of both
 // quantiles among the active rows [lo, hi), given their 1-based ranks in s_rank (updated in
 // place); the keys end in s_prefix (zero on entry). Rows lo + tid + k NT, k < KC, are read
 // once into registers; rows past lo + KC NT are re-read for every digit in batches of
-// kSelBatch per thread (all loads of a batch issued before any count). Digit h of a
+// kSelBatch per thread (all loads of a batch issued before any count). When the rows start
+// 16-byte aligned (lo = 0 and aligned arrays; the whole-batch call), thread t instead takes
+// groups of four consecutive rows with one vector load each (the same rows in total), so a
+// pass issues a quarter of the load instructions. Digit h of a
 // quantile counts, in LDS, the keys whose upper digits match the ones chosen so far; the
 // first digit's histogram is shared by both quantiles.
 template <int NT, int KC>
 __device__ void radix_select(const float* d, const uint8_t* active, int64_t lo, int64_t hi,
                              unsigned int (*s_hist)[kBins], long long* s_rank,
                              unsigned int* s_prefix) {
+  static_assert(KC % 4 == 0, "the vector path caches groups of four rows");
   const int tid = threadIdx.x;
+  const bool vec = lo == 0 && ((uintptr_t)d & 15) == 0 && ((uintptr_t)active & 3) == 0;
   unsigned int ck[KC];
-  {
+  if (vec) {  // block-uniform
+#pragma unroll
+    for (int k = 0; k < KC / 4; ++k) {
+      unsigned int k4[4];
+      keys4(d, active, 4 * ((int64_t)k * NT + tid), hi, k4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ck[4 * k + e] = k4[e];
+    }
+  } else {
     uint8_t a[KC];
     float x[KC];
 #pragma unroll
@@ -309,7 +343,18 @@ __device__ void radix_select(const float* d, const uint8_t* active, int64_t lo, 
     };
 #pragma unroll
     for (int k = 0; k < KC; ++k) count(ck[k]);
-    for (int64_t base = rest; base < hi; base += (int64_t)NT * kSelBatch) {
+    if (vec) {
+      for (int64_t base = rest; base < hi; base += (int64_t)NT * kSelBatch) {
+        unsigned int kk[kSelBatch / 4][4];
+#pragma unroll
+        for (int u = 0; u < kSelBatch / 4; ++u)
+          keys4(d, active, base + 4 * ((int64_t)u * NT + tid), hi, kk[u]);
+#pragma unroll
+        for (int u = 0; u < kSelBatch / 4; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) count(kk[u][e]);
+      }
+    } else for (int64_t base = rest; base < hi; base += (int64_t)NT * kSelBatch) {
       uint8_t a[kSelBatch];
       float x[kSelBatch];
 #pragma unroll
