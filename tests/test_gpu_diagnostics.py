@@ -36,7 +36,7 @@ def _check(d, act, eps_lo=0.2, eps_hi=0.2):
     return got, want
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 100, 4095, 4096, 4097, 12288, 100003])
+@pytest.mark.parametrize("n", [1, 2, 3, 100, 4095, 4096, 4097, 12288, 65536, 65537, 100003, 300001])
 def test_random_arrays(n):
     rng = np.random.default_rng(n)
     d = (rng.standard_normal(n) * 5e-3).astype(np.float32)
@@ -142,3 +142,19 @@ def test_unaligned_views_take_the_scalar_loads(n):
     want = oracle.diagnostics(d[1:], act[1:], 0.2, 0.2)
     assert status_name(st) == want["status"] == "OK"
     assert_stats_exact(got, want)
+
+
+def test_statuses_and_ties_above_the_single_block_size():
+    """Batches above 65536 rows take one launch per digit: no active row, a non-finite
+    dlogp, and all-equal magnitudes behave as in the single-block selection."""
+    n = 70001
+    st, s = _gpu_stats(np.zeros(n, np.float32), np.zeros(n, np.uint8))
+    assert st == "ENOACTIVE" and s["n_active"] == 0 and math.isnan(s["p99_abs_dlogp"])
+    d = np.full(n, -2.5e-4, np.float32)
+    d[::3] = 2.5e-4
+    got, want = _check(d, np.ones(n, np.uint8))
+    assert got["p95_abs_dlogp"] == got["max_abs_dlogp"] == np.float32(2.5e-4)
+    assert got["argmax_row"] == 0
+    d[777] = np.inf
+    st, s = _gpu_stats(d, np.ones(n, np.uint8))
+    assert st == "ENONFINITE" and s["n_nonfinite"] == 1

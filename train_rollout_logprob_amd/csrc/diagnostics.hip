@@ -52,14 +52,23 @@ struct SelState {
 };
 static_assert(sizeof(SelState) <= 512, "state size");
 
+// Batches above this many rows select the order statistics with one multi-block launch per
+// digit (integer histograms in the workspace) instead of re-reading every row three times
+// in one block.
+constexpr int64_t kSelSingleMax = 65536;
+constexpr int kPassThreads = 256;
+constexpr int kPassRowsPerBlock = 8192;
+
 struct DiagLayout {
-  size_t partial_off, total;
+  size_t partial_off, hist_off, total;
   int G;
   __host__ __device__ static DiagLayout make(int64_t N) {
     DiagLayout l;
     l.G = (int)((N + kDiagTile - 1) / kDiagTile);
     l.partial_off = 512;
-    l.total = l.partial_off + align_up((size_t)(l.G > 0 ? l.G : 1) * sizeof(TilePartial), 256);
+    l.hist_off = l.partial_off + align_up((size_t)(l.G > 0 ? l.G : 1) * sizeof(TilePartial), 256);
+    // digit histograms: [3 digits][2 quantiles][kBins] u32 (the first digit uses quantile 0)
+    l.total = l.hist_off + (N > kSelSingleMax ? align_up(3 * kNumQ * kBins * 4, 256) : 0);
     return l;
   }
 };
@@ -247,6 +256,10 @@ __global__ void __launch_bounds__(kDiagThreads) diag_tile(DiagParams p) {
     if (r >= p.N || !p.active[r]) continue;
     add_row(acc, p.d[r], r, lo_edge, hi_edge);
   }
+  if (p.N > kSelSingleMax && blockIdx.x == 0) {  // read by the digit launches that follow
+    unsigned int* h = (unsigned int*)(p.ws + lay.hist_off);
+    for (int i = tid; i < 3 * kNumQ * kBins; i += kDiagThreads) h[i] = 0;
+  }
   const RowStats t = block_reduce(acc);
   if (tid == 0) {
     TilePartial o = {};
@@ -406,10 +419,98 @@ __global__ void __launch_bounds__(kSelThreads) diag_select(DiagParams p) {
   }
   __syncthreads();
   if (s_n == 0) return;  // block-uniform
-  radix_select<kSelThreads, 16>(p.d, p.active, 0, p.N, s_hist, s_rank, s_prefix);
+  if (p.N > kSelSingleMax) {
+    const unsigned int* gh = (const unsigned int*)(p.ws + lay.hist_off);
+    for (int pass = 0; pass < 3; ++pass) {
+      for (int b = tid; b < kNumQ * kBins; b += kSelThreads)
+        (&s_hist[0][0])[b] = gh[(pass * kNumQ) * kBins + b];
+      __syncthreads();
+      pick_digits(s_hist[0], s_hist[pass == 0 ? 0 : 1], kShift[pass], s_rank, s_prefix);
+      __syncthreads();
+    }
+  } else {
+    radix_select<kSelThreads, 16>(p.d, p.active, 0, p.N, s_hist, s_rank, s_prefix);
+  }
   if (tid == 0) {
     st->stats.p95_abs_dlogp = __uint_as_float(s_prefix[0]);
     st->stats.p99_abs_dlogp = __uint_as_float(s_prefix[1]);
+  }
+}
+
+// One digit of the multi-block selection (batches above kSelSingleMax rows). Every block
+// first rebuilds the digits chosen so far from the histograms of the earlier launches (the
+// active count is the first histogram's total, so the ranks follow as in diag_select),
+// then counts the keys of its rows whose upper digits match into LDS histograms and adds
+// its non-zero bins to the launch's global histogram. All counts are integers: the result
+// does not depend on how rows or blocks are scheduled.
+template <int PASS>
+__global__ void __launch_bounds__(kPassThreads) diag_pass(DiagParams p) {
+  __shared__ unsigned int s_hist[kNumQ][kBins];
+  __shared__ long long s_rank[kNumQ];
+  __shared__ unsigned int s_prefix[kNumQ];
+  __shared__ unsigned int s_w[kPassThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const DiagLayout lay = DiagLayout::make(p.N);
+  unsigned int* gh = (unsigned int*)(p.ws + lay.hist_off);
+  if (tid < kNumQ) s_prefix[tid] = 0;
+  if (PASS > 0) {
+    for (int b = tid; b < kBins; b += kPassThreads) s_hist[0][b] = gh[b];
+    __syncthreads();
+    unsigned int c = 0;
+    for (int b = tid; b < kBins; b += kPassThreads) c += s_hist[0][b];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) c += (unsigned int)__shfl_xor((int)c, o);
+    if (lane == 0) s_w[wave] = c;
+    __syncthreads();
+    if (tid < kNumQ) {
+      long long n = 0;
+      for (int w = 0; w < kPassThreads / 64; ++w) n += s_w[w];
+      s_rank[tid] = quantile_rank(tid, n);
+    }
+    __syncthreads();
+    for (int pass = 0; pass < PASS; ++pass) {
+      if (pass > 0) {
+        for (int b = tid; b < kNumQ * kBins; b += kPassThreads)
+          (&s_hist[0][0])[b] = gh[(pass * kNumQ) * kBins + b];
+        __syncthreads();
+      }
+      pick_digits(s_hist[0], s_hist[pass == 0 ? 0 : 1], kShift[pass], s_rank, s_prefix);
+      __syncthreads();
+    }
+  }
+  for (int b = tid; b < kNumQ * kBins; b += kPassThreads) (&s_hist[0][0])[b] = 0;
+  __syncthreads();
+  constexpr int shift = kShift[PASS];
+  constexpr unsigned int mask = (1u << kBitsOf[PASS]) - 1u;
+  constexpr int hi_shift = PASS > 0 ? kShift[PASS > 0 ? PASS - 1 : 0] : 31;
+  const unsigned int pre0 = s_prefix[0] >> hi_shift, pre1 = s_prefix[1] >> hi_shift;
+  auto count = [&](unsigned int key) {
+    if (key == kNoKey) return;
+    if (PASS == 0) {
+      atomicAdd(&s_hist[0][key >> shift], 1u);
+    } else {
+      if ((key >> hi_shift) == pre0) atomicAdd(&s_hist[0][(key >> shift) & mask], 1u);
+      if ((key >> hi_shift) == pre1) atomicAdd(&s_hist[1][(key >> shift) & mask], 1u);
+    }
+  };
+  const int64_t lo = (int64_t)blockIdx.x * kPassRowsPerBlock;
+  const int64_t hi = lo + kPassRowsPerBlock < p.N ? lo + kPassRowsPerBlock : p.N;
+  const bool vec = ((uintptr_t)p.d & 15) == 0 && ((uintptr_t)p.active & 3) == 0;
+  if (vec) {  // block-uniform; lo is a multiple of 4
+    for (int64_t r0 = lo + 4 * (int64_t)tid; r0 < hi; r0 += 4 * kPassThreads) {
+      unsigned int k4[4];
+      keys4(p.d, p.active, r0, hi, k4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) count(k4[e]);
+    }
+  } else {
+    for (int64_t r = lo + tid; r < hi; r += kPassThreads)
+      count(p.active[r] ? key_of(p.d[r]) : kNoKey);
+  }
+  __syncthreads();
+  for (int b = tid; b < kNumQ * kBins; b += kPassThreads) {
+    const unsigned int c = (&s_hist[0][0])[b];
+    if (c) atomicAdd(&gh[(PASS * kNumQ) * kBins + b], c);
   }
 }
 
@@ -478,6 +579,12 @@ hipError_t launch_diagnostics(const DiagParams& p, hipStream_t s) {
   const DiagLayout lay = DiagLayout::make(p.N);
   const int G = lay.G > 0 ? lay.G : 1;  // one (empty) tile when N = 0
   hipLaunchKernelGGL(diag_tile, dim3(G), dim3(kDiagThreads), 0, s, p);
+  if (p.N > kSelSingleMax) {
+    const unsigned nb = (unsigned)((p.N + kPassRowsPerBlock - 1) / kPassRowsPerBlock);
+    hipLaunchKernelGGL(diag_pass<0>, dim3(nb), dim3(kPassThreads), 0, s, p);
+    hipLaunchKernelGGL(diag_pass<1>, dim3(nb), dim3(kPassThreads), 0, s, p);
+    hipLaunchKernelGGL(diag_pass<2>, dim3(nb), dim3(kPassThreads), 0, s, p);
+  }
   hipLaunchKernelGGL(diag_select, dim3(1), dim3(kSelThreads), 0, s, p);
   return hipGetLastError();
 }
