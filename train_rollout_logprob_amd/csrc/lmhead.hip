@@ -363,7 +363,7 @@ __global__ void __launch_bounds__(kPThreads, 1) lm_gemm_lse(GemmArgs a) {
   // then this wave's fills of stage kt + 1 are awaited and the block barrier makes every
   // fill visible and every read of this stage's buffers done; step 3 reads the first
   // fragments of stage kt + 1. A stage's fills go out in two halves of 8 instructions per
-  // wave, each interleaved one per MFMA with a step: the W half of stage kt + 2 in step 3
+  // wave, each interleaved one per MFMA pair with a step: the W half of stage kt + 2 in step 3
   // of stage kt (into this stage's buffer, free after the barrier), the hidden half of
   // stage kt + 1 in step 0 of stage kt (into the other buffer, free since the barrier of
   // stage kt - 1). Issuing all 16 in one step queued them behind the 4 waves' address
@@ -380,12 +380,9 @@ __global__ void __launch_bounds__(kPThreads, 1) lm_gemm_lse(GemmArgs a) {
     fill(rB, nB, k1);
     mfmas(0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 8; ++i) {  // per MFMA pair: one fragment read, one fill
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
