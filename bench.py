@@ -1,20 +1,24 @@
 """Throughput of the paired selected-token logprob + drift path on one MI355X.
 
-One step = drift_selected_logprob (classification, compaction, paired one-pass log-softmax
-gather) + drift_diagnostics (sums, counts, exact nearest-rank select, one host sync) over
-one batch of the Qwen3-8B-shaped scoring workload: bf16 logits, V=151936, B=8, L=2048,
-left padding, 12288 active rows, inputs resident in HBM before timing starts.
+One step = drift_selected_logprob (classification, paired one-pass log-softmax gather of
+both sides, drift) + drift_diagnostics (sums, counts, exact nearest-rank select, one host
+sync) over one batch, inputs resident in HBM before timing starts.
 
-Prints ONE JSON line (rank 0). `roofline` is for the dominant kernel (the paired scoring
-kernel): algorithmic bytes = active rows x V x 2 bytes x 2 sides, divided by its average
-duration measured with HIP events recorded by the library around that kernel on the launch
-stream. `cpu_baseline` is the fp64 CPU oracle timed on a bounded sample of the same rows.
+The main line is the large-batch workload, the largest that fits one GPU: bf16 logits,
+V=151936, B=32, L=4096 (prompt 1024 + response U[1024,3072]), right padding, about 40 GB
+of logits per side. `roofline` is for its dominant kernel, the paired scoring kernel:
+algorithmic bytes = active rows x V x 2 bytes x 2 sides, divided by the kernel's duration
+measured with HIP events the library records around it on the launch stream (average,
+median and min over the timed steps). `cpu_baseline` is the fp64 CPU oracle timed on a
+pool of host worker processes over a bounded sample of the same batch's active rows.
 
-Further legs are reported beside the main line, outside its timed region: `segments`
-(per-sequence diagnostics), `training` (the scoring kernel with per-row entropy and LSE
-written, and the dlogits kernel on the same batch), `exact` (the order-independent
-reduction, unsharded and as vocabulary shards merged in shard order) and `lmhead` (the
-fused LM-head selected logprob).
+`configs` carries the same measurement for the other scoring workloads, each generated
+after the previous one is freed: the Qwen3-8B-shaped batch (bf16, B=8, L=2048, left
+padding), the packed varlen batch (fp32, V=32000, 256 sequences by cu_seqlens) and the
+tiny correctness batch (fp32, V=1024). Further legs are measured outside the timed region:
+`segments` and `active_rows` on the main batch; `training` (entropy + LSE from the scoring
+pass, dlogits) and `exact` (order-independent reduction, unsharded and as vocabulary
+shards) on the Qwen3-8B-shaped batch; `lmhead`, the fused LM-head selected logprob.
 """
 import argparse
 import ctypes
@@ -38,10 +42,16 @@ WORKLOAD_TEXT = {
               "U[64,2048] via cu_seqlens, Student-t(2) drift",
     "tiny": "tiny paired scoring: fp32 logits, V=1024, B=2, L=64, right padding",
 }
+# the other scoring workloads measured beside the main one, in this order
+OTHER_CONFIGS = {"large": ("qwen8b", "packed", "tiny"), "qwen8b": ("large", "packed", "tiny"),
+                 "packed": ("large", "qwen8b", "tiny"), "tiny": ("large", "qwen8b", "packed")}
 
 
 SCORE_SOURCES = ("logprob.hip", "classify.h", "lse.h", "rowio.h", "common.h:score")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "score_rows_bf16_qwen8b.md")
+SCORE_PROFILES = {"qwen8b": TRAFFIC_PROFILE,
+                  "large": os.path.join(ROOT, "profiles", "score_rows_bf16_large.md"),
+                  "packed": os.path.join(ROOT, "profiles", "score_rows_f32_packed.md")}
 DLOGITS_SOURCES = ("dlogits.hip", "classify.h", "rowio.h", "common.h:score",
                    "common.h:dlogits")
 DLOGITS_PROFILE = os.path.join(ROOT, "profiles", "dlogits_rows_bf16_qwen8b.md")
@@ -140,27 +150,47 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(case, budget_s):
-    """fp64 oracle on a bounded sample of the workload's active rows (single process)."""
+def cpu_sample(pool, case, max_rows=16384):
+    """Copies a bounded sample of the batch's active rows (every k-th active row, in
+    order) of both sides into the oracle pool's shared host buffer, outside any timing."""
     import numpy as np
 
-    import oracle
     from train_rollout_logprob_amd import synth
 
     att = case.attention if case.attention is not None else np.ones(case.N, np.uint8)
-    rows = np.nonzero((att != 0) & (case.action != 0))[0]
-    done, spent, chunk = 0, 0.0, 16
-    while spent < budget_s and done < len(rows):
-        sel = rows[done: done + chunk]
-        tr = synth.rows_to_host(case.train, sel)
-        ro = synth.rows_to_host(case.rollout, sel)
-        t0 = time.perf_counter()
-        oracle.score_rows(tr, ro, case.dtype, case.ids[sel])
-        spent += time.perf_counter() - t0
-        done += len(sel)
-    return {"value": done / spent, "unit": "active tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} active rows of the same batch (both sides, V={case.V}), "
-                      f"numpy fp64 two-pass log-sum-exp, one process, {spent:.1f} s"}
+    live = (att != 0) & (case.action != 0)
+    if case.cu_seqlens is not None:
+        live &= np.arange(case.N) < int(case.cu_seqlens[-1])
+    rows = np.nonzero(live)[0]
+    step = max(1, -(-len(rows) // max_rows))
+    sel = rows[::step][:max_rows]
+    tr, ro = pool.buffers(len(sel), case.V, case.dtype)
+    for a in range(0, len(sel), 1024):
+        part = sel[a:a + 1024]
+        tr[a:a + len(part)] = synth.rows_to_host(case.train, part)
+        ro[a:a + len(part)] = synth.rows_to_host(case.rollout, part)
+    return {"rows": len(sel), "every": step, "of": len(rows), "V": case.V,
+            "dtype": case.dtype, "ids": case.ids[sel]}
+
+
+def cpu_baseline(pool, sample, budget_s):
+    """The fp64 oracle (textbook two-pass log-sum-exp, both sides, dlogp) on a pool of host
+    worker processes over the sampled rows, repeated until `budget_s` seconds of wall time
+    are spent; rows scored per second of the pool's wall time."""
+    n, V, dt = sample["rows"], sample["V"], sample["dtype"]
+    done, spent, passes = 0, 0.0, 0
+    while spent < budget_s or passes == 0:
+        _, _, _, wall = pool.score(n, V, dt, sample["ids"])
+        spent += wall
+        done += n
+        passes += 1
+    return {"value": done / spent, "unit": "active tokens/s", "cores": pool.workers,
+            "kind": "oracle",
+            "affinity_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"{n} active rows of the main batch (every {sample['every']}th of "
+                      f"{sample['of']}, both sides, V={V}, {dt}), scored {passes} times by "
+                      f"numpy fp64 two-pass log-sum-exp in {pool.workers} worker processes; "
+                      f"{spent:.1f} s of pool wall time"}
 
 
 def lmhead_leg(steps=5, warmup=2):
@@ -391,22 +421,104 @@ def training_leg(case, ids, att, act, cu, steps=10, warmup=2):
     }
 
 
+def score_leg(name, steps, warmup, xf="none", ceiling=True):
+    """Generates one scoring workload on cuda:0 and times `steps` steps (scoring +
+    diagnostics, one host sync each) after `warmup` untimed ones. Returns the measurement
+    and what later legs reuse (the case, its device inputs and the step runner)."""
+    import torch
+
+    from train_rollout_logprob_amd import binding as B
+    from train_rollout_logprob_amd import synth
+
+    dev = "cuda:0"
+    log(f"[bench] generating the {name} workload")
+    case = synth.make_logits_case(name, device=dev)
+    ids = torch.as_tensor(case.ids, device=dev)
+    att = torch.as_tensor(case.attention, device=dev) if case.attention is not None else None
+    act = torch.as_tensor(case.action, device=dev)
+    cu = torch.as_tensor(case.cu_seqlens, device=dev) if case.cu_seqlens is not None else None
+    n_active = case.n_active()
+    chain = {"none": None, "temperature": [("temperature", 0.7)],
+             "softcap": [("softcap", 30.0)]}[xf]
+    runner = B.ScoringStep(case.train, case.rollout, ids, att, act, case.layout, case.B,
+                           case.L, cu, case.eps_low, case.eps_high, transforms=(chain, chain))
+    n_ev = warmup + steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_ev)]
+    for e0, e1 in evs:          # create the underlying events
+        e0.record()
+        e1.record()
+    torch.cuda.synchronize()
+    handles = [(e0.cuda_event, e1.cuda_event) for e0, e1 in evs]
+
+    def step(i):
+        runner.set_events(*handles[i])
+        st = runner.run()
+        if st != B.DRIFT_OK:
+            raise RuntimeError(f"{name}: status {B.STATUS_NAMES[st]}")
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] {name}: timing {steps} steps")
+    t0 = time.perf_counter()
+    for i in range(warmup, n_ev):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern = sorted(evs[i][0].elapsed_time(evs[i][1]) for i in range(warmup, n_ev))
+    kern_avg = sum(kern) / len(kern)
+    if runner.stats.n_active != n_active:
+        raise RuntimeError(f"{name}: {runner.stats.n_active} active rows, expected {n_active}")
+    alg_bytes = n_active * case.V * case.elem_bytes * 2
+    achieved = alg_bytes / (kern_avg * 1e-3) / 1e9
+    ms_per_step = elapsed * 1e3 / steps
+    out = {
+        "workload": WORKLOAD_TEXT[name], "V": case.V, "B": case.B, "L": case.L, "N": case.N,
+        "n_active": n_active, "logits_dtype": case.dtype, "transforms": xf,
+        "ms_per_step": ms_per_step, "active_tokens_per_s": n_active * steps / elapsed,
+        "logits_gbs": alg_bytes * steps / elapsed / 1e9,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": recorded_traffic(SCORE_PROFILES[name])
+                     if name in SCORE_PROFILES and xf == "none" else None,
+                     "kernel": f"score_rows<{case.dtype}>", "kernel_ms": kern_avg,
+                     "kernel_ms_median": kern[len(kern) // 2], "kernel_ms_min": kern[0],
+                     "bytes_per_launch": alg_bytes},
+        "diagnostics": {k: getattr(runner.stats, k) for k in (
+            "ratio0", "clipfrac0", "approx_kl0", "mismatch_kl", "mean_abs_dlogp",
+            "p95_abs_dlogp", "p99_abs_dlogp", "max_abs_dlogp", "argmax_row")},
+    }
+    log(f"[bench] {name}: step {ms_per_step:.3f} ms, scoring kernel {kern_avg:.3f} ms "
+        f"(median {kern[len(kern) // 2]:.3f}, min {kern[0]:.3f}; {achieved:.0f} GB/s), "
+        f"{out['active_tokens_per_s'] / 1e6:.3f} M active tok/s")
+    if ceiling:
+        ceiling_gbs, ceiling_ms = read_ceiling(case)
+        out["roofline"].update({
+            "ceiling_gbs": ceiling_gbs, "frac_of_ceiling": achieved / ceiling_gbs,
+            "ceiling_kernel": "read_rows: pure 16-byte nontemporal reads of every row pair "
+                              "of the same tensors, one block per pair"})
+        log(f"[bench] {name}: pure-read ceiling {ceiling_gbs:.0f} GB/s ({ceiling_ms:.3f} ms); "
+            f"scoring kernel at {achieved / ceiling_gbs:.3f} of it")
+    if name == "tiny":
+        out["roofline"]["note"] = ("0.65 MB per launch: launch-latency bound, a correctness "
+                                   "case, not a bandwidth figure")
+    return out, (case, ids, att, act, cu, runner)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="qwen8b",
-                    choices=["qwen8b", "large", "packed", "tiny", "lmhead"],
-                    help="scoring workload (the benchmark line is quoted on qwen8b)")
-    ap.add_argument("--no-training", action="store_true",
-                    help="skip the entropy / dlogits leg reported beside the main line")
-    ap.add_argument("--no-exact", action="store_true",
-                    help="skip the exact-reduction / vocabulary-shard leg")
-    ap.add_argument("--no-lmhead", action="store_true",
-                    help="skip the fused LM-head leg reported beside the main line")
+    ap.add_argument("--workload", default="large", choices=["qwen8b", "large", "packed", "tiny",
+                                                             "lmhead"],
+                    help="the main line's scoring workload (default: large, the largest "
+                         "single-GPU batch)")
+    ap.add_argument("--legs", default="all", choices=["all", "none"],
+                    help="none: measure the main workload only (for profiling runs)")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
                     help="copy: a plain device copy of known size, to calibrate HBM counters")
     ap.add_argument("--copy-mib", type=int, default=4096)
@@ -419,14 +531,23 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
+    # the oracle's worker pool starts before this process touches the GPU
+    pool = None
+    if args.mode == "bench" and args.workload != "lmhead" and not args.no_cpu_baseline:
+        from oracle.pool import OraclePool
+        pool = OraclePool()
+    try:
+        run(args, pool)
+    finally:
+        if pool is not None:
+            pool.close()
+
+
+def run(args, pool):
     import torch
 
-    from train_rollout_logprob_amd import binding as B
-    from train_rollout_logprob_amd import synth
-
-    dev = "cuda:0"
     torch.cuda.set_device(0)
+    dev = "cuda:0"
     if args.mode == "copy":
         n = args.copy_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -454,113 +575,65 @@ def main():
     if args.workload == "lmhead":
         print(json.dumps(lmhead_leg(args.steps, args.warmup)), flush=True)
         return
-    log(f"[bench] generating the {args.workload} workload")
-    case = synth.make_logits_case(args.workload, device=dev)
-    ids = torch.as_tensor(case.ids, device=dev)
-    att = torch.as_tensor(case.attention, device=dev) if case.attention is not None else None
-    act = torch.as_tensor(case.action, device=dev)
-    cu = torch.as_tensor(case.cu_seqlens, device=dev) if case.cu_seqlens is not None else None
-    N, V = case.N, case.V
-    esz = case.elem_bytes
-    n_active = case.n_active()
-    chain = {"none": None, "temperature": [("temperature", 0.7)],
-             "softcap": [("softcap", 30.0)]}[args.xf]
-    runner = B.ScoringStep(case.train, case.rollout, ids, att, act, case.layout, case.B,
-                           case.L, cu, case.eps_low, case.eps_high, transforms=(chain, chain))
-    n_ev = args.warmup + args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n_ev)]
-    for e0, e1 in evs:          # create the underlying events
-        e0.record()
-        e1.record()
-    torch.cuda.synchronize()
-    handles = [(e0.cuda_event, e1.cuda_event) for e0, e1 in evs]
 
-    def step(i):
-        runner.set_events(*handles[i])
-        st = runner.run()
-        if st != B.DRIFT_OK:
-            raise RuntimeError(f"status {B.STATUS_NAMES[st]}")
-
-    log("[bench] warmup")
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    log(f"[bench] timing {args.steps} steps")
-    t0 = time.perf_counter()
-    for i in range(args.warmup, n_ev):
-        step(i)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    kern_ms = [evs[i][0].elapsed_time(evs[i][1]) for i in range(args.warmup, n_ev)]
-    kern_avg = sum(kern_ms) / len(kern_ms)
-    assert runner.stats.n_active == n_active, (runner.stats.n_active, n_active)
-
-    ms_per_step = elapsed * 1e3 / args.steps
-    value = n_active * args.steps / elapsed
-    alg_bytes = n_active * V * esz * 2
-    achieved = alg_bytes / (kern_avg * 1e-3) / 1e9
-    log(f"[bench] step {ms_per_step:.3f} ms, scoring kernel {kern_avg:.3f} ms "
-        f"({achieved:.0f} GB/s), {value / 1e6:.3f} M active tok/s")
-
-    cpu = None
-    ceiling_gbs, ceiling_ms = read_ceiling(case)
-    log(f"[bench] pure-read ceiling of the same tensors: {ceiling_gbs:.0f} GB/s "
-        f"({ceiling_ms:.3f} ms); scoring kernel at {achieved / ceiling_gbs:.3f} of it")
-
+    main_leg, (case, ids, att, act, cu, runner) = score_leg(args.workload, args.steps,
+                                                            args.warmup, args.xf)
+    rf = main_leg["roofline"]
     line = {
         "metric": METRIC,
-        "value": value,
+        "value": main_leg["active_tokens_per_s"],
         "unit": "active tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": main_leg["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT[args.workload],
-                   "V": V, "B": case.B, "L": case.L, "N": N, "n_active": n_active,
-                   "logits_dtype": case.dtype, "arith": "fp32 exp2, fp64 sums",
+        "config": {"workload": main_leg["workload"], "V": case.V, "B": case.B, "L": case.L,
+                   "N": case.N, "n_active": main_leg["n_active"], "logits_dtype": case.dtype,
+                   "arith": "logits widened to fp32; fp32 exp2 terms, fp64 sums and LSE",
                    "transforms": args.xf, "parallelism": "single GPU"},
-        "logits_gbs": alg_bytes * args.steps / elapsed / 1e9,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": recorded_traffic()
-                     if args.workload == "qwen8b" and args.xf == "none" else None,
-                     "kernel": f"score_rows<{case.dtype}>", "kernel_ms": kern_avg,
-                     "bytes_per_launch": alg_bytes,
-                     "ceiling_gbs": ceiling_gbs, "frac_of_ceiling": achieved / ceiling_gbs,
-                     "ceiling_kernel": "read_rows: pure 16-byte nontemporal reads of every "
-                                       "row pair of the same tensors, one block per pair"},
-        "cpu_baseline": cpu,
+        "logits_gbs": main_leg["logits_gbs"],
+        "roofline": rf,
+        "cpu_baseline": None,
+        "diagnostics": main_leg["diagnostics"],
     }
-    stats = {k: getattr(runner.stats, k) for k in (
-        "ratio0", "clipfrac0", "approx_kl0", "mismatch_kl", "mean_abs_dlogp",
-        "p95_abs_dlogp", "p99_abs_dlogp", "max_abs_dlogp", "argmax_row")}
-    line["diagnostics"] = stats
-    line["segments"] = segments_leg(case, runner.out[2], runner.out[3], runner.ws)
-    line["active_rows"] = active_rows_leg(case, runner.out[3])
-    assert line["active_rows"]["n_active"] == n_active
-    del runner
-    if not args.no_training and args.xf == "none":
-        log("[bench] training-state leg (entropy, lse, dlogits)")
-        torch.cuda.empty_cache()
-        line["training"] = training_leg(case, ids, att, act, cu)
-    if not args.no_exact and args.xf == "none":
-        log("[bench] exact-reduction leg (unsharded and vocabulary shards)")
-        torch.cuda.empty_cache()
-        line["exact"] = exact_leg(case, ids, att, act, cu)
-    if not args.no_lmhead and args.workload == "qwen8b" and args.xf == "none":
-        torch.cuda.empty_cache()
+    sample = None
+    if pool is not None:
+        log("[bench] copying the CPU baseline's sample rows to the host")
+        sample = cpu_sample(pool, case)
+    if args.legs == "all" and args.xf == "none":
+        line["segments"] = segments_leg(case, runner.out[2], runner.out[3], runner.ws)
+        line["active_rows"] = active_rows_leg(case, runner.out[3])
+        if line["active_rows"]["n_active"] != main_leg["n_active"]:
+            raise RuntimeError("active-row list length differs from the active count")
+    del case, ids, att, act, cu, runner
+    torch.cuda.empty_cache()
+    if args.legs == "all" and args.xf == "none":
+        line["configs"] = {}
+        for name in OTHER_CONFIGS[args.workload]:
+            leg, (case, ids, att, act, cu, runner) = score_leg(name, args.steps, args.warmup)
+            line["configs"][name] = leg
+            del runner
+            if name == "qwen8b":
+                torch.cuda.empty_cache()
+                log("[bench] training-state leg (entropy, lse, dlogits)")
+                line["training"] = training_leg(case, ids, att, act, cu)
+                torch.cuda.empty_cache()
+                log("[bench] exact-reduction leg (unsharded and vocabulary shards)")
+                line["exact"] = exact_leg(case, ids, att, act, cu)
+            del case, ids, att, act, cu
+            torch.cuda.empty_cache()
         log("[bench] fused LM-head leg")
         line["lmhead"] = lmhead_leg()
+        torch.cuda.empty_cache()
     # the CPU leg runs last, so the GPU legs above run at the clocks of a busy GPU
-    if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (oracle)")
-        line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    if sample is not None:
+        log(f"[bench] cpu baseline (oracle, {pool.workers} worker processes)")
+        line["cpu_baseline"] = cpu_baseline(pool, sample, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

@@ -117,7 +117,9 @@ typedef struct drift_lse_partial {
  *  logits_dtype    DRIFT_F32 or DRIFT_BF16 (both sides share it).
  *  ids_dtype       DRIFT_I32 or DRIFT_I64.
  *  layout          DRIFT_PAD_RIGHT, DRIFT_PAD_LEFT or DRIFT_PACKED.
- *  num_rows        N, rows of the logits tensors (B*L, or the packed capacity). N < 2^31.
+ *  num_rows        N, rows of the logits tensors (B*L, or the packed capacity). N < 2^31;
+ *                  batches beyond one dispatch's 2^32 - 1 work-items are scored by several
+ *                  launches over consecutive row ranges, with the same per-row results.
  *  vocab           V >= 1, logits per row; every column enters the log-sum-exp.
  *  row_stride      elements between the starts of consecutive rows, >= V.
  *  train_logits, rollout_logits
@@ -234,7 +236,11 @@ typedef struct drift_backend_desc {
 
 /* Workspace bytes for `op` over `num_rows` rows of `vocab` columns of element type
  * `dtype`; `hidden_dim` is H for DRIFT_OP_LMHEAD (num_rows = T there) and ignored
- * otherwise. Returns 0 for invalid arguments. Host only. */
+ * otherwise. Returns 0 for invalid arguments. Host only.
+ * The "WS2 Cross-Config Logprob Drift Contract" page, Kernel Integration Contract, asks a
+ * backend for no hidden long-lived state: the library allocates nothing and keeps nothing
+ * between calls, so every device buffer a call needs beyond its inputs and outputs is a
+ * caller-owned workspace of this size, and everything in it is rewritten by the call. */
 size_t drift_workspace_size(int op, int64_t num_rows, int64_t vocab, int64_t hidden_dim,
                             int dtype);
 
@@ -287,7 +293,12 @@ int drift_selected_logprob(const drift_logprob_args* args, float* train_logp,
 /* Synchronizes `stream` and returns the data-dependent status recorded by the last
  * drift_selected_logprob or drift_lmhead_logprob call on `ws` (priority EMASK > ETOKEN
  * > ENONFINITE), and, if first_bad_row is not NULL, the smallest row index of that
- * error class (-1 when OK). */
+ * error class (-1 when OK). A workspace that no such call initialised gives
+ * DRIFT_EWORKSPACE.
+ * Errors found on the device are reported here rather than hidden: the Kernel
+ * Integration Contract of "WS2 Cross-Config Logprob Drift Contract" rules out a silent
+ * fallback, and the Drift Source Taxonomy of the same page makes a logical-input
+ * violation (mask, token id) an invalid comparison, not a noisy one. */
 int drift_get_status(const void* ws, void* stream, int64_t* first_bad_row);
 
 /* Diagnostics over the active rows of `dlogp` ("Diagnostics" table). Fills *out_host
@@ -339,6 +350,9 @@ int drift_active_rows(const uint8_t* active, int64_t num_rows, int32_t* rows, in
  *   weight      bf16 [H, V] row-major, vocabulary contiguous (V % 8 == 0)
  *   target_ids  int32 [T]; active (nullable) uint8 [T]: inactive rows get 0.0
  *   logp        fp32 [T]
+ * The GEMM runs in one dispatch of one 256-thread block per 256 x 256 (vocab, token) tile,
+ * so ceil(T/256) * ceil(V/256), each rounded up to a multiple of 16, must not exceed
+ * 2^24 - 1 (T up to about 7.1M at V = 151936); larger T returns DRIFT_EINVAL.
  * Products accumulate in fp32 over k = 0..H-1 in a fixed order that does not depend on
  * T or on the row's position, so a row's result is bitwise the same in any batch. */
 int drift_lmhead_logprob(const void* hidden, const void* weight, int64_t T, int64_t H,

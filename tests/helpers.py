@@ -14,6 +14,30 @@ def gpu_available():
     return torch.cuda.is_available()
 
 
+_POOL = None
+
+
+def start_oracle_pool():
+    """Starts the oracle's host worker pool (called at test-session start, before any test
+    touches the GPU)."""
+    global _POOL
+    if _POOL is None:
+        from oracle.pool import OraclePool
+        _POOL = OraclePool()
+
+
+def stop_oracle_pool():
+    global _POOL
+    if _POOL is not None:
+        _POOL.close()
+        _POOL = None
+
+
+def oracle_pool():
+    """The session's oracle worker pool, or None if it was not started."""
+    return _POOL
+
+
 def device_inputs(case, dev="cuda"):
     ids = torch.as_tensor(case.ids, device=dev)
     att = torch.as_tensor(case.attention, device=dev) if case.attention is not None else None

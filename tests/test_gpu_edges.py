@@ -128,3 +128,53 @@ def test_segments_without_rows_or_active_rows():
         want["p99_abs_dlogp"])
     assert segs[2]["argmax_row"] == 40 + want["argmax_row"]
     assert B.segment_diagnostics(d, a, torch.zeros(1, dtype=torch.int32, device="cuda")) == []
+
+
+def test_batch_beyond_one_dispatch():
+    """A batch larger than one dispatch holds (2^32 - 1 work-items: 8388607 rows of 512
+    threads for fp32 scoring, 16777215 rows of 256 threads for dlogits) is covered by
+    consecutive launches over row ranges. Rows on both sides of each boundary, the last
+    rows and random rows against the oracle; every row's `active`; Gate A of the whole
+    dlogp array; dlogits rows on both sides of its boundary."""
+    B = B_()
+    N, V = 16777215 + 129, 8
+    splits = (8388607, 16777215)
+    print(f"[case] fp32 N={N} V={V}: scoring launches split at {splits}", flush=True)
+    rng = np.random.default_rng(41)
+    ids = rng.integers(0, V, N).astype(np.int32)
+    act = (rng.random(N) < 0.9).astype(np.uint8)
+    gen = torch.Generator(device="cuda").manual_seed(41)
+    ro = torch.randn((N, V), generator=gen, device="cuda") * 2.0
+    tr = ro + torch.randn((N, V), generator=gen, device="cuda") * 1e-3
+    ids_d = torch.as_tensor(ids, device="cuda")
+    act_d = torch.as_tensor(act, device="cuda")
+    lse_t = torch.empty(N, dtype=torch.float64, device="cuda")
+    lse_r = torch.empty(N, dtype=torch.float64, device="cuda")
+    t, r, d, a, ws = B.selected_logprob(tr, ro, ids_d, None, act_d, "right", N, 1, check=True,
+                                        lse=(lse_t, lse_r))
+    a_h = a.cpu().numpy()
+    assert np.array_equal(a_h, act)
+    near = np.concatenate([np.arange(s - 3, s + 3) for s in splits] + [np.arange(N - 4, N)])
+    rows = np.unique(np.concatenate([near, rng.integers(0, N, 500)]))
+    rows = rows[act[rows] == 1]
+    idx = torch.as_tensor(rows, device="cuda")
+    ot, orr, od = oracle.score_rows(tr.index_select(0, idx).cpu().numpy(),
+                                    ro.index_select(0, idx).cpu().numpy(), "f32", ids[rows])
+    for g, w in ((t, ot), (r, orr), (d, od)):
+        err = np.abs(g.index_select(0, idx).cpu().numpy().astype(np.float64) - w)
+        assert float(err.max()) <= LOGP_TOL
+    d_h = d.cpu().numpy()
+    st, s = B.diagnostics(d, a, 0.2, 0.2, logprob_ws=ws)
+    assert status_name(st) == "OK"
+    from helpers import assert_stats_exact
+    assert_stats_exact(s, oracle.diagnostics(d_h, a_h, 0.2, 0.2))
+    del d, r, lse_r
+    g = torch.empty((N, V), dtype=torch.float32, device="cuda")
+    B.dlogits(tr, ro, ids_d, 0, lse_t, a, out=g)
+    drows = np.arange(splits[1] - 3, splits[1] + 3)
+    idx = torch.as_tensor(drows, device="cuda")
+    want = oracle.dlogits_rows(tr.index_select(0, idx).cpu().numpy(), "f32", ids[drows],
+                               act[drows])
+    got = g.index_select(0, idx).cpu().numpy().astype(np.float64)
+    assert np.abs(got - want).max() <= 2e-5
+    torch.cuda.empty_cache()

@@ -92,15 +92,18 @@ def test_batch_composition_control_is_bitwise_zero():
 
 @pytest.mark.slow
 def test_full_size_sampled_rows_and_invariance():
-    """T=16384, H=4096, V=151936 as timed: sampled rows against the oracle, and four rows
-    (including the first and the last) re-scored in batches of 1, 7 and 64."""
+    """T=16384, H=4096, V=151936 as timed: 256 rows (the first, the last and 254 drawn
+    without replacement) against the oracle, and four rows (including the first and the
+    last) re-scored in batches of 1, 7 and 64."""
     from train_rollout_logprob_amd import binding as B
     case = synth.make_lmhead_case(device="cuda")
     ids = torch.as_tensor(case.ids, device="cuda")
     logp, ws = B.lmhead_logprob(case.hidden, case.weight, ids, check=True)
     full = logp.cpu().numpy()
     rng = np.random.default_rng(12)
-    rows = np.unique(np.concatenate([[0, case.T - 1], rng.integers(0, case.T, 14)]))
+    drawn = rng.choice(np.arange(1, case.T - 1), 254, replace=False)
+    rows = np.unique(np.concatenate([[0, case.T - 1], drawn]))
+    assert len(rows) == 256
     want = _oracle(case, rows)
     err = np.abs(full[rows].astype(np.float64) - want)
     print(f"[case] lmhead full max err {err.max():.3e} over {len(rows)} rows", flush=True)

@@ -325,6 +325,7 @@ int drift_lmhead_logprob(const void* hidden, const void* weight, int64_t T, int6
                          void* ws, size_t ws_bytes, void* stream) {
   if (T < 0 || T > INT32_MAX || H < 1 || V < 1 || V > INT32_MAX) return DRIFT_EINVAL;
   if (H % 8 != 0 || V % 8 != 0 || H > (int64_t{1} << 22)) return DRIFT_EINVAL;
+  if (!lmhead_shape_ok(T, V)) return DRIFT_EINVAL;
   if (T > 0 && (!hidden || !weight || !target_ids || !logp)) return DRIFT_EINVAL;
   if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(target_ids, 4) ||
       !aligned(logp, 4))

@@ -57,6 +57,7 @@ struct ScoreParams {
   // export) the per-side partial outputs; null = finalize the row here
   int64_t vstart;
   drift_lse_partial* part[2];
+  int64_t row0;  // first row of the launch (set by the launcher)
 };
 // Launches the header initialisation and the scoring kernel; `ev` (nullable) are recorded
 // right before and after the scoring kernel.
@@ -115,6 +116,7 @@ struct LmheadParams {
   char* ws;
 };
 size_t lmhead_ws_bytes(int64_t T, int64_t H, int64_t V);
+bool lmhead_shape_ok(int64_t T, int64_t V);  // the GEMM grid fits one dispatch
 hipError_t launch_lmhead(const LmheadParams& p, hipStream_t s);
 
 struct DlogitsParams {
@@ -127,6 +129,7 @@ struct DlogitsParams {
   const uint8_t* active;
   const float* grad;  // nullable: 1 on every active row
   void* out;
+  int64_t row0;  // first row of the launch (set by the launcher)
 };
 hipError_t launch_dlogits(const DlogitsParams& p, hipStream_t s);
 

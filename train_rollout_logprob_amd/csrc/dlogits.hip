@@ -111,7 +111,7 @@ __device__ __forceinline__ void grad_group(float (&x)[VEC], int64_t c0, int64_t 
 template <typename T, typename O, int NT, int U, bool XF>
 __global__ void __launch_bounds__(NT) dlogits_rows(DlogitsParams p) {
   constexpr int VEC = Elem<T>::kVec;
-  const int64_t r = blockIdx.x;
+  const int64_t r = p.row0 + blockIdx.x;
   const int tid = threadIdx.x;
   const char* row = (const char*)p.logits + (size_t)r * (size_t)p.stride * sizeof(T);
   char* orow = (char*)p.out + (size_t)r * (size_t)p.out_stride * sizeof(O);
@@ -172,11 +172,18 @@ __global__ void __launch_bounds__(NT) dlogits_rows(DlogitsParams p) {
 template <typename T, typename O>
 void launch_typed(const DlogitsParams& p, hipStream_t s) {
   constexpr int NT = DRIFT_DLOGITS_THREADS, U = DRIFT_DLOGITS_UNROLL;
-  const dim3 grid((unsigned)p.N);
-  if (p.xf.n > 0)
-    hipLaunchKernelGGL((dlogits_rows<T, O, NT, U, true>), grid, dim3(NT), 0, s, p);
-  else
-    hipLaunchKernelGGL((dlogits_rows<T, O, NT, U, false>), grid, dim3(NT), 0, s, p);
+  // at most 2^32 - 1 work-items per dispatch: larger batches take several launches over
+  // consecutive row ranges (p.row0 = first row of the launch)
+  const int64_t per = (int64_t)(0xffffffffu / (unsigned)NT);
+  DlogitsParams q = p;
+  for (int64_t r0 = 0; r0 < p.N; r0 += per) {
+    q.row0 = r0;
+    const dim3 grid((unsigned)(p.N - r0 < per ? p.N - r0 : per));
+    if (p.xf.n > 0)
+      hipLaunchKernelGGL((dlogits_rows<T, O, NT, U, true>), grid, dim3(NT), 0, s, q);
+    else
+      hipLaunchKernelGGL((dlogits_rows<T, O, NT, U, false>), grid, dim3(NT), 0, s, q);
+  }
 }
 
 }  // namespace

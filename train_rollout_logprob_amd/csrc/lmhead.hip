@@ -493,6 +493,15 @@ __global__ void __launch_bounds__(256) lm_merge(const Partial* __restrict__ part
 
 size_t lmhead_ws_bytes(int64_t T, int64_t H, int64_t V) { return LmLayout::make(T, H, V).total; }
 
+// The GEMM runs one block of kPThreads per (vocab tile, token tile) in one dispatch, which
+// holds at most 2^32 - 1 work-items: T is limited by that (about 7.1M tokens at V = 151936).
+bool lmhead_shape_ok(int64_t T, int64_t V) {
+  const int64_t nVt = (V + kBV - 1) / kBV, nTt = (T + kBT - 1) / kBT;
+  const int64_t nVt_pad = (nVt + kGroupV - 1) / kGroupV * kGroupV;
+  const int64_t nTt_pad = (nTt + kGroupT - 1) / kGroupT * kGroupT;
+  return nVt_pad * nTt_pad <= (int64_t)(0xffffffffu / kPThreads);
+}
+
 hipError_t launch_lmhead(const LmheadParams& p, hipStream_t s) {
   const LmLayout l = LmLayout::make(p.T, p.H, p.V);
   hipLaunchKernelGGL(lm_init, dim3(1), dim3(64), 0, s, p.ws);

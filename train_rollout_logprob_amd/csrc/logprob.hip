@@ -246,7 +246,7 @@ __global__ void __launch_bounds__(NT) score_rows(ScoreParams p) {
   __shared__ double s_s2[2][ENT ? NW : 1];
   __shared__ int64_t s_y;
   WsHeader* h = (WsHeader*)p.ws;
-  const int64_t r = blockIdx.x;
+  const int64_t r = p.row0 + blockIdx.x;
   const int tid = threadIdx.x;
   if (tid == 0) {
     int64_t end = p.N;
@@ -413,7 +413,7 @@ __global__ void __launch_bounds__(NT) score_rows_exact(ScoreParams p) {
   __shared__ AccX s_acc[2][NW];
   __shared__ int64_t s_y;
   WsHeader* h = (WsHeader*)p.ws;
-  const int64_t r = blockIdx.x;
+  const int64_t r = p.row0 + blockIdx.x;
   const int tid = threadIdx.x;
   const bool shard = p.part[0] != nullptr;
   if (tid == 0) {
@@ -564,6 +564,20 @@ __global__ void __launch_bounds__(256) merge_shards(MergeParams m) {
 static_assert(DRIFT_SCORE_THREADS_BF16 % 64 == 0 && DRIFT_SCORE_THREADS_BF16 <= 1024, "shape");
 static_assert(DRIFT_SCORE_THREADS_F32 % 64 == 0 && DRIFT_SCORE_THREADS_F32 <= 1024, "shape");
 
+// Launches `kernel` (one block of `nt` threads per row) over rows [0, p.N). A dispatch
+// holds at most 2^32 - 1 work-items per grid dimension, so larger batches are covered by
+// consecutive launches over row ranges (p.row0 = first row of the launch); a row's
+// arithmetic does not depend on the launch it falls in.
+template <typename K>
+void launch_over_rows(K kernel, ScoreParams p, int nt, hipStream_t s) {
+  const int64_t per = (int64_t)(0xffffffffu / (unsigned)nt);
+  for (int64_t r0 = 0; r0 < p.N; r0 += per) {
+    p.row0 = r0;
+    const int64_t n = p.N - r0 < per ? p.N - r0 : per;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)n), dim3(nt), 0, s, p);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_score(const ScoreParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
@@ -572,13 +586,12 @@ hipError_t launch_score(const ScoreParams& p, hipStream_t s, hipEvent_t ev0, hip
   if (e != hipSuccess) return e;
   if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
   if (p.N > 0) {
-    const dim3 grid((unsigned)p.N);
     const bool xf = p.xf[0].n > 0 || p.xf[1].n > 0;
     const bool ent = p.ent[0] != nullptr || p.ent[1] != nullptr;
     constexpr int NB = DRIFT_SCORE_THREADS_BF16, UB = DRIFT_SCORE_UNROLL_BF16;
     constexpr int NF = DRIFT_SCORE_THREADS_F32, UF = DRIFT_SCORE_UNROLL_F32;
 #define DRIFT_SCORE_LAUNCH(T, NT, U, X, E) \
-  hipLaunchKernelGGL((score_rows<T, NT, U, X, E>), grid, dim3(NT), 0, s, p)
+  launch_over_rows(score_rows<T, NT, U, X, E>, p, NT, s)
     if (p.dtype == DRIFT_BF16) {
       if (xf && ent) DRIFT_SCORE_LAUNCH(uint16_t, NB, UB, true, true);
       else if (xf) DRIFT_SCORE_LAUNCH(uint16_t, NB, UB, true, false);
@@ -611,9 +624,7 @@ hipError_t launch_score_exact(const ScoreParams& p, hipStream_t s, hipEvent_t ev
     const bool xf = p.xf[0].n > 0 || p.xf[1].n > 0;
     const int vec = p.dtype == DRIFT_BF16 ? 8 : 4;
     const bool wide = (p.V + vec - 1) / vec >= 4096;
-    auto go = [&](auto kernel, int nt) {
-      hipLaunchKernelGGL(kernel, dim3((unsigned)p.N), dim3(nt), 0, s, p);
-    };
+    auto go = [&](auto kernel, int nt) { launch_over_rows(kernel, p, nt, s); };
     constexpr int U = 4;
     if (p.dtype == DRIFT_BF16) {
       if (wide) xf ? go(score_rows_exact<uint16_t, 256, U, true>, 256)
