@@ -42,6 +42,8 @@ WORKLOAD_TEXT = {
               "U[64,2048] via cu_seqlens, Student-t(2) drift",
     "tiny": "tiny paired scoring: fp32 logits, V=1024, B=2, L=64, right padding",
 }
+# legs measured beside the main line (outside its timed region)
+LEGS = ("segments", "configs", "training", "exact", "lmhead")
 # the other scoring workloads measured beside the main one, in this order
 OTHER_CONFIGS = {"large": ("qwen8b", "packed", "tiny"), "qwen8b": ("large", "packed", "tiny"),
                  "packed": ("large", "qwen8b", "tiny"), "tiny": ("large", "qwen8b", "packed")}
@@ -517,14 +519,19 @@ def main():
                                                              "lmhead"],
                     help="the main line's scoring workload (default: large, the largest "
                          "single-GPU batch)")
-    ap.add_argument("--legs", default="all", choices=["all", "none"],
-                    help="none: measure the main workload only (for profiling runs)")
+    ap.add_argument("--legs", default="all",
+                    help="legs beside the main line: all, none (for profiling runs), or a "
+                         "comma list of " + ", ".join(LEGS))
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
                     help="copy: a plain device copy of known size, to calibrate HBM counters")
     ap.add_argument("--copy-mib", type=int, default=4096)
     ap.add_argument("--xf", default="none", choices=["none", "temperature", "softcap"],
                     help="apply a logit transform on both sides (cost of the option)")
     args = ap.parse_args()
+    args.legs = (set(LEGS) if args.legs == "all" else set() if args.legs == "none"
+                 else set(args.legs.split(",")))
+    if not args.legs <= set(LEGS):
+        ap.error(f"--legs: unknown leg(s) {sorted(args.legs - set(LEGS))}")
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build has "
               f"no multi-GPU path; the per-row work shards by rows with no exchange.",
@@ -605,28 +612,39 @@ def run(args, pool):
     if pool is not None:
         log("[bench] copying the CPU baseline's sample rows to the host")
         sample = cpu_sample(pool, case)
-    if args.legs == "all" and args.xf == "none":
+    legs = args.legs if args.xf == "none" else set()
+
+    def qwen8b_legs(case, ids, att, act, cu):
+        if "training" in legs:
+            torch.cuda.empty_cache()
+            log("[bench] training-state leg (entropy, lse, dlogits)")
+            line["training"] = training_leg(case, ids, att, act, cu)
+        if "exact" in legs:
+            torch.cuda.empty_cache()
+            log("[bench] exact-reduction leg (unsharded and vocabulary shards)")
+            line["exact"] = exact_leg(case, ids, att, act, cu)
+
+    if "segments" in legs:
         line["segments"] = segments_leg(case, runner.out[2], runner.out[3], runner.ws)
         line["active_rows"] = active_rows_leg(case, runner.out[3])
         if line["active_rows"]["n_active"] != main_leg["n_active"]:
             raise RuntimeError("active-row list length differs from the active count")
-    del case, ids, att, act, cu, runner
+    del runner
+    if args.workload == "qwen8b":
+        qwen8b_legs(case, ids, att, act, cu)
+    del case, ids, att, act, cu
     torch.cuda.empty_cache()
-    if args.legs == "all" and args.xf == "none":
+    if "configs" in legs:
         line["configs"] = {}
         for name in OTHER_CONFIGS[args.workload]:
             leg, (case, ids, att, act, cu, runner) = score_leg(name, args.steps, args.warmup)
             line["configs"][name] = leg
             del runner
             if name == "qwen8b":
-                torch.cuda.empty_cache()
-                log("[bench] training-state leg (entropy, lse, dlogits)")
-                line["training"] = training_leg(case, ids, att, act, cu)
-                torch.cuda.empty_cache()
-                log("[bench] exact-reduction leg (unsharded and vocabulary shards)")
-                line["exact"] = exact_leg(case, ids, att, act, cu)
+                qwen8b_legs(case, ids, att, act, cu)
             del case, ids, att, act, cu
             torch.cuda.empty_cache()
+    if "lmhead" in legs:
         log("[bench] fused LM-head leg")
         line["lmhead"] = lmhead_leg()
         torch.cuda.empty_cache()
