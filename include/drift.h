@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define DRIFT_ABI_VERSION 6
+#define DRIFT_ABI_VERSION 7
 
 /* ---- status codes ---------------------------------------------------------------- */
 #define DRIFT_OK          0
@@ -311,6 +311,31 @@ int drift_get_status(const void* ws, void* stream, int64_t* first_bad_row);
 int drift_diagnostics(const float* dlogp, const uint8_t* active, int64_t num_rows,
                       double eps_low, double eps_high, const void* logprob_ws,
                       drift_stats* out_host, void* ws, size_t ws_bytes, void* stream);
+
+/* Largest batch of drift_diagnostics_noalloc. */
+#define DRIFT_NOALLOC_MAX_ROWS (1 << 22)
+
+/* drift_diagnostics for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): no workspace argument,
+ * no synchronization, statistics written to device memory.
+ *   out_dev   drift_stats [1] device, caller-owned: receives the statistics; its `status`
+ *             field holds what drift_diagnostics would return (DRIFT_OK, DRIFT_ENOACTIVE,
+ *             DRIFT_ENONFINITE, or the logprob_ws status)
+ *   other arguments as drift_diagnostics; num_rows <= DRIFT_NOALLOC_MAX_ROWS, else
+ *   DRIFT_EINVAL before any launch
+ * The statistics are bitwise those of drift_diagnostics on the same inputs. The kernels'
+ * scratch (tile partials and digit histograms, 561 KiB) is a device array inside the
+ * library, one copy per GPU, kept until the process ends; the first call on a device looks
+ * up its address (hipGetSymbolAddress) with that device current, later calls reuse it.
+ * Every call on a GPU shares that GPU's scratch, and the kernels rewrite everything they
+ * read from it, so sequential calls are independent; calls that can overlap on one GPU
+ * (different streams, threads or processes sharing it) race and must be serialized by
+ * the caller. The call itself allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine) and records no memset. Asynchronous; returns DRIFT_EHIP if a launch or
+ * the address lookup fails. */
+int drift_diagnostics_noalloc(const float* dlogp, const uint8_t* active, int64_t num_rows,
+                              double eps_low, double eps_high, const void* logprob_ws,
+                              drift_stats* out_dev, void* stream);
 
 /* The same statistics per segment of rows ("Diagnostics" table: per-sequence views, and
  * the per-rank versions of a distributed run, each rank's rows being one segment).

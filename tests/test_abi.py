@@ -23,7 +23,7 @@ def test_header_declares_the_boundary():
                             "drift_dlogits", "drift_segment_diagnostics",
                             "drift_shard_partials", "drift_merge_shards",
                             "drift_active_rows", "drift_backend_descriptor",
-                            "drift_strerror"])
+                            "drift_strerror", "drift_diagnostics_noalloc"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -50,7 +50,7 @@ def test_struct_layouts_match_header():
 def test_descriptor_and_strerror():
     from train_rollout_logprob_amd import binding as B
     d = B.drift_backend_descriptor()
-    assert d["abi_version"] == 6 and d["archs"] == "gfx950"
+    assert d["abi_version"] == 7 and d["archs"] == "gfx950"
     assert "batch composition" in d["determinism"]
     assert d["lse_domain"] == "natural log"
     assert d["build_fingerprint"].startswith("src:")
@@ -255,3 +255,18 @@ def test_active_rows_host_checks():
     assert f(ok, 5000, ctypes.c_void_p((1 << 20) + 2), ok, ws, need, None) == B.DRIFT_EINVAL
     assert f(ok, 5000, ok, ok, ws, need - 1, None) == B.DRIFT_EWORKSPACE
     assert f(ok, 5000, ok, ok, ws + 8, need, None) == B.DRIFT_EWORKSPACE
+
+
+def test_diagnostics_noalloc_host_checks():
+    """Sizes beyond the scratch, null or misaligned outputs and bad eps fail before any
+    launch (fake device pointers are never dereferenced)."""
+    from train_rollout_logprob_amd import binding as B
+    lib = B.lib
+    d, a, out = 4096, 8192, 16384
+    big = B.DRIFT_NOALLOC_MAX_ROWS + 1
+    assert lib.drift_diagnostics_noalloc(d, a, big, 0.2, 0.2, None, out, None) == B.DRIFT_EINVAL
+    assert lib.drift_diagnostics_noalloc(d, a, 10, 0.2, 0.2, None, None, None) == B.DRIFT_EINVAL
+    assert lib.drift_diagnostics_noalloc(d, a, 10, 0.2, 0.2, None, out + 4, None) == B.DRIFT_EINVAL
+    assert lib.drift_diagnostics_noalloc(d, a, -1, 0.2, 0.2, None, out, None) == B.DRIFT_EINVAL
+    assert lib.drift_diagnostics_noalloc(d, a, 10, 1.0, 0.2, None, out, None) == B.DRIFT_EINVAL
+    assert lib.drift_diagnostics_noalloc(None, a, 10, 0.2, 0.2, None, out, None) == B.DRIFT_EINVAL

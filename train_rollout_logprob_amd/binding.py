@@ -44,7 +44,9 @@ XF_CODES = {"scale": DRIFT_XF_SCALE, "temperature": DRIFT_XF_TEMPERATURE,
 EXPORTS = ("drift_workspace_size", "drift_selected_logprob", "drift_get_status",
            "drift_diagnostics", "drift_segment_diagnostics", "drift_lmhead_logprob",
            "drift_dlogits", "drift_shard_partials", "drift_merge_shards",
-           "drift_active_rows", "drift_backend_descriptor", "drift_strerror")
+           "drift_active_rows", "drift_backend_descriptor", "drift_strerror",
+           "drift_diagnostics_noalloc")
+DRIFT_NOALLOC_MAX_ROWS = 1 << 22
 
 
 class drift_transform(ctypes.Structure):
@@ -108,6 +110,9 @@ def _load():
     lib.drift_diagnostics.argtypes = [vp, vp, i64, ctypes.c_double, ctypes.c_double, vp,
                                       ctypes.POINTER(drift_stats), vp, sz, vp]
     lib.drift_diagnostics.restype = ctypes.c_int
+    lib.drift_diagnostics_noalloc.argtypes = [vp, vp, i64, ctypes.c_double, ctypes.c_double,
+                                              vp, vp, vp]
+    lib.drift_diagnostics_noalloc.restype = ctypes.c_int
     lib.drift_segment_diagnostics.argtypes = [vp, vp, i64, vp, i64, ctypes.c_double,
                                               ctypes.c_double, vp, vp, vp]
     lib.drift_segment_diagnostics.restype = ctypes.c_int
@@ -167,6 +172,13 @@ def drift_segment_diagnostics(dlogp, active, num_rows: int, seg_offsets, num_seg
                               stream=None) -> int:
     return int(lib.drift_segment_diagnostics(_ptr(dlogp), _ptr(active), num_rows,
                                              _ptr(seg_offsets), num_segments, eps_low,
+                                             eps_high, _ptr(logprob_ws), _ptr(out_dev),
+                                             _stream(stream)))
+
+
+def drift_diagnostics_noalloc(dlogp, active, num_rows: int, eps_low: float, eps_high: float,
+                              logprob_ws, out_dev, stream=None) -> int:
+    return int(lib.drift_diagnostics_noalloc(_ptr(dlogp), _ptr(active), num_rows, eps_low,
                                              eps_high, _ptr(logprob_ws), _ptr(out_dev),
                                              _stream(stream)))
 
@@ -472,6 +484,21 @@ def segment_diagnostics(dlogp, active, seg_offsets, eps_low=0.2, eps_high=0.2, l
     host = bytearray(out.cpu().numpy().tobytes())
     arr = (drift_stats * max(S, 1)).from_buffer(host)
     return [arr[i].as_dict() for i in range(S)]
+
+
+def diagnostics_noalloc(dlogp, active, eps_low=0.2, eps_high=0.2, logprob_ws=None, out=None,
+                        stream=None):
+    """Call drift_diagnostics_noalloc (no workspace; statistics written to the device
+    buffer `out`, a uint8 tensor of sizeof(drift_stats) bytes, allocated here if None).
+    Returns (stats dict, out); the dict comes from one synchronizing copy of `out`."""
+    N = dlogp.shape[0]
+    if out is None:
+        out = torch.empty(ctypes.sizeof(drift_stats), dtype=torch.uint8, device=dlogp.device)
+    st = drift_diagnostics_noalloc(dlogp, active, N, eps_low, eps_high, logprob_ws, out, stream)
+    if st != DRIFT_OK:
+        raise DriftError(st, "drift_diagnostics_noalloc")
+    host = bytearray(out.cpu().numpy().tobytes())
+    return drift_stats.from_buffer(host).as_dict(), out
 
 
 def report(stats: dict, segments=None, **metadata) -> dict:

@@ -264,7 +264,7 @@ int drift_diagnostics(const float* dlogp, const uint8_t* active, int64_t num_row
     return DRIFT_EINVAL;
   if (!ws || !aligned(ws, 256) || ws_bytes < diag_ws_bytes(num_rows)) return DRIFT_EWORKSPACE;
   hipStream_t s = (hipStream_t)stream;
-  DiagParams dp;
+  DiagParams dp{};
   dp.N = num_rows;
   dp.eps_low = eps_low;
   dp.eps_high = eps_high;
@@ -279,6 +279,30 @@ int drift_diagnostics(const float* dlogp, const uint8_t* active, int64_t num_row
     return DRIFT_EHIP;
   if (hipStreamSynchronize(s) != hipSuccess) return DRIFT_EHIP;
   return out_host->status;
+}
+
+int drift_diagnostics_noalloc(const float* dlogp, const uint8_t* active, int64_t num_rows,
+                              double eps_low, double eps_high, const void* logprob_ws,
+                              drift_stats* out_dev, void* stream) {
+  if (!out_dev || !aligned(out_dev, 8) || num_rows < 0) return DRIFT_EINVAL;
+  if (num_rows > DRIFT_NOALLOC_MAX_ROWS) return DRIFT_EINVAL;
+  if (num_rows > 0 && (!dlogp || !active || !aligned(dlogp, 4))) return DRIFT_EINVAL;
+  if (!(eps_low >= 0.0 && eps_low < 1.0 && eps_high >= 0.0 && eps_high < 1.0))
+    return DRIFT_EINVAL;
+  char* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (diag_noalloc_scratch(&ws, &ws_bytes) != hipSuccess) return DRIFT_EHIP;
+  if (ws_bytes < diag_ws_bytes(num_rows)) return DRIFT_EWORKSPACE;  // cannot happen
+  DiagParams dp{};
+  dp.N = num_rows;
+  dp.eps_low = eps_low;
+  dp.eps_high = eps_high;
+  dp.d = dlogp;
+  dp.active = active;
+  dp.lp = (const WsHeader*)logprob_ws;
+  dp.ws = ws;
+  dp.out = out_dev;
+  return launch_diagnostics(dp, (hipStream_t)stream) == hipSuccess ? DRIFT_OK : DRIFT_EHIP;
 }
 
 int drift_segment_diagnostics(const float* dlogp, const uint8_t* active, int64_t num_rows,

@@ -82,6 +82,7 @@ struct DiagParams {
   const uint8_t* active;
   const WsHeader* lp;  // nullable: header of the drift_selected_logprob call that made d
   char* ws;
+  drift_stats* out;    // nullable: where the statistics go (null = the workspace's record)
 };
 
 // Status recorded in a logprob workspace header (priority mask > token > non-finite).
@@ -103,6 +104,10 @@ struct SegParams {
 };
 hipError_t launch_segment_diagnostics(const SegParams& p, hipStream_t s);
 size_t diag_ws_bytes(int64_t N);
+// The diagnostics scratch of the current device for drift_diagnostics_noalloc (a
+// file-scope device array of the diagnostics source; its address is looked up once per
+// device).
+hipError_t diag_noalloc_scratch(char** ptr, size_t* bytes);
 size_t diag_stats_offset();
 hipError_t launch_diagnostics(const DiagParams& p, hipStream_t s);
 

@@ -23,6 +23,9 @@
 // depend on scheduling; the sums are fp64 in an order that depends only on N.
 #include <math.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "common.h"
 
 namespace drift {
@@ -59,19 +62,29 @@ constexpr int64_t kSelSingleMax = 65536;
 constexpr int kPassThreads = 256;
 constexpr int kPassRowsPerBlock = 8192;
 
+constexpr size_t up256(size_t x) { return (x + 255) / 256 * 256; }
+
 struct DiagLayout {
-  size_t partial_off, hist_off, total;
-  int G;
-  __host__ __device__ static DiagLayout make(int64_t N) {
+  size_t partial_off = 0, hist_off = 0, total = 0;
+  int G = 0;
+  __host__ __device__ static constexpr DiagLayout make(int64_t N) {
     DiagLayout l;
     l.G = (int)((N + kDiagTile - 1) / kDiagTile);
     l.partial_off = 512;
-    l.hist_off = l.partial_off + align_up((size_t)(l.G > 0 ? l.G : 1) * sizeof(TilePartial), 256);
+    l.hist_off = l.partial_off + up256((size_t)(l.G > 0 ? l.G : 1) * sizeof(TilePartial));
     // digit histograms: [3 digits][2 quantiles][kBins] u32 (the first digit uses quantile 0)
-    l.total = l.hist_off + (N > kSelSingleMax ? align_up(3 * kNumQ * kBins * 4, 256) : 0);
+    l.total = l.hist_off + (N > kSelSingleMax ? up256(3 * kNumQ * kBins * 4) : 0);
     return l;
   }
 };
+
+// Scratch of drift_diagnostics_noalloc: the workspace of its largest batch
+// (DRIFT_NOALLOC_MAX_ROWS rows: state, tile partials, digit histograms), one copy per GPU,
+// held until the process ends. Host code uses the per-device address from
+// diag_noalloc_scratch, never this name.
+constexpr size_t kNoAllocScratchBytes = DiagLayout::make(DRIFT_NOALLOC_MAX_ROWS).total;
+static_assert(kNoAllocScratchBytes < (size_t{1} << 20), "modest scratch");
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 __device__ __forceinline__ unsigned int key_of(float d) { return __float_as_uint(fabsf(d)); }
 constexpr unsigned int kNoKey = 0xffffffffu;  // no row (keys have bit 31 clear)
@@ -396,7 +409,7 @@ __global__ void __launch_bounds__(kSelThreads) diag_select(DiagParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const DiagLayout lay = DiagLayout::make(p.N);
   const TilePartial* tp = (const TilePartial*)(p.ws + lay.partial_off);
-  SelState* st = (SelState*)p.ws;
+  drift_stats& S = p.out ? *p.out : ((SelState*)p.ws)->stats;
   if (wave == 0) {
     RowStats a = {};
     for (int g = lane; g < lay.G; g += 64) {
@@ -410,7 +423,7 @@ __global__ void __launch_bounds__(kSelThreads) diag_select(DiagParams p) {
   if (tid == 0) {
     RowStats a = {};
     for (int g = 0; g < 64; ++g) add_stats(a, s_lane[g]);
-    finish_stats(st->stats, a, p.lp);
+    finish_stats(S, a, p.lp);
     for (int q = 0; q < kNumQ; ++q) {
       s_rank[q] = quantile_rank(q, a.n);
       s_prefix[q] = 0;
@@ -432,8 +445,8 @@ __global__ void __launch_bounds__(kSelThreads) diag_select(DiagParams p) {
     radix_select<kSelThreads, 16>(p.d, p.active, 0, p.N, s_hist, s_rank, s_prefix);
   }
   if (tid == 0) {
-    st->stats.p95_abs_dlogp = __uint_as_float(s_prefix[0]);
-    st->stats.p99_abs_dlogp = __uint_as_float(s_prefix[1]);
+    S.p95_abs_dlogp = __uint_as_float(s_prefix[0]);
+    S.p99_abs_dlogp = __uint_as_float(s_prefix[1]);
   }
 }
 
@@ -567,6 +580,32 @@ __global__ void __launch_bounds__(kDiagThreads) diag_segments(SegParams p) {
 }  // namespace
 
 size_t diag_ws_bytes(int64_t N) { return DiagLayout::make(N).total; }
+
+hipError_t diag_noalloc_scratch(char** ptr, size_t* bytes) {
+  // the device address of `scratch`, looked up once per device with that device current
+  constexpr int kMaxDevices = 64;
+  static std::atomic<char*> cache[kMaxDevices];
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  char* p = cache[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = cache[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* q = nullptr;
+      e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      p = (char*)q;
+      cache[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  *bytes = kNoAllocScratchBytes;
+  return hipSuccess;
+}
 size_t diag_stats_offset() { return offsetof(SelState, stats); }
 
 hipError_t launch_segment_diagnostics(const SegParams& p, hipStream_t s) {
