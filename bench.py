@@ -197,7 +197,8 @@ def cpu_baseline(pool, sample, budget_s):
 
 def lmhead_leg(steps=5, warmup=2):
     """Fused LM-head workload (hidden [16384, 4096] x W [4096, 151936], bf16): the whole
-    drift_lmhead_logprob call timed with events on the launch stream."""
+    drift_lmhead_logprob call timed with events on the launch stream; beside it, for
+    context, the vendor library's plain GEMM of the same shape (logits written out)."""
     import torch
 
     from train_rollout_logprob_amd import binding as B
@@ -222,11 +223,29 @@ def lmhead_leg(steps=5, warmup=2):
     ms = e0.elapsed_time(e1) / steps
     flop = 2.0 * case.T * case.H * case.V
     tflops = flop / (ms * 1e-3) / 1e12
-    return {"workload": f"fused LM-head: hidden [{case.T}, {case.H}] x W [{case.H}, {case.V}] "
-                        f"bf16, fp32 accumulation", "ms_per_call": ms,
-            "active_tokens_per_s": case.T / (ms * 1e-3), "tflops": tflops,
-            "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS, "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
-            "flop_per_call": flop}
+    out = {"workload": f"fused LM-head: hidden [{case.T}, {case.H}] x W [{case.H}, {case.V}] "
+                       f"bf16, fp32 accumulation", "ms_per_call": ms,
+           "active_tokens_per_s": case.T / (ms * 1e-3), "tflops": tflops,
+           "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS, "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+           "flop_per_call": flop}
+    del ws
+    torch.cuda.empty_cache()
+    # context, not the product path: the plain bf16 GEMM of the same shape through the
+    # vendor library (torch.matmul -> hipBLASLt), which writes the logits instead of
+    # reducing them, timed the same way on the same box
+    z = torch.empty((case.T, case.V), dtype=torch.bfloat16, device="cuda:0")
+    for _ in range(warmup):
+        torch.matmul(case.hidden, case.weight, out=z)
+    e0.record()
+    for _ in range(steps):
+        torch.matmul(case.hidden, case.weight, out=z)
+    e1.record()
+    torch.cuda.synchronize()
+    ref_ms = e0.elapsed_time(e1) / steps
+    out["plain_gemm_reference"] = {"what": "torch.matmul bf16 of the same shape (hipBLASLt), "
+                                           "logits written to HBM", "ms_per_call": ref_ms,
+                                   "tflops": flop / (ref_ms * 1e-3) / 1e12}
+    return out
 
 
 def segments_leg(case, d, active, logprob_ws, steps=20):
