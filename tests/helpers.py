@@ -1,5 +1,7 @@
 """Shared helpers of the GPU tests: run the library on a synthetic batch, and run the
 oracle on the same inputs copied to the host."""
+import math
+
 import numpy as np
 import torch
 
@@ -131,3 +133,32 @@ def make_small(spec, dev="cuda"):
     spec = dict(spec)
     name = spec.pop("name")
     return synth.make_logits_case(name, device=dev, **spec)
+
+
+def assert_gate_b(got, want, d_oracle_active, eps_low=0.2, eps_high=0.2, tol=LOGP_TOL):
+    """Gate B: the library's statistics of its fp32 dlogp against the oracle's statistics of
+    its own fp64 dlogp. Means to MEAN_RTOL relative (mean_dlogp and mismatch_kl, which sit
+    near 0, to MEAN_RTOL of mean |d|). Each GPU dlogp is within `tol` of the oracle's, so an
+    order statistic of |d| is too, and a clip decision can differ only for rows within
+    `tol` of a clip edge: the clip counts may differ by at most the number of such rows,
+    and the worst row must match when its lead over the runner-up exceeds 2 tol."""
+    assert got["n_active"] == want["n_active"]
+    assert got["n_nonfinite"] == want["n_nonfinite"] == 0
+    for k in ("ratio0", "approx_kl0", "mean_abs_dlogp"):
+        g, w = got[k], want[k]
+        assert abs(g - w) <= MEAN_RTOL * abs(w), (k, g, w)
+    for k in ("mean_dlogp", "mismatch_kl"):
+        g, w = got[k], want[k]
+        assert abs(g - w) <= MEAN_RTOL * want["mean_abs_dlogp"], (k, g, w)
+    d = np.asarray(d_oracle_active, dtype=np.float64)
+    near_lo = int((np.abs(d - math.log1p(-eps_low)) <= tol).sum())
+    near_hi = int((np.abs(d - math.log1p(eps_high)) <= tol).sum())
+    assert abs(got["n_clip_low"] - want["n_clip_low"]) <= near_lo
+    assert abs(got["n_clip_high"] - want["n_clip_high"]) <= near_hi
+    n_clip = got["n_clip_low"] + got["n_clip_high"]
+    assert abs(got["clipfrac0"] - n_clip / got["n_active"]) <= 1e-15
+    for k in ("p95_abs_dlogp", "p99_abs_dlogp", "max_abs_dlogp"):
+        assert abs(got[k] - want[k]) <= tol, (k, got[k], want[k])
+    a = np.sort(np.abs(d))
+    if len(a) > 1 and a[-1] - a[-2] > 2 * tol:
+        assert got["argmax_row"] == want["argmax_row"]
