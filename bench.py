@@ -208,16 +208,16 @@ def lmhead_leg(steps=5, warmup=2):
     ids = torch.as_tensor(case.ids, device="cuda:0")
     ws = B.workspace(B.DRIFT_OP_LMHEAD, case.T, case.V, B.DRIFT_BF16, "cuda:0",
                      hidden_dim=case.H)
-    out = torch.empty(case.T, dtype=torch.float32, device="cuda:0")
+    lp = torch.empty(case.T, dtype=torch.float32, device="cuda:0")
     for _ in range(warmup):
-        B.lmhead_logprob(case.hidden, case.weight, ids, ws=ws, out=out)
+        B.lmhead_logprob(case.hidden, case.weight, ids, ws=ws, out=lp)
     st, _ = B.drift_get_status(ws)
     if st != B.DRIFT_OK:
         raise RuntimeError(f"lmhead status {B.STATUS_NAMES[st]}")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
-        B.lmhead_logprob(case.hidden, case.weight, ids, ws=ws, out=out)
+        B.lmhead_logprob(case.hidden, case.weight, ids, ws=ws, out=lp)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
@@ -229,6 +229,27 @@ def lmhead_leg(steps=5, warmup=2):
            "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS, "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
            "flop_per_call": flop}
     del ws
+    torch.cuda.empty_cache()
+    # the same call with the weight kept as [V, H] (a linear layer's layout; read in place,
+    # no per-call transpose), bitwise the same outputs
+    w_vh = case.weight.t().contiguous()
+    ws = B.workspace(B.DRIFT_OP_LMHEAD_VH, case.T, case.V, B.DRIFT_BF16, "cuda:0",
+                     hidden_dim=case.H)
+    out_vh = torch.empty_like(lp)
+    for _ in range(warmup):
+        B.lmhead_logprob(case.hidden, w_vh, ids, ws=ws, out=out_vh, weight_layout="vh")
+    e0.record()
+    for _ in range(steps):
+        B.lmhead_logprob(case.hidden, w_vh, ids, ws=ws, out=out_vh, weight_layout="vh")
+    e1.record()
+    torch.cuda.synchronize()
+    vh_ms = e0.elapsed_time(e1) / steps
+    out["weight_vh"] = {"what": "drift_lmhead_logprob_vh: W given as [V, H], read in place",
+                        "ms_per_call": vh_ms, "tflops": flop / (vh_ms * 1e-3) / 1e12,
+                        "frac": flop / (vh_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                        "bitwise_equal_to_hv": bool(torch.equal(out_vh.view(torch.int32),
+                                                                lp.view(torch.int32)))}
+    del ws, w_vh
     torch.cuda.empty_cache()
     # context, not the product path: the plain bf16 GEMM of the same shape through the
     # vendor library (torch.matmul -> hipBLASLt), which writes the logits instead of

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define DRIFT_ABI_VERSION 7
+#define DRIFT_ABI_VERSION 8
 
 /* ---- status codes ---------------------------------------------------------------- */
 #define DRIFT_OK          0
@@ -108,6 +108,7 @@ typedef struct drift_lse_partial {
 #define DRIFT_OP_DIAGNOSTICS      1
 #define DRIFT_OP_LMHEAD           2
 #define DRIFT_OP_ACTIVE_ROWS      3
+#define DRIFT_OP_LMHEAD_VH        4  /* drift_lmhead_logprob_vh */
 
 /*
  * Arguments of drift_selected_logprob. Logical inputs follow "Measurement Contract"
@@ -383,6 +384,19 @@ int drift_active_rows(const uint8_t* active, int64_t num_rows, int32_t* rows, in
 int drift_lmhead_logprob(const void* hidden, const void* weight, int64_t T, int64_t H,
                          int64_t V, const int32_t* target_ids, const uint8_t* active,
                          float* logp, void* ws, size_t ws_bytes, void* stream);
+
+/* drift_lmhead_logprob with the weight stored [V, H] row-major (hidden contiguous: the
+ * layout of a linear layer's [out_features, in_features] weight, as the head's weight is
+ * usually kept), the same head GEMM of "[WS2] Framework for ablation experiment", LogProb
+ * knobs row 9, and the same results bit for bit: the products run over the same K order
+ * on the same values. When H % 64 == 0 the weight is read in place (no transposed copy:
+ * the workspace, drift_workspace_size(DRIFT_OP_LMHEAD_VH, T, V, H, DRIFT_BF16), then
+ * holds only the partials and at most two 256-row tail panels); otherwise it is copied
+ * with K padding. Arguments, alignment, limits and statuses as drift_lmhead_logprob;
+ * weight_vh is bf16 [V, H] with 16-byte aligned rows (H % 8 == 0). */
+int drift_lmhead_logprob_vh(const void* hidden, const void* weight_vh, int64_t T, int64_t H,
+                            int64_t V, const int32_t* target_ids, const uint8_t* active,
+                            float* logp, void* ws, size_t ws_bytes, void* stream);
 
 /* Gradient of the selected-token logprob of one side with respect to its stored logits
  * ("[WS2] Framework for ablation experiment", LogProb knobs row 11: dlogits), for the

@@ -23,7 +23,8 @@ def test_header_declares_the_boundary():
                             "drift_dlogits", "drift_segment_diagnostics",
                             "drift_shard_partials", "drift_merge_shards",
                             "drift_active_rows", "drift_backend_descriptor",
-                            "drift_strerror", "drift_diagnostics_noalloc"])
+                            "drift_strerror", "drift_diagnostics_noalloc",
+                            "drift_lmhead_logprob_vh"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -50,7 +51,7 @@ def test_struct_layouts_match_header():
 def test_descriptor_and_strerror():
     from train_rollout_logprob_amd import binding as B
     d = B.drift_backend_descriptor()
-    assert d["abi_version"] == 7 and d["archs"] == "gfx950"
+    assert d["abi_version"] == 8 and d["archs"] == "gfx950"
     assert "batch composition" in d["determinism"]
     assert d["lse_domain"] == "natural log"
     assert d["build_fingerprint"].startswith("src:")
@@ -73,6 +74,16 @@ def test_workspace_sizes():
     assert f(B.DRIFT_OP_LMHEAD, 16384, 151936, B.DRIFT_BF16, 4100) == 0 # H % 8
     # transposed W + partials: at least H*V*2 bytes
     assert f(B.DRIFT_OP_LMHEAD, 16384, 151936, B.DRIFT_BF16, 4096) >= 4096 * 151936 * 2
+    # [V, H] weight read in place when H % 64 == 0: partials, z and one 256-row tail panel
+    # of W (V % 256 != 0), no transposed copy
+    vh = f(B.DRIFT_OP_LMHEAD_VH, 16384, 151936, B.DRIFT_BF16, 4096)
+    assert 0 < vh < 4096 * 151936 * 2
+    assert vh == f(B.DRIFT_OP_LMHEAD, 16384, 151936, B.DRIFT_BF16, 4096) - \
+        (151936 + 128) * 4096 * 2 + 256 * 4096 * 2
+    # H not a multiple of 64: the weight is copied with K padding as for [H, V]
+    assert f(B.DRIFT_OP_LMHEAD_VH, 300, 1000, B.DRIFT_BF16, 264) == \
+        f(B.DRIFT_OP_LMHEAD, 300, 1000, B.DRIFT_BF16, 264)
+    assert f(B.DRIFT_OP_LMHEAD_VH, 16384, 151936, B.DRIFT_BF16, 4100) == 0
     assert f(9, 10, 10, B.DRIFT_F32) == 0
 
 
@@ -110,6 +121,13 @@ def test_host_checks_fail_closed_without_launching():
     big = 1 << 20                                     # aligned addresses, never dereferenced
     assert lib.drift_lmhead_logprob(big, big, 4, (1 << 22) + 8, 16, big, None, big, big, 1 << 40,
                                     None) == B.DRIFT_EINVAL             # H above 2^22
+    for fn in (lib.drift_lmhead_logprob, lib.drift_lmhead_logprob_vh):
+        assert fn(None, None, 4, 4100, 16, None, None, None, None, 0, None) == B.DRIFT_EINVAL
+        assert fn(big, big, 4, 64, 12, big, None, big, big, 1 << 40, None) == B.DRIFT_EINVAL
+        assert fn(big + 8, big, 4, 64, 16, big, None, big, big, 1 << 40,
+                  None) == B.DRIFT_EINVAL                               # hidden not 16-aligned
+        assert fn(big, big, 4, 64, 16, big, None, big, big, 64,
+                  None) == B.DRIFT_EWORKSPACE                           # workspace too small
     assert lib.drift_get_status(None, None, None) == B.DRIFT_EWORKSPACE
     # vocab_real and transform chains are checked before the workspace
     a.layout, a.num_rows, a.batch, a.seq_len, a.vocab, a.row_stride = B.DRIFT_PAD_RIGHT, 0, 0, 1, 10, 10

@@ -42,6 +42,11 @@ def test_parity_ragged_shapes(T, H, V):
     err = np.abs(logp.cpu().numpy().astype(np.float64) - want)
     print(f"[case] max err {err.max():.3e}", flush=True)
     assert err.max() <= LOGP_TOL
+    # the weight as [V, H] (read in place when H % 64 == 0, else copied with K padding):
+    # the same products in the same K order, so bitwise the [H, V] result
+    w_vh = case.weight.t().contiguous()
+    logp_vh, _ = B.lmhead_logprob(case.hidden, w_vh, ids, check=True, weight_layout="vh")
+    assert torch.equal(logp_vh.view(torch.int32), logp.view(torch.int32))
 
 
 def test_active_mask_and_token_errors():
@@ -93,7 +98,8 @@ def test_batch_composition_control_is_bitwise_zero():
 @pytest.mark.slow
 def test_full_size_sampled_rows_and_invariance():
     """T=16384, H=4096, V=151936 as timed: 256 rows (the first, the last and 254 drawn
-    without replacement) against the oracle, and four rows (including the first and the
+    without replacement) against the oracle, the whole batch with the weight given as
+    [V, H] bitwise equal to the [H, V] call, and four rows (including the first and the
     last) re-scored in batches of 1, 7 and 64."""
     from train_rollout_logprob_amd import binding as B
     case = synth.make_lmhead_case(device="cuda")
@@ -108,6 +114,10 @@ def test_full_size_sampled_rows_and_invariance():
     err = np.abs(full[rows].astype(np.float64) - want)
     print(f"[case] lmhead full max err {err.max():.3e} over {len(rows)} rows", flush=True)
     assert err.max() <= LOGP_TOL
+    w_vh = case.weight.t().contiguous()
+    logp_vh, _ = B.lmhead_logprob(case.hidden, w_vh, ids, check=True, weight_layout="vh")
+    assert torch.equal(logp_vh.view(torch.int32), logp.view(torch.int32))
+    del w_vh, logp_vh
     probe = [0, 1234, 9999, case.T - 1]
     for bs in (1, 7, 64):
         for pr in probe:

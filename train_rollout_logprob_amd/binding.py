@@ -32,6 +32,7 @@ DRIFT_F32, DRIFT_BF16, DRIFT_I32, DRIFT_I64 = 0, 1, 2, 3
 DRIFT_PAD_RIGHT, DRIFT_PAD_LEFT, DRIFT_PACKED = 0, 1, 2
 LAYOUTS = {"right": DRIFT_PAD_RIGHT, "left": DRIFT_PAD_LEFT, "packed": DRIFT_PACKED}
 DRIFT_OP_SELECTED_LOGPROB, DRIFT_OP_DIAGNOSTICS, DRIFT_OP_LMHEAD, DRIFT_OP_ACTIVE_ROWS = 0, 1, 2, 3
+DRIFT_OP_LMHEAD_VH = 4
 DRIFT_XF_SCALE, DRIFT_XF_TEMPERATURE, DRIFT_XF_SOFTCAP = 1, 2, 3
 DRIFT_MAX_TRANSFORMS = 4
 DRIFT_REDUCE_TREE, DRIFT_REDUCE_EXACT = 0, 1
@@ -45,7 +46,7 @@ EXPORTS = ("drift_workspace_size", "drift_selected_logprob", "drift_get_status",
            "drift_diagnostics", "drift_segment_diagnostics", "drift_lmhead_logprob",
            "drift_dlogits", "drift_shard_partials", "drift_merge_shards",
            "drift_active_rows", "drift_backend_descriptor", "drift_strerror",
-           "drift_diagnostics_noalloc")
+           "drift_diagnostics_noalloc", "drift_lmhead_logprob_vh")
 DRIFT_NOALLOC_MAX_ROWS = 1 << 22
 
 
@@ -120,6 +121,8 @@ def _load():
     lib.drift_active_rows.restype = ctypes.c_int
     lib.drift_lmhead_logprob.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]
     lib.drift_lmhead_logprob.restype = ctypes.c_int
+    lib.drift_lmhead_logprob_vh.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]
+    lib.drift_lmhead_logprob_vh.restype = ctypes.c_int
     lib.drift_dlogits.argtypes = [ctypes.POINTER(drift_logprob_args), ctypes.c_int, vp, vp, vp,
                                   ctypes.c_int, vp, i64, vp]
     lib.drift_dlogits.restype = ctypes.c_int
@@ -194,6 +197,13 @@ def drift_lmhead_logprob(hidden, weight, T: int, H: int, V: int, target_ids, act
     return int(lib.drift_lmhead_logprob(_ptr(hidden), _ptr(weight), T, H, V, _ptr(target_ids),
                                         _ptr(active), _ptr(logp), _ptr(ws), ws_bytes,
                                         _stream(stream)))
+
+
+def drift_lmhead_logprob_vh(hidden, weight_vh, T: int, H: int, V: int, target_ids, active, logp,
+                            ws, ws_bytes: int, stream=None) -> int:
+    return int(lib.drift_lmhead_logprob_vh(_ptr(hidden), _ptr(weight_vh), T, H, V,
+                                           _ptr(target_ids), _ptr(active), _ptr(logp), _ptr(ws),
+                                           ws_bytes, _stream(stream)))
 
 
 def drift_dlogits(args: drift_logprob_args, side: int, lse, active, grad_logp, out_dtype: int,
@@ -569,26 +579,34 @@ class ScoringStep:
 
 
 def lmhead_logprob(hidden, weight, ids, active=None, ws=None, out=None, stream=None,
-                   check=False):
-    """Call drift_lmhead_logprob on torch tensors: hidden bf16 [T, H], weight bf16 [H, V],
-    ids int32 [T], active uint8 [T] or None. Returns (logp, ws)."""
+                   check=False, weight_layout="hv"):
+    """Call drift_lmhead_logprob on torch tensors: hidden bf16 [T, H], weight bf16 [H, V]
+    (weight_layout "hv") or [V, H] ("vh": drift_lmhead_logprob_vh, read in place), ids
+    int32 [T], active uint8 [T] or None. Returns (logp, ws)."""
     T, H = hidden.shape
-    H2, V = weight.shape
+    if weight_layout == "hv":
+        H2, V = weight.shape
+        op, fn, name = DRIFT_OP_LMHEAD, drift_lmhead_logprob, "drift_lmhead_logprob"
+    elif weight_layout == "vh":
+        V, H2 = weight.shape
+        op, fn, name = DRIFT_OP_LMHEAD_VH, drift_lmhead_logprob_vh, "drift_lmhead_logprob_vh"
+    else:
+        raise ValueError("weight_layout is 'hv' or 'vh'")
     if H2 != H or hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
-        raise ValueError("hidden [T, H] and weight [H, V] must be bf16 with matching H")
+        raise ValueError("hidden [T, H] and the weight must be bf16 with matching H")
     if not (hidden.is_contiguous() and weight.is_contiguous() and ids.is_contiguous()):
         raise ValueError("hidden, weight and ids must be contiguous")
     if ids.dtype != torch.int32:
         raise ValueError("ids must be int32")
     if ws is None:
-        ws = workspace(DRIFT_OP_LMHEAD, T, V, DRIFT_BF16, hidden.device, hidden_dim=H)
+        ws = workspace(op, T, V, DRIFT_BF16, hidden.device, hidden_dim=H)
     if out is None:
         out = torch.empty(T, dtype=torch.float32, device=hidden.device)
-    st = drift_lmhead_logprob(hidden, weight, T, H, V, ids, active, out, ws, ws.numel(), stream)
+    st = fn(hidden, weight, T, H, V, ids, active, out, ws, ws.numel(), stream)
     if st != DRIFT_OK:
-        raise DriftError(st, "drift_lmhead_logprob")
+        raise DriftError(st, name)
     if check:
         st, _ = drift_get_status(ws, stream)
         if st != DRIFT_OK:
-            raise DriftError(st, "drift_lmhead_logprob (device)")
+            raise DriftError(st, name + " (device)")
     return out, ws

@@ -68,8 +68,9 @@ size_t drift_workspace_size(int op, int64_t num_rows, int64_t vocab, int64_t hid
     case DRIFT_OP_DIAGNOSTICS:
       return diag_ws_bytes(num_rows);
     case DRIFT_OP_LMHEAD:
+    case DRIFT_OP_LMHEAD_VH:
       if (dtype != DRIFT_BF16 || hidden_dim < 1 || hidden_dim % 8 || vocab % 8) return 0;
-      return lmhead_ws_bytes(num_rows, hidden_dim, vocab);
+      return lmhead_ws_bytes(num_rows, hidden_dim, vocab, op == DRIFT_OP_LMHEAD_VH);
     case DRIFT_OP_ACTIVE_ROWS:
       return compact_ws_bytes(num_rows);
     default:
@@ -344,9 +345,13 @@ int drift_active_rows(const uint8_t* active, int64_t num_rows, int32_t* rows, in
              : DRIFT_EHIP;
 }
 
-int drift_lmhead_logprob(const void* hidden, const void* weight, int64_t T, int64_t H, int64_t V,
-                         const int32_t* target_ids, const uint8_t* active, float* logp,
-                         void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int lmhead_call(const void* hidden, const void* weight, bool w_vh, int64_t T, int64_t H,
+                int64_t V, const int32_t* target_ids, const uint8_t* active, float* logp,
+                void* ws, size_t ws_bytes, void* stream) {
   if (T < 0 || T > INT32_MAX || H < 1 || V < 1 || V > INT32_MAX) return DRIFT_EINVAL;
   if (H % 8 != 0 || V % 8 != 0 || H > (int64_t{1} << 22)) return DRIFT_EINVAL;
   if (!lmhead_shape_ok(T, V)) return DRIFT_EINVAL;
@@ -354,11 +359,13 @@ int drift_lmhead_logprob(const void* hidden, const void* weight, int64_t T, int6
   if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(target_ids, 4) ||
       !aligned(logp, 4))
     return DRIFT_EINVAL;
-  if (!ws || !aligned(ws, 256) || ws_bytes < lmhead_ws_bytes(T, H, V)) return DRIFT_EWORKSPACE;
+  if (!ws || !aligned(ws, 256) || ws_bytes < lmhead_ws_bytes(T, H, V, w_vh))
+    return DRIFT_EWORKSPACE;
   LmheadParams lp;
   lp.T = T;
   lp.H = H;
   lp.V = V;
+  lp.w_vh = w_vh;
   lp.hidden = hidden;
   lp.weight = weight;
   lp.ids = target_ids;
@@ -367,6 +374,24 @@ int drift_lmhead_logprob(const void* hidden, const void* weight, int64_t T, int6
   lp.ws = (char*)ws;
   if (launch_lmhead(lp, (hipStream_t)stream) != hipSuccess) return DRIFT_EHIP;
   return DRIFT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int drift_lmhead_logprob(const void* hidden, const void* weight, int64_t T, int64_t H, int64_t V,
+                         const int32_t* target_ids, const uint8_t* active, float* logp,
+                         void* ws, size_t ws_bytes, void* stream) {
+  return lmhead_call(hidden, weight, false, T, H, V, target_ids, active, logp, ws, ws_bytes,
+                     stream);
+}
+
+int drift_lmhead_logprob_vh(const void* hidden, const void* weight_vh, int64_t T, int64_t H,
+                            int64_t V, const int32_t* target_ids, const uint8_t* active,
+                            float* logp, void* ws, size_t ws_bytes, void* stream) {
+  return lmhead_call(hidden, weight_vh, true, T, H, V, target_ids, active, logp, ws, ws_bytes,
+                     stream);
 }
 
 int drift_dlogits(const drift_logprob_args* a, int side, const double* lse,

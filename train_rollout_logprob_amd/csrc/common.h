@@ -113,6 +113,7 @@ hipError_t launch_diagnostics(const DiagParams& p, hipStream_t s);
 
 struct LmheadParams {
   int64_t T, H, V;
+  bool w_vh;  // weight stored [V, H] (K contiguous) instead of [H, V]
   const void* hidden;
   const void* weight;
   const int32_t* ids;
@@ -120,7 +121,7 @@ struct LmheadParams {
   float* logp;
   char* ws;
 };
-size_t lmhead_ws_bytes(int64_t T, int64_t H, int64_t V);
+size_t lmhead_ws_bytes(int64_t T, int64_t H, int64_t V, bool w_vh);
 bool lmhead_shape_ok(int64_t T, int64_t V);  // the GEMM grid fits one dispatch
 hipError_t launch_lmhead(const LmheadParams& p, hipStream_t s);
 

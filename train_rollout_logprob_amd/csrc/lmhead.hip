@@ -1,14 +1,17 @@
 // Fused LM-head selected logprob on the matrix cores.
 //
 // logp[t] = z[t, y_t] - LSE_v(z[t, v]) with z = hidden . W, W stored [H, V] (vocabulary
-// contiguous): the head GEMM of "[WS2] Framework for ablation experiment", LogProb knobs
-// row 9, fused with the online log-sum-exp of row 10, so the logits never reach memory.
+// contiguous) or [V, H] (hidden contiguous, the layout of a linear layer's weight): the
+// head GEMM of "[WS2] Framework for ablation experiment", LogProb knobs row 9, fused with
+// the online log-sum-exp of row 10, so the logits never reach memory.
 //
 // Launches:
 //   lm_init          workspace header;
-//   lm_transpose_w   W [H, V] -> WT [Vp, Hp] (K contiguous, zero padded) in the workspace,
-//                    so both MFMA operands load as 16-byte K-contiguous vectors;
-//   lm_pad_hidden    (only when T or H is not a tile multiple) hidden -> [Tp, Hp], zero pad;
+//   lm_transpose_w   (W [H, V]) W -> WT [Vp, Hp] (K contiguous, zero padded) in the
+//                    workspace, so both MFMA operands load as 16-byte K-contiguous vectors;
+//   lm_pad_rows      (H not a multiple of 64) hidden, or W [V, H], -> [rows, Hp] with K
+//                    padding; and the last 256-row panel of an operand read in place
+//                    when its row count is not a multiple of 256;
 //   lm_gemm_lse      C^T tiles: 256 vocab rows x 256 tokens per block, 4 waves of 128 x 128,
 //                    K = H in steps of 64 through two LDS buffers filled by direct-to-LDS
 //                    loads, v_mfma_f32_32x32x16_bf16 with fp32 accumulation. The epilogue
@@ -59,22 +62,35 @@ struct Partial {  // 16 bytes
   double s;
 };
 
+// Workspace of one call. Both GEMM operands are read as K-contiguous [rows, Hp] panels of
+// 256 rows. W [H, V] is always transposed into `wt` (all Vp rows); W given as [V, H] is
+// read in place when H is a multiple of 64, else copied with K padding into `wt`. Hidden
+// is read in place when H is a multiple of 64, else copied with K padding into `hid`. An
+// operand read in place whose row count is not a multiple of 256 has its last panel copied
+// (rows past the end zero) into a 256-row tail buffer, so that no panel reads past the
+// caller's array.
 struct LmLayout {
   int64_t Vp, Tp, Hp, nVt, nTt;
-  size_t wt_off, hid_off, part_off, zsel_off, total;
-  bool pad_hidden;
-  __host__ __device__ static LmLayout make(int64_t T, int64_t H, int64_t V) {
+  size_t wt_off, hid_off, wtail_off, htail_off, part_off, zsel_off, total;
+  bool copy_w, copy_hidden, w_tail, h_tail;
+  __host__ __device__ static LmLayout make(int64_t T, int64_t H, int64_t V, bool w_vh) {
     LmLayout l;
     l.Vp = (V + kBV - 1) / kBV * kBV;
     l.Tp = (T + kBT - 1) / kBT * kBT;
     l.Hp = (H + kBK - 1) / kBK * kBK;
     l.nVt = l.Vp / kBV;
     l.nTt = l.Tp / kBT;
-    l.pad_hidden = (l.Tp != T) || (l.Hp != H);
+    const bool kpad = l.Hp != H;
+    l.copy_w = !w_vh || kpad;
+    l.copy_hidden = kpad;
+    l.w_tail = !l.copy_w && l.Vp != V;
+    l.h_tail = !l.copy_hidden && l.Tp != T;
+    const size_t panel = (size_t)kBV * l.Hp * 2;
     l.wt_off = 256;
-    l.hid_off = l.wt_off + align_up((size_t)l.Vp * l.Hp * 2, 256);
-    const size_t hid_bytes = l.pad_hidden ? (size_t)l.Tp * l.Hp * 2 : 0;
-    l.part_off = l.hid_off + align_up(hid_bytes, 256);
+    l.hid_off = l.wt_off + (l.copy_w ? align_up((size_t)l.Vp * l.Hp * 2, 256) : 0);
+    l.wtail_off = l.hid_off + (l.copy_hidden ? align_up((size_t)l.Tp * l.Hp * 2, 256) : 0);
+    l.htail_off = l.wtail_off + (l.w_tail ? panel : 0);
+    l.part_off = l.htail_off + (l.h_tail ? panel : 0);
     l.zsel_off = l.part_off + align_up((size_t)l.nVt * l.Tp * sizeof(Partial), 256);
     l.total = l.zsel_off + align_up((size_t)l.Tp * 4, 256);
     return l;
@@ -126,9 +142,11 @@ __global__ void __launch_bounds__(256) lm_transpose_w(const uint16_t* __restrict
   }
 }
 
-__global__ void __launch_bounds__(256) lm_pad_hidden(const uint16_t* __restrict__ hid,
-                                                      uint16_t* __restrict__ out, int64_t T,
-                                                      int64_t H, int64_t Tp, int64_t Hp) {
+// Rows [0, T) of a row-major [T, H] bf16 array into [Tp, Hp], zero padded in both
+// directions (grid-stride over 16-byte groups).
+__global__ void __launch_bounds__(256) lm_pad_rows(const uint16_t* __restrict__ hid,
+                                                   uint16_t* __restrict__ out, int64_t T,
+                                                   int64_t H, int64_t Tp, int64_t Hp) {
   const int64_t nvec = Tp * (Hp / 8);
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nvec;
        i += (int64_t)gridDim.x * 256) {
@@ -156,8 +174,11 @@ __device__ __forceinline__ void tile_of(int64_t b, int64_t nTt_pad, int64_t& vt,
 }
 
 struct GemmArgs {
-  const uint16_t* wt;   // [Vp, Hp]
-  const uint16_t* hid;  // [Tp, Hp] (padded copy) or the caller's [T, H] when no pad
+  const uint16_t* wt;     // W as K-contiguous rows [>= V, Hp]: the transposed or padded copy,
+                          // or the caller's [V, H] weight
+  const uint16_t* hid;    // [>= T, Hp]: the padded copy or the caller's [T, H]
+  const uint16_t* wtail;  // nullable: the last vocab panel (256 rows, zero past V)
+  const uint16_t* htail;  // nullable: the last token panel (256 rows, zero past T)
   int64_t T, V, Hp, nVt, nTt, nVt_pad, nTt_pad, Tp;
   const int32_t* ids;
   Partial* part;        // [nVt, Tp]
@@ -286,8 +307,8 @@ __global__ void __launch_bounds__(kPThreads, 1) lm_gemm_lse(GemmArgs a) {
   const int wv = wave >> 1, wt = wave & 1;
   const int lr = lane & 31, lh = lane >> 5;
   const int64_t v0 = vt * kBV, t0 = tt * kBT;
-  const uint16_t* gA = a.wt + v0 * a.Hp;
-  const uint16_t* gB = a.hid + t0 * a.Hp;
+  const uint16_t* gA = (a.wtail && vt == a.nVt - 1) ? a.wtail : a.wt + v0 * a.Hp;
+  const uint16_t* gB = (a.htail && tt == a.nTt - 1) ? a.htail : a.hid + t0 * a.Hp;
   if (a.T < 0) {  // never taken; keeps the LDS arrays from being treated as never written
     sA0[tid] = sA1[tid] = sB0[tid] = sB1[tid] = 0;
   }
@@ -303,9 +324,9 @@ __global__ void __launch_bounds__(kPThreads, 1) lm_gemm_lse(GemmArgs a) {
       (uint32_t)(((lane >> 3) * a.Hp + (((lane & 7) ^ ((lane >> 4) & 7)) * 8)) * 2),
       (uint32_t)(((lane >> 3) * a.Hp + (((lane & 7) ^ ((4 + (lane >> 4)) & 7)) * 8)) * 2)};
   // The fills go through buffer resources over the block's two operand panels (256 rows x
-  // Hp each; reads past a panel return 0): the per-lane byte offset is one of the two
-  // constants above and the rest is one scalar offset per instruction, so no address
-  // arithmetic or address registers are needed in the loop.
+  // Hp each, all inside the array the panel comes from): the per-lane byte offset is one
+  // of the two constants above and the rest is one scalar offset per instruction, so no
+  // address arithmetic or address registers are needed in the loop.
   const uint32_t panel_bytes = (uint32_t)(kBV * a.Hp * 2);
   const __amdgpu_buffer_rsrc_t rA =
       __builtin_amdgcn_make_buffer_rsrc((void*)gA, (short)0, panel_bytes, 0x00020000);
@@ -491,7 +512,9 @@ __global__ void __launch_bounds__(256) lm_merge(const Partial* __restrict__ part
 
 }  // namespace
 
-size_t lmhead_ws_bytes(int64_t T, int64_t H, int64_t V) { return LmLayout::make(T, H, V).total; }
+size_t lmhead_ws_bytes(int64_t T, int64_t H, int64_t V, bool w_vh) {
+  return LmLayout::make(T, H, V, w_vh).total;
+}
 
 // The GEMM runs one block of kPThreads per (vocab tile, token tile) in one dispatch, which
 // holds at most 2^32 - 1 work-items: T is limited by that (about 7.1M tokens at V = 151936).
@@ -503,24 +526,51 @@ bool lmhead_shape_ok(int64_t T, int64_t V) {
 }
 
 hipError_t launch_lmhead(const LmheadParams& p, hipStream_t s) {
-  const LmLayout l = LmLayout::make(p.T, p.H, p.V);
+  const LmLayout l = LmLayout::make(p.T, p.H, p.V, p.w_vh);
   hipLaunchKernelGGL(lm_init, dim3(1), dim3(64), 0, s, p.ws);
   if (p.T == 0) return hipGetLastError();
-  uint16_t* wt = (uint16_t*)(p.ws + l.wt_off);
-  hipLaunchKernelGGL(lm_transpose_w, dim3((unsigned)(l.Vp / 64), (unsigned)(l.Hp / 64)), dim3(256),
-                     0, s, (const uint16_t*)p.weight, wt, p.H, p.V, l.Hp);
-  const uint16_t* hid = (const uint16_t*)p.hidden;
-  if (l.pad_hidden) {
-    uint16_t* hp = (uint16_t*)(p.ws + l.hid_off);
-    const int64_t nvec = l.Tp * (l.Hp / 8);
+  // rows [0, rows) of src [rows, H] into dst [rows_p, Hp], zero padded (grid-stride)
+  auto pad_copy = [&](const uint16_t* src, uint16_t* dst, int64_t rows, int64_t rows_p) {
+    const int64_t nvec = rows_p * (l.Hp / 8);
     const unsigned blocks = (unsigned)((nvec + 255) / 256 < 65536 ? (nvec + 255) / 256 : 65536);
-    hipLaunchKernelGGL(lm_pad_hidden, dim3(blocks), dim3(256), 0, s, hid, hp, p.T, p.H, l.Tp,
+    hipLaunchKernelGGL(lm_pad_rows, dim3(blocks), dim3(256), 0, s, src, dst, rows, p.H, rows_p,
                        l.Hp);
-    hid = hp;
+  };
+  const uint16_t* wt = (const uint16_t*)p.weight;
+  if (l.copy_w) {
+    uint16_t* w = (uint16_t*)(p.ws + l.wt_off);
+    if (p.w_vh)
+      pad_copy((const uint16_t*)p.weight, w, p.V, l.Vp);
+    else
+      hipLaunchKernelGGL(lm_transpose_w, dim3((unsigned)(l.Vp / 64), (unsigned)(l.Hp / 64)),
+                         dim3(256), 0, s, (const uint16_t*)p.weight, w, p.H, p.V, l.Hp);
+    wt = w;
+  }
+  const uint16_t* hid = (const uint16_t*)p.hidden;
+  if (l.copy_hidden) {
+    uint16_t* h = (uint16_t*)(p.ws + l.hid_off);
+    pad_copy(hid, h, p.T, l.Tp);
+    hid = h;
+  }
+  const uint16_t* wtail = nullptr;
+  const uint16_t* htail = nullptr;
+  if (l.w_tail) {
+    uint16_t* d = (uint16_t*)(p.ws + l.wtail_off);
+    const int64_t r0 = (l.nVt - 1) * kBV;
+    pad_copy(wt + r0 * l.Hp, d, p.V - r0, kBV);
+    wtail = d;
+  }
+  if (l.h_tail) {
+    uint16_t* d = (uint16_t*)(p.ws + l.htail_off);
+    const int64_t r0 = (l.nTt - 1) * kBT;
+    pad_copy(hid + r0 * l.Hp, d, p.T - r0, kBT);
+    htail = d;
   }
   GemmArgs g;
   g.wt = wt;
   g.hid = hid;
+  g.wtail = wtail;
+  g.htail = htail;
   g.T = p.T;
   g.V = p.V;
   g.Hp = l.Hp;
