@@ -12,7 +12,8 @@
 //   lm_pad_rows      (H not a multiple of 64) hidden, or W [V, H], -> [rows, Hp] with K
 //                    padding; and the last 256-row panel of an operand read in place
 //                    when its row count is not a multiple of 256;
-//   lm_gemm_lse      C^T tiles: 256 vocab rows x 256 tokens per block, 4 waves of 128 x 128,
+//   lm_gemm_lse      C^T tiles: 256 vocab rows x 256 tokens per block, 8 waves (two per
+//                    SIMD) of 128 vocab rows x 64 tokens,
 //                    K = H in steps of 64 through two LDS buffers filled by direct-to-LDS
 //                    loads, v_mfma_f32_32x32x16_bf16 with fp32 accumulation. The epilogue
 //                    turns each token's 256 logits into a (k, s) log-sum-exp partial and
@@ -41,10 +42,13 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBV = 256;        // vocab rows per block (MFMA M)
 constexpr int kBT = 256;        // tokens per block (MFMA N)
 constexpr int kBK = 64;         // K per LDS stage
-constexpr int kPW = 128;        // rows (vocab) and tokens per wave: a 2 x 2 wave grid
-constexpr int kPT = kPW / 32;   // 32x32 MFMA tiles per wave along each side
-constexpr int kPThreads = 256;
-static_assert(kBV == kBT && kBK == 64 && kBV == 2 * kPW, "tile shape");
+constexpr int kPW = 128;        // vocab rows per wave: 2 vocab waves
+constexpr int kPN = 64;         // tokens per wave: 4 token waves
+constexpr int kPT = kPW / 32;   // 32x32 MFMA tiles per wave along the vocab
+constexpr int kPU = kPN / 32;   // and along the tokens
+constexpr int kPWaves = 8;      // two waves per SIMD
+constexpr int kPThreads = 64 * kPWaves;
+static_assert(kBV == kBT && kBK == 64 && kBV == 2 * kPW && kBT == 4 * kPN, "tile shape");
 #ifndef DRIFT_LM_GROUP_V
 #define DRIFT_LM_GROUP_V 16
 #endif
@@ -281,11 +285,12 @@ __device__ __forceinline__ void lse_epilogue(const f32x16 (&acc)[TM][TN], const 
   }
 }
 
-// The head GEMM with its LSE epilogue. 4 waves (one per SIMD) in a 2 x 2 grid each compute
-// 128 vocab rows x 128 tokens (4 x 4 MFMA tiles, accumulators in the AGPRs). Within a K
-// stage the four 16-wide steps are interleaved by hand with the memory work: the MFMAs of
-// a step run while the next step's fragments are read from LDS into the other register
-// set. The stage tiles move from global memory into
+// The head GEMM with its LSE epilogue. 8 waves, two per SIMD (waves w and w + 4 share one),
+// in a 2 (vocab) x 4 (tokens) grid each compute 128 vocab rows x 64 tokens (4 x 2 MFMA
+// tiles, 128 accumulators). Within a K stage the four 16-wide steps are interleaved by hand
+// with the memory work: the MFMAs of a step run while the next step's fragments are read
+// from LDS into the other register set, and while one wave of a SIMD waits the other's
+// MFMAs can issue. The stage tiles move from global memory into
 // LDS with buffer_load_dwordx4 ... lds (lane l of an instruction fills bytes [16 l, 16 l + 16)
 // of a 1 KB LDS span, checked on the GPU), so no VGPRs hold them and the LDS fills count
 // on vmcnt while the fragment reads alone count on lgkmcnt. Rows are 128 bytes without
@@ -298,13 +303,13 @@ __global__ void __launch_bounds__(kPThreads, 1) lm_gemm_lse(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t sA1[kBV * kBK];
   __shared__ __attribute__((aligned(1024))) uint16_t sB0[kBT * kBK];
   __shared__ __attribute__((aligned(1024))) uint16_t sB1[kBT * kBK];
-  __shared__ float s_k[2][kPW];
-  __shared__ double s_s[2][kPW];
+  __shared__ float s_k[4][kPN];
+  __shared__ double s_s[4][kPN];
   int64_t vt, tt;
   tile_of(blockIdx.x, a.nTt_pad, vt, tt);
   if (vt >= a.nVt || tt >= a.nTt) return;  // block-uniform
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wv = wave >> 1, wt = wave & 1;
+  const int wv = wave >> 2, wt = wave & 3;
   const int lr = lane & 31, lh = lane >> 5;
   const int64_t v0 = vt * kBV, t0 = tt * kBT;
   const uint16_t* gA = (a.wtail && vt == a.nVt - 1) ? a.wtail : a.wt + v0 * a.Hp;
@@ -313,7 +318,7 @@ __global__ void __launch_bounds__(kPThreads, 1) lm_gemm_lse(GemmArgs a) {
     sA0[tid] = sA1[tid] = sB0[tid] = sB1[tid] = 0;
   }
 
-  // LDS fills: wave w moves the 8-row blocks 8w .. 8w + 7 of both tiles. Lane l of an
+  // LDS fills: wave w moves the 8-row blocks 4w .. 4w + 3 of both tiles. Lane l of an
   // instruction for rows r0 .. r0 + 7 takes row r0 + l / 8 and stored chunk l % 8, i.e.
   // logical chunk (l % 8) ^ ((r0 / 2 + l / 16) & 7).
   // The stored chunk of a lane depends on the 8-row block only through its parity (r0 / 2
@@ -332,64 +337,65 @@ __global__ void __launch_bounds__(kPThreads, 1) lm_gemm_lse(GemmArgs a) {
       __builtin_amdgcn_make_buffer_rsrc((void*)gA, (short)0, panel_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rB =
       __builtin_amdgcn_make_buffer_rsrc((void*)gB, (short)0, panel_bytes, 0x00020000);
-  // one operand's share of a stage: this wave's 8 blocks of 8 rows (8 instructions of 1 KB)
+  // one operand's share of a stage: this wave's 4 blocks of 8 rows (4 instructions of 1 KB)
   auto fill = [&](const __amdgpu_buffer_rsrc_t& r, uint16_t* d, int64_t k0) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r0 = (wave_u * 8 + j) * 8;
+    for (int j = 0; j < 4; ++j) {
+      const int r0 = (wave_u * 4 + j) * 8;
       const uint32_t so = (uint32_t)(((int64_t)r0 * a.Hp + k0) * 2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(d + r0 * kBK), 16, lane_off[j & 1],
                                                so, 0, 0);
     }
   };
 
-  f32x16 acc[kPT][kPT];
+  f32x16 acc[kPT][kPU];
 #pragma unroll
   for (int i = 0; i < kPT; ++i)
 #pragma unroll
-    for (int j = 0; j < kPT; ++j)
+    for (int j = 0; j < kPU; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  bf16x8 fa[2][kPT], fb[2][kPT];
+  bf16x8 fa[2][kPT], fb[2][kPU];
   const int swz = (lr >> 1) & 7;  // rows 128 wv + 32 i + lr share ((row >> 1) & 7)
   auto fread = [&](const uint16_t* bA, const uint16_t* bB, int kk, int set) {
     const int ch = (2 * kk + lh) ^ swz;
 #pragma unroll
-    for (int i = 0; i < kPT; ++i) {
+    for (int i = 0; i < kPT; ++i)
       fa[set][i] = *(const bf16x8*)(bA + (kPW * wv + 32 * i + lr) * kBK + ch * 8);
-      fb[set][i] = *(const bf16x8*)(bB + (kPW * wt + 32 * i + lr) * kBK + ch * 8);
-    }
+#pragma unroll
+    for (int i = 0; i < kPU; ++i)
+      fb[set][i] = *(const bf16x8*)(bB + (kPN * wt + 32 * i + lr) * kBK + ch * 8);
   };
   auto mfmas = [&](int set) {
 #pragma unroll
     for (int i = 0; i < kPT; ++i)
 #pragma unroll
-      for (int j = 0; j < kPT; ++j)
+      for (int j = 0; j < kPU; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j],
                                                             0, 0, 0);
   };
   // the next step's fragment reads go out early in the step, one after each MFMA
   auto interleave_reads = [&]() {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 6; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
 
   // Stage kt reads the buffers of parity kt % 2: steps 0-2 read the next step's fragments;
   // then this wave's fills of stage kt + 1 are awaited and the block barrier makes every
   // fill visible and every read of this stage's buffers done; step 3 reads the first
-  // fragments of stage kt + 1. A stage's fills go out in two halves of 8 instructions per
+  // fragments of stage kt + 1. A stage's fills go out in two halves of 4 instructions per
   // wave, each interleaved one per MFMA pair with a step: the W half of stage kt + 2 in step 3
   // of stage kt (into this stage's buffer, free after the barrier), the hidden half of
   // stage kt + 1 in step 0 of stage kt (into the other buffer, free since the barrier of
-  // stage kt - 1). Issuing all 16 in one step queued them behind the 4 waves' address
-  // units for about twice the step's length, and the MFMAs behind them in program order
-  // waited (the split measured 5-6 % faster per call, bitwise the same). The last stages
+  // stage kt - 1). Issuing a whole stage's fills in one step queued them behind the CU's
+  // address unit for about twice the step's length, and the MFMAs behind them in program
+  // order waited (the split measured 5-6 % faster per call, bitwise the same). The last stages
   // re-fill with the last stage's data, which nobody reads; stage 0 re-fills the hidden
   // half of stage 1 with the data the prologue put there.
   const int64_t nk = a.Hp / kBK;
@@ -400,8 +406,16 @@ __global__ void __launch_bounds__(kPThreads, 1) lm_gemm_lse(GemmArgs a) {
     fread(cA, cB, 1, 1);
     fill(rB, nB, k1);
     mfmas(0);
+    // per MFMA pair: one or two fragment reads, one fill
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {  // per MFMA pair: one fragment read, one fill
+    for (int i = 0; i < 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -420,7 +434,14 @@ __global__ void __launch_bounds__(kPThreads, 1) lm_gemm_lse(GemmArgs a) {
     fill(rA, const_cast<uint16_t*>(cA), k2);
     mfmas(1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -446,9 +467,9 @@ __global__ void __launch_bounds__(kPThreads, 1) lm_gemm_lse(GemmArgs a) {
   __syncthreads();
 
   if (v0 + kBV <= a.V)  // block-uniform
-    lse_epilogue<kPT, kPT, kPW, kPW, true>(acc, a, vt, v0, t0, wv, wt, lr, lh, s_k, s_s);
+    lse_epilogue<kPT, kPU, kPW, kPN, true>(acc, a, vt, v0, t0, wv, wt, lr, lh, s_k, s_s);
   else
-    lse_epilogue<kPT, kPT, kPW, kPW, false>(acc, a, vt, v0, t0, wv, wt, lr, lh, s_k, s_s);
+    lse_epilogue<kPT, kPU, kPW, kPN, false>(acc, a, vt, v0, t0, wv, wt, lr, lh, s_k, s_s);
 }
 
 // Four lanes per token: lane q folds the vocab tiles [q*c, (q+1)*c) in ascending order
