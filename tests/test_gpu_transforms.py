@@ -33,6 +33,11 @@ CHAINS = {
                [("scale", 2.0), ("softcap", 30.0), ("temperature", 1.5)]),
     "per_side": (None, [("temperature", 0.9)]),
     "order_swapped": ([("scale", 3.0), ("softcap", 10.0)], [("softcap", 10.0), ("scale", 3.0)]),
+    # saturating soft-cap: most logits end near +-5 (the folded form's g near 0 and 1)
+    "softcap_saturating": ([("scale", 8.0), ("softcap", 5.0)], [("scale", 8.0), ("softcap", 5.0)]),
+    # a cap above the folded form's bound, and two soft-cap steps: the step-by-step chain
+    "softcap_wide": ([("softcap", 60.0)], [("softcap", 60.0)]),
+    "two_softcaps": ([("softcap", 30.0), ("softcap", 20.0)], [("softcap", 25.0)]),
 }
 
 

@@ -51,6 +51,36 @@ Chain make_chain(const drift_transform& t) {
     c.inv[i] = (float)(1.0 / (double)v);
     c.v[i] = (used && t.op[i] == DRIFT_XF_TEMPERATURE) ? c.inv[i] : v;
   }
+  // the folded form (rowio.h): factors before and after the one soft-cap step, in fp64
+  const double log2e = 1.44269504088896340736;
+  int nsoft = 0;
+  double pre = 1.0, post = 1.0, cap = 1.0;
+  for (int i = 0; i < t.count; ++i) {
+    if (t.op[i] == DRIFT_XF_SOFTCAP) {
+      ++nsoft;
+      cap = (double)t.value[i];
+      continue;
+    }
+    const double f = t.op[i] == DRIFT_XF_TEMPERATURE ? 1.0 / (double)t.value[i]
+                                                     : (double)t.value[i];
+    (nsoft == 0 ? pre : post) *= f;
+  }
+  c.kind = nsoft == 0 ? 1 : (nsoft == 1 ? 2 : 0);
+  const double fa = nsoft == 0 ? 0.0 : post * cap;
+  const double fb = nsoft == 0 ? pre : -2.0 * post * cap;
+  c.fc = nsoft == 1 ? (float)(2.0 * log2e * pre / cap) : 0.0f;
+  c.fa = (float)fa;
+  c.fb = (float)fb;
+  c.fal = (float)(fa * log2e);
+  c.fbl = (float)(fb * log2e);
+  // factors whose folded form leaves the fp32 range keep the step-by-step chain
+  const float f[5] = {c.fc, c.fa, c.fb, c.fal, c.fbl};
+  for (float x : f)
+    if (!(fabsf(x) < INFINITY)) c.kind = 0;
+  if (c.kind == 2 && !(fabsf(c.fc) >= 1.17549435e-38f)) c.kind = 0;  // fc not a normal float
+  // g carries at most 3.6e-7 |fa| of error into z (one-ulp exp2 and reciprocal); above
+  // |fa| = 40 that would exceed 1.5e-5 and the chain is applied step by step instead
+  if (c.kind == 2 && !(fabsf(c.fa) <= 40.0f)) c.kind = 0;
   return c;
 }
 

@@ -45,6 +45,23 @@ namespace {
 
 constexpr float kRaise = 16.0f;  // a group sum at or above this raises the wave's k
 
+// A group's values as the log-sum-exp reads them, with z(i) the logit and expo(i, base(nk))
+// the exponent z log2e - k for nk = -k: the logits themselves (Plain), or the values g of a
+// folded chain with z = fa + fb g (Folded; rowio.h), whose exponent is one FMA of g.
+template <int VEC> struct Plain {
+  const float (&x)[VEC];
+  __device__ __forceinline__ float z(int i) const { return x[i]; }
+  __device__ __forceinline__ float base(float nk) const { return nk; }
+  __device__ __forceinline__ float expo(int i, float c) const { return fmaf(x[i], kLog2e, c); }
+};
+template <int VEC> struct Folded {
+  const float (&g)[VEC];
+  const Chain& ch;
+  __device__ __forceinline__ float z(int i) const { return fmaf(ch.fb, g[i], ch.fa); }
+  __device__ __forceinline__ float base(float nk) const { return ch.fal + nk; }
+  __device__ __forceinline__ float expo(int i, float c) const { return fmaf(g[i], ch.fbl, c); }
+};
+
 // exp2 terms of one group in fp32, summed pairwise; with ENT also the first moment of
 // the exponent, sum of 2^a * a over the group (a = x*log2e - k) as a chain of fp32 FMAs in
 // element order; -inf exponents contribute 0. The moment is first taken without a guard: a
@@ -52,13 +69,14 @@ constexpr float kRaise = 16.0f;  // a group sum at or above this raises the wave
 // take it again with the exponent clamped to -1e30. Both give the same bits wherever the
 // first is not NaN (a term with a below -1e30 has 2^a = 0 and adds a signed zero to the
 // chain either way).
-template <int VEC, bool ENT>
-__device__ __forceinline__ void group_sums(const float (&x)[VEC], float nk, float& t, float& t2) {
+template <int VEC, bool ENT, typename G>
+__device__ __forceinline__ void group_sums(const G& grp, float nk, float& t, float& t2) {
+  const float c = grp.base(nk);
   float e[VEC];
   float w = 0.0f;
 #pragma unroll
   for (int i = 0; i < VEC; ++i) {
-    const float a = fmaf(x[i], kLog2e, nk);
+    const float a = grp.expo(i, c);
     e[i] = __builtin_amdgcn_exp2f(a);
     if constexpr (ENT) w = fmaf(e[i], a, w);
   }
@@ -66,7 +84,7 @@ __device__ __forceinline__ void group_sums(const float (&x)[VEC], float nk, floa
     if (w != w) {
       w = 0.0f;
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) w = fmaf(e[i], fmaxf(fmaf(x[i], kLog2e, nk), -1.0e30f), w);
+      for (int i = 0; i < VEC; ++i) w = fmaf(e[i], fmaxf(grp.expo(i, c), -1.0e30f), w);
     }
   }
 #pragma unroll
@@ -87,15 +105,15 @@ __device__ __forceinline__ float wave_max(float m) {
 // Adds one group of VEC logits to a lane's partial (Acc, or AccE with the entropy moment).
 // Every lane of the wave calls it at the same point (groups past the end of the row are all
 // -inf), so k stays wave-uniform.
-template <int VEC, typename A>
-__device__ __forceinline__ void push(A& a, const float (&x)[VEC]) {
+template <int VEC, typename A, typename G>
+__device__ __forceinline__ void push_group(A& a, const G& grp) {
   constexpr bool ENT = std::is_same<A, AccE>::value;
   float t, t2;
-  group_sums<VEC, ENT>(x, -a.k, t, t2);
+  group_sums<VEC, ENT>(grp, -a.k, t, t2);
   if (__ballot(!(t < kRaise))) {  // wave-uniform: raise k
-    float m = x[0];
+    float m = grp.z(0);
 #pragma unroll
-    for (int i = 1; i < VEC; ++i) m = fmaxf(m, x[i]);
+    for (int i = 1; i < VEC; ++i) m = fmaxf(m, grp.z(i));
     m = wave_max(m);  // NaN-ignoring; -inf if every logit in the wave's group is -inf/NaN
     const float kn = ceilf(m * kLog2e);
     if (kn > a.k) {
@@ -113,14 +131,19 @@ __device__ __forceinline__ void push(A& a, const float (&x)[VEC]) {
       t = 0.0f;
 #pragma unroll
       for (int i = 0; i < VEC; ++i)
-        if (!(x[i] == -INFINITY)) t = NAN;
+        if (!(grp.z(i) == -INFINITY)) t = NAN;
       t2 = t;
     } else {
-      group_sums<VEC, ENT>(x, -a.k, t, t2);
+      group_sums<VEC, ENT>(grp, -a.k, t, t2);
     }
   }
   a.s += (double)t;
   if constexpr (ENT) a.s2 += (double)t2;
+}
+
+template <int VEC, typename A>
+__device__ __forceinline__ void push(A& a, const float (&x)[VEC]) {
+  push_group<VEC>(a, Plain<VEC>{x});
 }
 
 // Exact mode: one group's integer pieces into the lane's bins. The window top is raised
@@ -146,7 +169,7 @@ __device__ __forceinline__ void push(AccX& a, const float (&x)[VEC]) {
 // -inf) belongs to the lane that would own group V / VEC. All lanes run the same number
 // of pushes (missing groups are all -inf and add exactly 0). U groups per side are
 // loaded ahead for memory-level parallelism; U does not change the arithmetic.
-template <typename T, int NT, int U, bool kAligned, bool XF, typename A>
+template <typename T, int NT, int U, bool kAligned, int XF, typename A>
 __device__ __forceinline__ void stream_row(const char* rt, const char* rr, int64_t V, int tid,
                                            A& at, A& ar, const ScoreParams& p) {
   constexpr int VEC = Elem<T>::kVec;
@@ -169,12 +192,21 @@ __device__ __forceinline__ void stream_row(const char* rt, const char* rr, int64
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         float x[VEC];
-        Elem<T>::unpack(bt[u], x);
-        if constexpr (XF) apply_chain<VEC>(x, p.xf[0]);
-        push<VEC>(at, x);
-        Elem<T>::unpack(br[u], x);
-        if constexpr (XF) apply_chain<VEC>(x, p.xf[1]);
-        push<VEC>(ar, x);
+        if constexpr (XF == 2) {  // both chains folded: the terms from g (rowio.h)
+          Elem<T>::unpack(bt[u], x);
+          fold_values<VEC>(x, p.xf[0]);
+          push_group<VEC>(at, Folded<VEC>{x, p.xf[0]});
+          Elem<T>::unpack(br[u], x);
+          fold_values<VEC>(x, p.xf[1]);
+          push_group<VEC>(ar, Folded<VEC>{x, p.xf[1]});
+        } else {
+          Elem<T>::unpack(bt[u], x);
+          if constexpr (XF == 1) apply_chain<VEC>(x, p.xf[0]);
+          push<VEC>(at, x);
+          Elem<T>::unpack(br[u], x);
+          if constexpr (XF == 1) apply_chain<VEC>(x, p.xf[1]);
+          push<VEC>(ar, x);
+        }
       }
     }
   }
@@ -192,7 +224,15 @@ __device__ __forceinline__ void stream_row(const char* rt, const char* rr, int64
         xr[e] = (i < V) ? Elem<T>::load1(rr, i) : 0.0f;
       }
     }
-    if constexpr (XF) {
+    if constexpr (XF == 2) {  // the folded chain's logits, z = fa + fb g
+      fold_values<VEC>(xt, p.xf[0]);
+      fold_values<VEC>(xr, p.xf[1]);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        xt[e] = fmaf(p.xf[0].fb, xt[e], p.xf[0].fa);
+        xr[e] = fmaf(p.xf[1].fb, xr[e], p.xf[1].fa);
+      }
+    } else if constexpr (XF == 1) {
       apply_chain<VEC>(xt, p.xf[0]);
       apply_chain<VEC>(xr, p.xf[1]);
     }
@@ -237,7 +277,7 @@ __global__ void __launch_bounds__(256) init_header(ScoreParams p) {
 
 // One block per row: thread 0 classifies and validates the row; active rows with a valid
 // id are streamed by the whole block.
-template <typename T, int NT, int U, bool XF, bool ENT>
+template <typename T, int NT, int U, int XF, bool ENT>
 __global__ void __launch_bounds__(NT) score_rows(ScoreParams p) {
   using A = std::conditional_t<ENT, AccE, Acc>;
   constexpr int NW = NT / 64;
@@ -586,23 +626,28 @@ hipError_t launch_score(const ScoreParams& p, hipStream_t s, hipEvent_t ev0, hip
   if (e != hipSuccess) return e;
   if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
   if (p.N > 0) {
-    const bool xf = p.xf[0].n > 0 || p.xf[1].n > 0;
+    // chains: none (0), step by step (1), or both folded (2, rowio.h)
+    const int xf = !(p.xf[0].n > 0 || p.xf[1].n > 0) ? 0
+                   : (p.xf[0].kind != 0 && p.xf[1].kind != 0) ? 2 : 1;
     const bool ent = p.ent[0] != nullptr || p.ent[1] != nullptr;
     constexpr int NB = DRIFT_SCORE_THREADS_BF16, UB = DRIFT_SCORE_UNROLL_BF16;
     constexpr int NF = DRIFT_SCORE_THREADS_F32, UF = DRIFT_SCORE_UNROLL_F32;
 #define DRIFT_SCORE_LAUNCH(T, NT, U, X, E) \
   launch_over_rows(score_rows<T, NT, U, X, E>, p, NT, s)
+#define DRIFT_SCORE_LAUNCH_XF(T, NT, U, E)              \
+  do {                                                  \
+    if (xf == 2) DRIFT_SCORE_LAUNCH(T, NT, U, 2, E);    \
+    else if (xf == 1) DRIFT_SCORE_LAUNCH(T, NT, U, 1, E); \
+    else DRIFT_SCORE_LAUNCH(T, NT, U, 0, E);            \
+  } while (0)
     if (p.dtype == DRIFT_BF16) {
-      if (xf && ent) DRIFT_SCORE_LAUNCH(uint16_t, NB, UB, true, true);
-      else if (xf) DRIFT_SCORE_LAUNCH(uint16_t, NB, UB, true, false);
-      else if (ent) DRIFT_SCORE_LAUNCH(uint16_t, NB, UB, false, true);
-      else DRIFT_SCORE_LAUNCH(uint16_t, NB, UB, false, false);
+      if (ent) DRIFT_SCORE_LAUNCH_XF(uint16_t, NB, UB, true);
+      else DRIFT_SCORE_LAUNCH_XF(uint16_t, NB, UB, false);
     } else {
-      if (xf && ent) DRIFT_SCORE_LAUNCH(float, NF, UF, true, true);
-      else if (xf) DRIFT_SCORE_LAUNCH(float, NF, UF, true, false);
-      else if (ent) DRIFT_SCORE_LAUNCH(float, NF, UF, false, true);
-      else DRIFT_SCORE_LAUNCH(float, NF, UF, false, false);
+      if (ent) DRIFT_SCORE_LAUNCH_XF(float, NF, UF, true);
+      else DRIFT_SCORE_LAUNCH_XF(float, NF, UF, false);
     }
+#undef DRIFT_SCORE_LAUNCH_XF
 #undef DRIFT_SCORE_LAUNCH
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

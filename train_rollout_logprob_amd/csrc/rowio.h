@@ -44,12 +44,39 @@ template <> struct Elem<uint16_t> {  // bf16 bit patterns
 // One side's transform chain as the kernels read it: steps in order, each multiplying by
 // v (SCALE: the value, TEMPERATURE: its reciprocal) or, for SOFTCAP, x -> v * tanh(x * inv)
 // with inv = 1 / v.
+//
+// The same chain folded into one step for the log-sum-exp terms of the streaming kernel
+// (kind != 0): z = fa + fb * g(x), with
+//   kind 1 (multiplying steps only): g(x) = x, fa = 0, fb = the product of the factors;
+//   kind 2 (one SOFTCAP step of value c, factor p before it and q after it):
+//     g(x) = 1 / (1 + 2^(fc * x)), fc = 2 log2(e) p / c, fa = q c, fb = -2 q c,
+//   from tanh(u) = 1 - 2 / (e^(2u) + 1) (the logistic form of tanh), so that
+//   q c tanh(p x / c) = fa + fb g(x); g takes one hardware exp2 and one reciprocal, and
+//   fa + fb g is within 3.6e-7 |fa| of the exact value (measured over every bf16 input
+//   with both instructions off by one ulp either way); used when |fa| <= 40;
+//   kind 0: two or more SOFTCAP steps, or a fold out of those bounds (no fold).
+// The selected logit always takes the step-by-step chain (apply_chain).
+// fal = fa log2(e) and fbl = fb log2(e) make the exponent z log2(e) - k one FMA of g.
 struct Chain {
   int32_t n;
   int32_t op[DRIFT_MAX_TRANSFORMS];
   float v[DRIFT_MAX_TRANSFORMS];
   float inv[DRIFT_MAX_TRANSFORMS];
+  int32_t kind;
+  float fc, fa, fb, fal, fbl;
 };
+
+// g(x) of the folded chain, in place (kind 1: unchanged). The chain is a kernel argument,
+// so the branch is uniform. 2^(fc x) overflows to +inf for large fc x, and g is then 0:
+// the soft-cap's saturation; x = -inf gives g = 1.
+template <int VEC>
+__device__ __forceinline__ void fold_values(float (&x)[VEC], const Chain& c) {
+  if (c.kind == 2) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+      x[e] = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(x[e] * c.fc) + 1.0f);
+  }
+}
 
 // Applies the chain to a group in place. Branches are uniform (the chain is a kernel
 // argument).
