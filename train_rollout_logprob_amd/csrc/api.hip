@@ -81,6 +81,7 @@ Chain make_chain(const drift_transform& t) {
   // g carries at most 3.6e-7 |fa| of error into z (one-ulp exp2 and reciprocal); above
   // |fa| = 40 that would exceed 1.5e-5 and the chain is applied step by step instead
   if (c.kind == 2 && !(fabsf(c.fa) <= 40.0f)) c.kind = 0;
+  c.kfix = (float)(ceil(fabs((double)c.fa) * log2e) + 1.0);
   return c;
 }
 

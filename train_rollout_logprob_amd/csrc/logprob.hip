@@ -146,6 +146,17 @@ __device__ __forceinline__ void push(A& a, const float (&x)[VEC]) {
   push_group<VEC>(a, Plain<VEC>{x});
 }
 
+// A group of a folded soft-cap chain (kind 2) with the fixed offset k = kfix: every term is
+// within [2^-118, 2^-1], so there is nothing to raise; a NaN value makes the sum NaN.
+template <int VEC, typename A, typename G>
+__device__ __forceinline__ void push_fixed(A& a, const G& grp) {
+  constexpr bool ENT = std::is_same<A, AccE>::value;
+  float t, t2;
+  group_sums<VEC, ENT>(grp, -a.k, t, t2);
+  a.s += (double)t;
+  if constexpr (ENT) a.s2 += (double)t2;
+}
+
 // Exact mode: one group's integer pieces into the lane's bins. The window top is raised
 // for the whole wave at once (ballot + max), as k is in the fixed-tree mode.
 template <int VEC>
@@ -178,6 +189,10 @@ __device__ __forceinline__ void stream_row(const char* rt, const char* rr, int64
   const int64_t full_iters = nfull / NT;              // iterations where every lane is full
   const int64_t iters = (ngroups + NT - 1) / NT;
   int64_t j = 0;
+  if constexpr (XF == 2) {  // a folded soft-cap side starts at its fixed offset (rowio.h)
+    if (p.xf[0].kind == 2) at.k = p.xf[0].kfix;
+    if (p.xf[1].kind == 2) ar.k = p.xf[1].kfix;
+  }
   if constexpr (kAligned) {
     const u32x4* vt = (const u32x4*)rt;
     const u32x4* vr = (const u32x4*)rr;
@@ -195,10 +210,16 @@ __device__ __forceinline__ void stream_row(const char* rt, const char* rr, int64
         if constexpr (XF == 2) {  // both chains folded: the terms from g (rowio.h)
           Elem<T>::unpack(bt[u], x);
           fold_values<VEC>(x, p.xf[0]);
-          push_group<VEC>(at, Folded<VEC>{x, p.xf[0]});
+          if (p.xf[0].kind == 2)
+            push_fixed<VEC>(at, Folded<VEC>{x, p.xf[0]});
+          else
+            push_group<VEC>(at, Folded<VEC>{x, p.xf[0]});
           Elem<T>::unpack(br[u], x);
           fold_values<VEC>(x, p.xf[1]);
-          push_group<VEC>(ar, Folded<VEC>{x, p.xf[1]});
+          if (p.xf[1].kind == 2)
+            push_fixed<VEC>(ar, Folded<VEC>{x, p.xf[1]});
+          else
+            push_group<VEC>(ar, Folded<VEC>{x, p.xf[1]});
         } else {
           Elem<T>::unpack(bt[u], x);
           if constexpr (XF == 1) apply_chain<VEC>(x, p.xf[0]);

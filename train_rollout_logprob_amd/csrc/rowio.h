@@ -64,6 +64,9 @@ struct Chain {
   float inv[DRIFT_MAX_TRANSFORMS];
   int32_t kind;
   float fc, fa, fb, fal, fbl;
+  // kind 2: |z| <= |fa|, so a fixed exponent offset ceil(|fa| log2 e) + 1 keeps every term
+  // in [2^-118, 2^-1] (|fa| <= 40) and the running maximum is not needed
+  float kfix;
 };
 
 // g(x) of the folded chain, in place (kind 1: unchanged). The chain is a kernel argument,
