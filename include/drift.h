@@ -383,9 +383,10 @@ int drift_active_rows(const uint8_t* active, int64_t num_rows, int32_t* rows, in
  *   weight      bf16 [H, V] row-major, vocabulary contiguous (V % 8 == 0)
  *   target_ids  int32 [T]; active (nullable) uint8 [T]: inactive rows get 0.0
  *   logp        fp32 [T]
- * The GEMM runs in one dispatch of one 256-thread block per 256 x 256 (vocab, token) tile,
+ * The GEMM runs in one dispatch of one 512-thread block per 256 x 256 (vocab, token) tile,
  * so ceil(T/256) * ceil(V/256), each rounded up to a multiple of 16, must not exceed
- * 2^24 - 1 (T up to about 7.1M at V = 151936); larger T returns DRIFT_EINVAL.
+ * 2^23 - 1 (T up to 3,530,752 at V = 151936); larger T returns DRIFT_EINVAL, and
+ * drift_workspace_size returns 0 for it.
  * Products accumulate in fp32 over k = 0..H-1 in a fixed order that does not depend on
  * T or on the row's position, so a row's result is bitwise the same in any batch. */
 int drift_lmhead_logprob(const void* hidden, const void* weight, int64_t T, int64_t H,

@@ -128,6 +128,15 @@ def test_host_checks_fail_closed_without_launching():
                   None) == B.DRIFT_EINVAL                               # hidden not 16-aligned
         assert fn(big, big, 4, 64, 16, big, None, big, big, 64,
                   None) == B.DRIFT_EWORKSPACE                           # workspace too small
+        # one dispatch of 512-thread blocks over padded 256 x 256 tiles: T <= 3,530,752 at
+        # V = 151936 (the workspace check comes after the shape check)
+        assert fn(big, big, 3530752, 4096, 151936, big, None, big, big, 64,
+                  None) == B.DRIFT_EWORKSPACE
+        assert fn(big, big, 3530753, 4096, 151936, big, None, big, big, 1 << 40,
+                  None) == B.DRIFT_EINVAL
+    for op in (B.DRIFT_OP_LMHEAD, B.DRIFT_OP_LMHEAD_VH):
+        assert B.drift_workspace_size(op, 3530752, 151936, 4096, B.DRIFT_BF16) > 0
+        assert B.drift_workspace_size(op, 3530753, 151936, 4096, B.DRIFT_BF16) == 0
     assert lib.drift_get_status(None, None, None) == B.DRIFT_EWORKSPACE
     # vocab_real and transform chains are checked before the workspace
     a.layout, a.num_rows, a.batch, a.seq_len, a.vocab, a.row_stride = B.DRIFT_PAD_RIGHT, 0, 0, 1, 10, 10

@@ -101,6 +101,7 @@ size_t drift_workspace_size(int op, int64_t num_rows, int64_t vocab, int64_t hid
     case DRIFT_OP_LMHEAD:
     case DRIFT_OP_LMHEAD_VH:
       if (dtype != DRIFT_BF16 || hidden_dim < 1 || hidden_dim % 8 || vocab % 8) return 0;
+      if (hidden_dim > (int64_t{1} << 22) || !lmhead_shape_ok(num_rows, vocab)) return 0;
       return lmhead_ws_bytes(num_rows, hidden_dim, vocab, op == DRIFT_OP_LMHEAD_VH);
     case DRIFT_OP_ACTIVE_ROWS:
       return compact_ws_bytes(num_rows);

@@ -538,7 +538,7 @@ size_t lmhead_ws_bytes(int64_t T, int64_t H, int64_t V, bool w_vh) {
 }
 
 // The GEMM runs one block of kPThreads per (vocab tile, token tile) in one dispatch, which
-// holds at most 2^32 - 1 work-items: T is limited by that (about 7.1M tokens at V = 151936).
+// holds at most 2^32 - 1 work-items: T is limited by that (3,530,752 tokens at V = 151936).
 bool lmhead_shape_ok(int64_t T, int64_t V) {
   const int64_t nVt = (V + kBV - 1) / kBV, nTt = (T + kBT - 1) / kBT;
   const int64_t nVt_pad = (nVt + kGroupV - 1) / kGroupV * kGroupV;
