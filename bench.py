@@ -17,8 +17,9 @@ after the previous one is freed: the Qwen3-8B-shaped batch (bf16, B=8, L=2048, l
 padding), the packed varlen batch (fp32, V=32000, 256 sequences by cu_seqlens) and the
 tiny correctness batch (fp32, V=1024). Further legs are measured outside the timed region:
 `segments` and `active_rows` on the main batch; `training` (entropy + LSE from the scoring
-pass, dlogits) and `exact` (order-independent reduction, unsharded and as vocabulary
-shards) on the Qwen3-8B-shaped batch; `lmhead`, the fused LM-head selected logprob.
+pass, dlogits), `exact` (order-independent reduction, unsharded and as vocabulary shards)
+and `transforms` (temperature and soft-cap chains) on the Qwen3-8B-shaped batch; `lmhead`,
+the fused LM-head selected logprob.
 """
 import argparse
 import ctypes
@@ -43,7 +44,7 @@ WORKLOAD_TEXT = {
     "tiny": "tiny paired scoring: fp32 logits, V=1024, B=2, L=64, right padding",
 }
 # legs measured beside the main line (outside its timed region)
-LEGS = ("segments", "configs", "training", "exact", "lmhead")
+LEGS = ("segments", "configs", "training", "exact", "transforms", "lmhead")
 # the other scoring workloads measured beside the main one, in this order
 OTHER_CONFIGS = {"large": ("qwen8b", "packed", "tiny"), "qwen8b": ("large", "packed", "tiny"),
                  "packed": ("large", "qwen8b", "tiny"), "tiny": ("large", "qwen8b", "packed")}
@@ -463,6 +464,66 @@ def training_leg(case, ids, att, act, cu, steps=10, warmup=2):
     }
 
 
+def time_steps(runner, steps, warmup, name):
+    """Runs `warmup` untimed and `steps` timed steps of a ScoringStep (scoring kernel
+    bracketed by events on its launch stream, diagnostics, one host sync each). Returns the
+    sorted kernel times (ms) and the wall time of the timed steps (s)."""
+    import torch
+
+    from train_rollout_logprob_amd import binding as B
+
+    n_ev = warmup + steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_ev)]
+    for e0, e1 in evs:          # create the underlying events
+        e0.record()
+        e1.record()
+    torch.cuda.synchronize()
+    handles = [(e0.cuda_event, e1.cuda_event) for e0, e1 in evs]
+
+    def step(i):
+        runner.set_events(*handles[i])
+        st = runner.run()
+        if st != B.DRIFT_OK:
+            raise RuntimeError(f"{name}: status {B.STATUS_NAMES[st]}")
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(warmup, n_ev):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    return sorted(evs[i][0].elapsed_time(evs[i][1]) for i in range(warmup, n_ev)), elapsed
+
+
+def transforms_leg(case, ids, att, act, cu, steps=20, warmup=3):
+    """The scoring step on the same batch with the same logit transform on both sides:
+    temperature 0.7 (a multiplying chain) and soft-cap 30 (x -> 30 tanh(x / 30)); kernel
+    time from events on the launch stream."""
+    from train_rollout_logprob_amd import binding as B
+
+    alg = case.n_active() * case.V * case.elem_bytes * 2
+    out = {"workload": "same batch, the same chain on both sides"}
+    for xf, chain in (("temperature", [("temperature", 0.7)]),
+                      ("softcap", [("softcap", 30.0)])):
+        runner = B.ScoringStep(case.train, case.rollout, ids, att, act, case.layout, case.B,
+                               case.L, cu, case.eps_low, case.eps_high,
+                               transforms=(chain, chain))
+        kern, _ = time_steps(runner, steps, warmup, f"{case.name} {xf}")
+        avg = sum(kern) / len(kern)
+        out[xf] = {"chain": chain, "kernel": f"score_rows<{case.dtype}, folded chain>",
+                   "kernel_ms": avg, "kernel_ms_median": kern[len(kern) // 2],
+                   "kernel_ms_min": kern[0], "bytes_per_launch": alg,
+                   "achieved_gbs": alg / (avg * 1e-3) / 1e9,
+                   "frac": alg / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        log(f"[bench] {case.name} {xf}: scoring kernel {avg:.3f} ms "
+            f"(median {kern[len(kern) // 2]:.3f}), {out[xf]['achieved_gbs']:.0f} GB/s")
+        del runner
+    return out
+
+
 def score_leg(name, steps, warmup, xf="none", ceiling=True):
     """Generates one scoring workload on cuda:0 and times `steps` steps (scoring +
     diagnostics, one host sync each) after `warmup` untimed ones. Returns the measurement
@@ -484,31 +545,8 @@ def score_leg(name, steps, warmup, xf="none", ceiling=True):
              "softcap": [("softcap", 30.0)]}[xf]
     runner = B.ScoringStep(case.train, case.rollout, ids, att, act, case.layout, case.B,
                            case.L, cu, case.eps_low, case.eps_high, transforms=(chain, chain))
-    n_ev = warmup + steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n_ev)]
-    for e0, e1 in evs:          # create the underlying events
-        e0.record()
-        e1.record()
-    torch.cuda.synchronize()
-    handles = [(e0.cuda_event, e1.cuda_event) for e0, e1 in evs]
-
-    def step(i):
-        runner.set_events(*handles[i])
-        st = runner.run()
-        if st != B.DRIFT_OK:
-            raise RuntimeError(f"{name}: status {B.STATUS_NAMES[st]}")
-
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
     log(f"[bench] {name}: timing {steps} steps")
-    t0 = time.perf_counter()
-    for i in range(warmup, n_ev):
-        step(i)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    kern = sorted(evs[i][0].elapsed_time(evs[i][1]) for i in range(warmup, n_ev))
+    kern, elapsed = time_steps(runner, steps, warmup, name)
     kern_avg = sum(kern) / len(kern)
     if runner.stats.n_active != n_active:
         raise RuntimeError(f"{name}: {runner.stats.n_active} active rows, expected {n_active}")
@@ -663,6 +701,9 @@ def run(args, pool):
             torch.cuda.empty_cache()
             log("[bench] exact-reduction leg (unsharded and vocabulary shards)")
             line["exact"] = exact_leg(case, ids, att, act, cu)
+        if "transforms" in legs:
+            log("[bench] logit-transform leg (temperature, soft-cap)")
+            line["transforms"] = transforms_leg(case, ids, att, act, cu)
 
     if "segments" in legs:
         line["segments"] = segments_leg(case, runner.out[2], runner.out[3], runner.ws)
