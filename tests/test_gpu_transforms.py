@@ -1,6 +1,8 @@
 """GPU parity of the vocab-padding mask and the per-side logit transform chains
 ("[WS2] Framework for ablation experiment", LogProb knobs rows 2 and 7) against the
 fp64 oracle."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -107,3 +109,37 @@ def test_transforms_keep_batch_composition_invariance():
         if ref is None:
             ref = v
         assert np.array_equal(v.view(np.uint32), ref.view(np.uint32)), bs
+
+
+@pytest.mark.parametrize("chain", [[("softcap", 15.0)], [("scale", 2.0), ("softcap", 40.0)],
+                                   [("softcap", 60.0)]], ids=["folded", "folded_scaled",
+                                                              "step_by_step"])
+def test_softcap_of_infinite_logits(chain):
+    """A soft-cap maps +-inf logits to +-cap: rows with infinite logits (the selected one
+    among them) stay finite and match the oracle; a NaN logit still fails the row closed
+    (ENONFINITE) and leaves the other rows' values unchanged."""
+    from train_rollout_logprob_amd import binding as B
+    V, N = 3001, 5
+    g = torch.Generator(device="cuda")
+    g.manual_seed(21)
+    x = torch.randn((N, V), generator=g, device="cuda") * 4
+    ids = torch.tensor([7, 100, 3000, 0, 1234], dtype=torch.int32, device="cuda")
+    x[0, 50:60] = math.inf
+    x[1, :2500] = -math.inf
+    x[2, 3000] = math.inf                   # the selected logit, in the ragged last group
+    x[3, 0] = -math.inf                     # the selected logit
+    tr = (chain, chain)
+    t, r, d, a, ws = B.selected_logprob(x, x, ids, layout="right", batch=1, seq_len=N,
+                                        check=True, transforms=tr)
+    want = oracle.score_rows(x.cpu().numpy(), x.cpu().numpy(), "f32", ids.cpu().numpy(),
+                             transforms=tr)[0]
+    got = t.double().cpu().numpy()
+    assert np.all(np.isfinite(want)) and np.abs(got - want).max() <= LOGP_TOL, (got, want)
+    y = x.clone()
+    y[4, 17] = math.nan
+    t2, r2, d2, a2, ws2 = B.selected_logprob(y, y, ids, layout="right", batch=1, seq_len=N,
+                                             transforms=tr)
+    st, bad = B.drift_get_status(ws2)
+    assert status_name(st) == "ENONFINITE" and bad == 4
+    assert math.isnan(t2[4].item())
+    assert np.array_equal(t2[:4].cpu().numpy().view(np.uint32), t[:4].cpu().numpy().view(np.uint32))
