@@ -1,4 +1,5 @@
-"""Full-size workloads on the GPU, in the launch configuration the benchmark times.
+"""Full-size workloads on the GPU, in the launch configuration the benchmark times (and the
+Qwen3-8B-shaped batch once more with a soft-cap of 30 on both sides).
 
 Every active row of each scoring workload is compared with the fp64 oracle (the oracle
 runs in a pool of host worker processes started before this process touched the GPU):
@@ -37,7 +38,7 @@ def _copy_rows(dst, src, idx):
         torch.from_numpy(dst).copy_(sub)
 
 
-def _oracle_all_rows(pool, case, rows):
+def _oracle_all_rows(pool, case, rows, transforms=(None, None)):
     """Oracle logps and dlogp (float64) of the given rows, scored chunk by chunk."""
     per = max(1, CHUNK_BYTES // (2 * case.V * case.elem_bytes))
     per = min(per, len(rows))
@@ -48,23 +49,30 @@ def _oracle_all_rows(pool, case, rows):
         idx = torch.as_tensor(sel, device=case.train.device)
         _copy_rows(bt[:len(sel)], case.train, idx)
         _copy_rows(br[:len(sel)], case.rollout, idx)
-        t, r, d, _ = pool.score(len(sel), case.V, case.dtype, case.ids[sel])
+        t, r, d, _ = pool.score(len(sel), case.V, case.dtype, case.ids[sel],
+                                transforms=transforms)
         out[:, a:a + len(sel)] = (t, r, d)
     return out
 
 
-@pytest.mark.parametrize("name", ["tiny", "qwen8b", "packed", "large"])
+# soft-cap 30 on both sides: the folded log-sum-exp terms of the scoring kernel at full size
+CHAIN = {"qwen8b_softcap": [("softcap", 30.0)]}
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen8b", "packed", "large", "qwen8b_softcap"])
 def test_full_size_every_active_row(name):
     from train_rollout_logprob_amd import binding as B
     pool = oracle_pool()
     if pool is None:
         pytest.skip("the oracle worker pool was not started (no GPU counted at start-up)")
     print(f"[case] full {name}: generating", flush=True)
-    case = synth.make_logits_case(name, device="cuda")
+    chain = CHAIN.get(name)
+    tr = (chain, chain)
+    case = synth.make_logits_case(name.split("_")[0], device="cuda")
     ids, att, act, cu = device_inputs(case)
     print(f"[case] full {name}: N={case.N} V={case.V} n_active={case.n_active()}", flush=True)
     step = B.ScoringStep(case.train, case.rollout, ids, att, act, case.layout, case.B, case.L,
-                         cu, case.eps_low, case.eps_high)
+                         cu, case.eps_low, case.eps_high, transforms=tr)
     st = step.run()
     assert status_name(st) == "OK"
     s = step.stats.as_dict()
@@ -79,7 +87,7 @@ def test_full_size_every_active_row(name):
     assert np.all(th[a_h == 0] == 0) and np.all(rh[a_h == 0] == 0) and np.all(dh[a_h == 0] == 0)
     print(f"[case] full {name}: oracle over {len(rows)} rows in {pool.workers} workers",
           flush=True)
-    ot, orr, od = _oracle_all_rows(pool, case, rows)
+    ot, orr, od = _oracle_all_rows(pool, case, rows, tr)
     for name_, g, w in (("train", th, ot), ("rollout", rh, orr), ("dlogp", dh, od)):
         err = np.abs(g[rows].astype(np.float64) - w)
         print(f"[case] {name} {name_}: max err {err.max():.3e} (row {rows[int(err.argmax())]}) "
