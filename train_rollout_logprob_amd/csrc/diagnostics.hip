@@ -263,11 +263,19 @@ __global__ void __launch_bounds__(kDiagThreads) diag_tile(DiagParams p) {
   const double lo_edge = 1.0 - p.eps_low, hi_edge = 1.0 + p.eps_high;
   RowStats acc = {};
   const int64_t tile0 = (int64_t)blockIdx.x * kDiagTile;
+  // all loads first (one round trip), then the rows in the same order as ever
+  uint8_t act[kRowsPerThread];
+  float dv[kRowsPerThread];
 #pragma unroll
   for (int j = 0; j < kRowsPerThread; ++j) {
     const int64_t r = tile0 + (int64_t)j * kDiagThreads + tid;
-    if (r >= p.N || !p.active[r]) continue;
-    add_row(acc, p.d[r], r, lo_edge, hi_edge);
+    act[j] = r < p.N ? p.active[r] : (uint8_t)0;
+    dv[j] = r < p.N ? p.d[r] : 0.0f;
+  }
+#pragma unroll
+  for (int j = 0; j < kRowsPerThread; ++j) {
+    const int64_t r = tile0 + (int64_t)j * kDiagThreads + tid;
+    if (act[j]) add_row(acc, dv[j], r, lo_edge, hi_edge);
   }
   if (p.N > kSelSingleMax && blockIdx.x == 0) {  // read by the digit launches that follow
     unsigned int* h = (unsigned int*)(p.ws + lay.hist_off);
@@ -290,6 +298,12 @@ __global__ void __launch_bounds__(kDiagThreads) diag_tile(DiagParams p) {
 }
 
 constexpr int kSelBatch = 8;                  // rows per thread per batch of loads
+static_assert(kPassRowsPerBlock % (4 * kPassThreads) == 0 &&
+                  (kPassRowsPerBlock / kPassThreads) % kSelBatch == 0,
+              "a pass block's rows split evenly into batches");
+static_assert(kBins % kPassThreads == 0 && (kNumQ * kBins) % kPassThreads == 0 &&
+                  (kNumQ * kBins) % kSelThreads == 0,
+              "histogram copies split evenly over the threads");
 
 // Keys of rows r0 .. r0 + 3 (kNoKey for inactive rows and rows past hi): one 16-byte load
 // of d and one 4-byte load of the mask when all four rows exist; d and active must then be
@@ -412,10 +426,20 @@ __global__ void __launch_bounds__(kSelThreads) diag_select(DiagParams p) {
   drift_stats& S = p.out ? *p.out : ((SelState*)p.ws)->stats;
   if (wave == 0) {
     RowStats a = {};
-    for (int g = lane; g < lay.G; g += 64) {
-      const TilePartial b = tp[g];
-      const RowStats bs = {b.s_abs, b.s_exp, b.s_kl, b.s_d, b.n, b.lo, b.hi, b.nonfinite, b.best};
-      add_stats(a, bs);
+    // lane j folds tiles j, j + 64, ... in ascending order, loading four at a time
+    for (int g0 = lane; g0 < lay.G; g0 += 4 * 64) {
+      RowStats bs[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int g = g0 + 64 * u;
+        if (g < lay.G) {
+          const TilePartial& b = tp[g];
+          bs[u] = {b.s_abs, b.s_exp, b.s_kl, b.s_d, b.n, b.lo, b.hi, b.nonfinite, b.best};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (g0 + 64 * u < lay.G) add_stats(a, bs[u]);
     }
     s_lane[lane] = a;
   }
@@ -435,8 +459,11 @@ __global__ void __launch_bounds__(kSelThreads) diag_select(DiagParams p) {
   if (p.N > kSelSingleMax) {
     const unsigned int* gh = (const unsigned int*)(p.ws + lay.hist_off);
     for (int pass = 0; pass < 3; ++pass) {
-      for (int b = tid; b < kNumQ * kBins; b += kSelThreads)
+#pragma unroll
+      for (int i = 0; i < kNumQ * kBins / kSelThreads; ++i) {
+        const int b = tid + i * kSelThreads;
         (&s_hist[0][0])[b] = gh[(pass * kNumQ) * kBins + b];
+      }
       __syncthreads();
       pick_digits(s_hist[0], s_hist[pass == 0 ? 0 : 1], kShift[pass], s_rank, s_prefix);
       __syncthreads();
@@ -467,10 +494,13 @@ __global__ void __launch_bounds__(kPassThreads) diag_pass(DiagParams p) {
   unsigned int* gh = (unsigned int*)(p.ws + lay.hist_off);
   if (tid < kNumQ) s_prefix[tid] = 0;
   if (PASS > 0) {
-    for (int b = tid; b < kBins; b += kPassThreads) s_hist[0][b] = gh[b];
+#pragma unroll
+    for (int i = 0; i < kBins / kPassThreads; ++i)
+      s_hist[0][tid + i * kPassThreads] = gh[tid + i * kPassThreads];
     __syncthreads();
     unsigned int c = 0;
-    for (int b = tid; b < kBins; b += kPassThreads) c += s_hist[0][b];
+#pragma unroll
+    for (int i = 0; i < kBins / kPassThreads; ++i) c += s_hist[0][tid + i * kPassThreads];
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) c += (unsigned int)__shfl_xor((int)c, o);
     if (lane == 0) s_w[wave] = c;
@@ -483,8 +513,11 @@ __global__ void __launch_bounds__(kPassThreads) diag_pass(DiagParams p) {
     __syncthreads();
     for (int pass = 0; pass < PASS; ++pass) {
       if (pass > 0) {
-        for (int b = tid; b < kNumQ * kBins; b += kPassThreads)
+#pragma unroll
+        for (int i = 0; i < kNumQ * kBins / kPassThreads; ++i) {
+          const int b = tid + i * kPassThreads;
           (&s_hist[0][0])[b] = gh[(pass * kNumQ) * kBins + b];
+        }
         __syncthreads();
       }
       pick_digits(s_hist[0], s_hist[pass == 0 ? 0 : 1], kShift[pass], s_rank, s_prefix);
@@ -509,16 +542,29 @@ __global__ void __launch_bounds__(kPassThreads) diag_pass(DiagParams p) {
   const int64_t lo = (int64_t)blockIdx.x * kPassRowsPerBlock;
   const int64_t hi = lo + kPassRowsPerBlock < p.N ? lo + kPassRowsPerBlock : p.N;
   const bool vec = ((uintptr_t)p.d & 15) == 0 && ((uintptr_t)p.active & 3) == 0;
+  // every load of the block's rows is issued before any count
   if (vec) {  // block-uniform; lo is a multiple of 4
-    for (int64_t r0 = lo + 4 * (int64_t)tid; r0 < hi; r0 += 4 * kPassThreads) {
-      unsigned int k4[4];
-      keys4(p.d, p.active, r0, hi, k4);
+    constexpr int kIt = kPassRowsPerBlock / (4 * kPassThreads);
+    unsigned int kk[kIt][4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) count(k4[e]);
-    }
+    for (int it = 0; it < kIt; ++it)
+      keys4(p.d, p.active, lo + 4 * ((int64_t)it * kPassThreads + tid), hi, kk[it]);
+#pragma unroll
+    for (int it = 0; it < kIt; ++it)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) count(kk[it][e]);
   } else {
-    for (int64_t r = lo + tid; r < hi; r += kPassThreads)
-      count(p.active[r] ? key_of(p.d[r]) : kNoKey);
+    constexpr int kIt = kPassRowsPerBlock / kPassThreads;
+    for (int i0 = 0; i0 < kIt; i0 += kSelBatch) {
+      unsigned int kb[kSelBatch];
+#pragma unroll
+      for (int u = 0; u < kSelBatch; ++u) {
+        const int64_t r = lo + tid + (int64_t)(i0 + u) * kPassThreads;
+        kb[u] = (r < hi && p.active[r]) ? key_of(p.d[r]) : kNoKey;
+      }
+#pragma unroll
+      for (int u = 0; u < kSelBatch; ++u) count(kb[u]);
+    }
   }
   __syncthreads();
   for (int b = tid; b < kNumQ * kBins; b += kPassThreads) {
