@@ -22,7 +22,11 @@
 //     batch-composition control of the "Attention Debug Matrix" page);
 //   * LSE is exported in the natural-log domain: lse = (k + log2 s) * ln2 in fp64
 //     (Attention knobs row 6, LSE domain); logp and dlogp are formed in fp64 and rounded
-//     once to fp32.
+//     once to fp32;
+//   * a per-side transform chain (LogProb knobs row 7) with at most one soft-cap step is
+//     folded for the log-sum-exp terms (rowio.h): the exponent is one FMA of the value
+//     g(x), and a soft-capped side, whose logits are bounded by the cap, keeps a fixed k
+//     instead of the running maximum. The selected logit takes the chain step by step.
 // The selected logit is read once by its single owner (LogProb knobs row 8).
 //
 // The same file holds the kernels of the optional outputs and modes, which share the row
@@ -179,7 +183,8 @@ __device__ __forceinline__ void push(AccX& a, const float (&x)[VEC]) {
 // pushes them in ascending order; the last partial group (V % VEC logits, padded with
 // -inf) belongs to the lane that would own group V / VEC. All lanes run the same number
 // of pushes (missing groups are all -inf and add exactly 0). U groups per side are
-// loaded ahead for memory-level parallelism; U does not change the arithmetic.
+// loaded ahead for memory-level parallelism; U does not change the arithmetic. XF: 0 no
+// chain, 1 chains applied step by step, 2 both chains folded (rowio.h).
 template <typename T, int NT, int U, bool kAligned, int XF, typename A>
 __device__ __forceinline__ void stream_row(const char* rt, const char* rr, int64_t V, int tid,
                                            A& at, A& ar, const ScoreParams& p) {
