@@ -71,7 +71,7 @@ struct Chain {
 
 // g(x) of the folded chain, in place (kind 1: unchanged). The chain is a kernel argument,
 // so the branch is uniform. 2^(fc x) overflows to +inf for large fc x, and g is then 0:
-// the soft-cap's saturation; x = -inf gives g = 1.
+// the soft-cap's saturation; fc x = -inf gives g = 1.
 template <int VEC>
 __device__ __forceinline__ void fold_values(float (&x)[VEC], const Chain& c) {
   if (c.kind == 2) {
