@@ -73,8 +73,11 @@ Chain make_chain(const drift_transform& t) {
   c.fb = (float)fb;
   c.fal = (float)(fa * log2e);
   c.fbl = (float)(fb * log2e);
+  c.fald = (double)c.fa * log2e;
+  c.fbld = (double)c.fb * log2e;
+  c.fdz = nsoft == 1 ? (float)(4.0 * pre * post) : 0.0f;
   // factors whose folded form leaves the fp32 range keep the step-by-step chain
-  const float f[5] = {c.fc, c.fa, c.fb, c.fal, c.fbl};
+  const float f[6] = {c.fc, c.fa, c.fb, c.fal, c.fbl, c.fdz};
   for (float x : f)
     if (!(fabsf(x) < INFINITY)) c.kind = 0;
   if (c.kind == 2 && !(fabsf(c.fc) >= 1.17549435e-38f)) c.kind = 0;  // fc not a normal float

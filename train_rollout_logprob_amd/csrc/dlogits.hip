@@ -9,7 +9,9 @@
 // an elementwise, HBM-bound pass. The exponent z_v - LSE is formed in fp64 and rounded
 // once to fp32 before exp2, so p_v carries the error of one exp2 and one rounding.
 // Inactive rows are written with zeros; an active row whose LSE is NaN (an id the
-// forward pass rejected) comes out NaN over [0, Vr).
+// forward pass rejected) comes out NaN over [0, Vr). A chain with at most one soft-cap step
+// is taken in its folded form (rowio.h), as the scoring pass forms its log-sum-exp terms
+// when both sides' chains fold.
 #include <math.h>
 
 #include "classify.h"
@@ -86,12 +88,28 @@ template <> struct Out<uint16_t> {  // bf16 bit patterns
   }
 };
 
-// dL/dx for the VEC logits of group g (columns c0 .. c0+VEC-1).
-template <int VEC, bool XF>
+// dL/dx for the VEC logits of group g (columns c0 .. c0+VEC-1). XF: 0 no chain, 1 the
+// chain step by step, 2 the folded chain (rowio.h): z = fa + fb v with v = g(x) for a
+// soft-cap (slope fdz g (1 - g)) or v = x for multiplying steps (slope fb), the same
+// values the scoring pass's log-sum-exp terms were formed from; the exponent
+// z log2(e) - LSE log2(e) is then one fp64 FMA of v.
+template <int VEC, int XF>
 __device__ __forceinline__ void grad_group(float (&x)[VEC], int64_t c0, int64_t y, int64_t Vr,
                                            double L2, float g, const Chain& c) {
   float dz[VEC];
-  if constexpr (XF) {
+  double sl = kLog2eD, base = -L2;  // exponent = v * sl + base
+  if constexpr (XF == 2) {
+    if (c.kind == 2) {
+      fold_values<VEC>(x, c);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) dz[e] = c.fdz * fmaf(-x[e], x[e], x[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) dz[e] = c.fb;
+    }
+    sl = c.fbld;
+    base = c.fald - L2;
+  } else if constexpr (XF == 1) {
     apply_chain_grad<VEC>(x, dz, c);
   } else {
 #pragma unroll
@@ -100,7 +118,7 @@ __device__ __forceinline__ void grad_group(float (&x)[VEC], int64_t c0, int64_t 
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
     const int64_t col = c0 + e;
-    const float a = (float)fma((double)x[e], kLog2eD, -L2);
+    const float a = (float)fma((double)x[e], sl, base);
     const float pv = __builtin_amdgcn_exp2f(a);
     const float oh = col == y ? 1.0f : 0.0f;
     const float gv = (g * dz[e]) * (oh - pv);
@@ -108,7 +126,7 @@ __device__ __forceinline__ void grad_group(float (&x)[VEC], int64_t c0, int64_t 
   }
 }
 
-template <typename T, typename O, int NT, int U, bool XF>
+template <typename T, typename O, int NT, int U, int XF>
 __global__ void __launch_bounds__(NT) dlogits_rows(DlogitsParams p) {
   constexpr int VEC = Elem<T>::kVec;
   const int64_t r = p.row0 + blockIdx.x;
@@ -179,10 +197,12 @@ void launch_typed(const DlogitsParams& p, hipStream_t s) {
   for (int64_t r0 = 0; r0 < p.N; r0 += per) {
     q.row0 = r0;
     const dim3 grid((unsigned)(p.N - r0 < per ? p.N - r0 : per));
-    if (p.xf.n > 0)
-      hipLaunchKernelGGL((dlogits_rows<T, O, NT, U, true>), grid, dim3(NT), 0, s, q);
+    if (p.xf.n == 0)
+      hipLaunchKernelGGL((dlogits_rows<T, O, NT, U, 0>), grid, dim3(NT), 0, s, q);
+    else if (p.xf.kind != 0)
+      hipLaunchKernelGGL((dlogits_rows<T, O, NT, U, 2>), grid, dim3(NT), 0, s, q);
     else
-      hipLaunchKernelGGL((dlogits_rows<T, O, NT, U, false>), grid, dim3(NT), 0, s, q);
+      hipLaunchKernelGGL((dlogits_rows<T, O, NT, U, 1>), grid, dim3(NT), 0, s, q);
   }
 }
 

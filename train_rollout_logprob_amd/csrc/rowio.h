@@ -67,6 +67,11 @@ struct Chain {
   // kind 2: |z| <= |fa|, so a fixed exponent offset ceil(|fa| log2 e) + 1 keeps every term
   // in [2^-118, 2^-1] (|fa| <= 40) and the running maximum is not needed
   float kfix;
+  // the gradient's form (dlogits): fa log2(e) and fb log2(e) in fp64, and the slope
+  // dz/dx = fb (kind 1) or fdz g (1 - g) with fdz = 4 p q (kind 2: the derivative of
+  // q c tanh(p x / c) is p q (1 - tanh^2) and 1 - tanh^2 = 4 g (1 - g))
+  double fald, fbld;
+  float fdz;
 };
 
 // g(x) of the folded chain, in place (kind 1: unchanged). The chain is a kernel argument,
