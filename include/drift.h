@@ -76,8 +76,9 @@ extern "C" {
  * with at most one SOFTCAP step is folded into z = a + b g(x): g = x for multiplying
  * steps only, and g = 1 / (1 + 2^(c x)) around one SOFTCAP step (tanh(u) = 1 - 2 /
  * (e^(2u) + 1), one hardware exp2 and one reciprocal per logit), within 3.6e-7 |a| of the
- * exact value, where |a| is the cap times the factors after it; used when |a| <= 40,
- * else (and for two SOFTCAP steps) the steps are applied one by one to every logit. */
+ * exact value, where |a| is the cap times the factors after it; used when |a| <= 40 on
+ * both sides, else (and for two SOFTCAP steps) the steps are applied one by one to every
+ * logit. drift_dlogits takes a side's chain in the same folded form when it folds. */
 
 typedef struct drift_transform {
   int32_t count;                       /* steps in use, 0 = identity                     */

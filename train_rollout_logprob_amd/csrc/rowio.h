@@ -46,7 +46,7 @@ template <> struct Elem<uint16_t> {  // bf16 bit patterns
 // with inv = 1 / v.
 //
 // The same chain folded into one step for the log-sum-exp terms of the streaming kernel
-// (kind != 0): z = fa + fb * g(x), with
+// and for the gradient (dlogits) (kind != 0): z = fa + fb * g(x), with
 //   kind 1 (multiplying steps only): g(x) = x, fa = 0, fb = the product of the factors;
 //   kind 2 (one SOFTCAP step of value c, factor p before it and q after it):
 //     g(x) = 1 / (1 + 2^(fc * x)), fc = 2 log2(e) p / c, fa = q c, fb = -2 q c,
