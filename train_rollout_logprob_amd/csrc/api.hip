@@ -485,7 +485,7 @@ const drift_backend_desc* drift_backend_descriptor(void) {
       "logits widened to fp32; exp2 in fp32 with a power-of-two running max; sums in "
       "fp64; lse/logp/dlogp formed in fp64, rounded once to fp32; diagnostics in fp64; "
       "transform chains with at most one softcap (|cap x later factors| <= 40) folded "
-      "for the lse terms (softcap as 1 - 2/(1 + 2^(2 log2e x/cap)), one exp2 and one "
+      "for the lse terms and dlogits (softcap as 1 - 2/(1 + 2^(2 log2e x/cap)), one exp2 and one "
       "reciprocal, within 3.6e-7 cap; a fixed exponent offset), others and the selected "
       "logit step by step; lmhead products bf16 x bf16 -> fp32 accumulate, fixed k order",
       "natural log",
