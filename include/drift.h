@@ -71,14 +71,15 @@ extern "C" {
 #define DRIFT_XF_TEMPERATURE 2  /* x -> x / value        (value > 0; as x * (1/value))   */
 #define DRIFT_XF_SOFTCAP     3  /* x -> value * tanh(x * (1/value))  (value > 0)         */
 #define DRIFT_MAX_TRANSFORMS 4
-/* Arithmetic of a chain in drift_selected_logprob with DRIFT_REDUCE_TREE: the selected
+/* Arithmetic of a chain in drift_selected_logprob (either reduction): the selected
  * logit takes the steps one by one (tanhf for SOFTCAP). For the log-sum-exp terms a chain
  * with at most one SOFTCAP step is folded into z = a + b g(x): g = x for multiplying
  * steps only, and g = 1 / (1 + 2^(c x)) around one SOFTCAP step (tanh(u) = 1 - 2 /
  * (e^(2u) + 1), one hardware exp2 and one reciprocal per logit), within 3.6e-7 |a| of the
  * exact value, where |a| is the cap times the factors after it; used when |a| <= 40 on
  * both sides, else (and for two SOFTCAP steps) the steps are applied one by one to every
- * logit. drift_dlogits takes a side's chain in the same folded form when it folds. */
+ * logit (DRIFT_REDUCE_EXACT forms each folded logit a + b g(x) before its integer
+ * bins). drift_dlogits takes a side's chain in the same folded form when it folds. */
 
 typedef struct drift_transform {
   int32_t count;                       /* steps in use, 0 = identity                     */

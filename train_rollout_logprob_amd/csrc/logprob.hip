@@ -194,7 +194,8 @@ __device__ __forceinline__ void stream_row(const char* rt, const char* rr, int64
   const int64_t full_iters = nfull / NT;              // iterations where every lane is full
   const int64_t iters = (ngroups + NT - 1) / NT;
   int64_t j = 0;
-  if constexpr (XF == 2) {  // a folded soft-cap side starts at its fixed offset (rowio.h)
+  if constexpr (XF == 2 && !std::is_same<A, AccX>::value) {
+    // a folded soft-cap side starts at its fixed offset (rowio.h)
     if (p.xf[0].kind == 2) at.k = p.xf[0].kfix;
     if (p.xf[1].kind == 2) ar.k = p.xf[1].kfix;
   }
@@ -212,7 +213,19 @@ __device__ __forceinline__ void stream_row(const char* rt, const char* rr, int64
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         float x[VEC];
-        if constexpr (XF == 2) {  // both chains folded: the terms from g (rowio.h)
+        if constexpr (XF == 2 && std::is_same<A, AccX>::value) {
+          // exact mode, folded chains: the logits z = fa + fb g, as in the ragged group
+          Elem<T>::unpack(bt[u], x);
+          fold_values<VEC>(x, p.xf[0]);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) x[e] = fmaf(p.xf[0].fb, x[e], p.xf[0].fa);
+          push<VEC>(at, x);
+          Elem<T>::unpack(br[u], x);
+          fold_values<VEC>(x, p.xf[1]);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) x[e] = fmaf(p.xf[1].fb, x[e], p.xf[1].fa);
+          push<VEC>(ar, x);
+        } else if constexpr (XF == 2) {  // both chains folded: the terms from g (rowio.h)
           Elem<T>::unpack(bt[u], x);
           fold_values<VEC>(x, p.xf[0]);
           if (p.xf[0].kind == 2)
@@ -473,7 +486,7 @@ __device__ __forceinline__ void unscored_outputs(const ScoreParams& p, int64_t r
 // One block per row, as score_rows, with the exact accumulator. The row holds the global
 // columns [vstart, vstart + V); with p.part set it writes the shard partials instead of
 // finalizing.
-template <typename T, int NT, int U, bool XF>
+template <typename T, int NT, int U, int XF>
 __global__ void __launch_bounds__(NT) score_rows_exact(ScoreParams p) {
   constexpr int NW = NT / 64;
   __shared__ AccX s_acc[2][NW];
@@ -692,21 +705,28 @@ hipError_t launch_score_exact(const ScoreParams& p, hipStream_t s, hipEvent_t ev
     // follows the row length: 256 threads for rows of 4096 or more 16-byte groups, 128 for
     // shorter ones (vocabulary shards), which keep more rows in flight per CU (measured on
     // MI355X: 8 fp32 shards of 4000 columns 9.6 -> 7.6 ms, full rows unchanged).
-    const bool xf = p.xf[0].n > 0 || p.xf[1].n > 0;
+    // chains as in launch_score: none (0), step by step (1), both folded (2)
+    const int xf = !(p.xf[0].n > 0 || p.xf[1].n > 0) ? 0
+                   : (p.xf[0].kind != 0 && p.xf[1].kind != 0) ? 2 : 1;
     const int vec = p.dtype == DRIFT_BF16 ? 8 : 4;
     const bool wide = (p.V + vec - 1) / vec >= 4096;
     auto go = [&](auto kernel, int nt) { launch_over_rows(kernel, p, nt, s); };
     constexpr int U = 4;
+    auto by_xf = [&](auto k0, auto k1, auto k2, int nt) {
+      if (xf == 2) go(k2, nt);
+      else if (xf == 1) go(k1, nt);
+      else go(k0, nt);
+    };
     if (p.dtype == DRIFT_BF16) {
-      if (wide) xf ? go(score_rows_exact<uint16_t, 256, U, true>, 256)
-                   : go(score_rows_exact<uint16_t, 256, U, false>, 256);
-      else xf ? go(score_rows_exact<uint16_t, 128, U, true>, 128)
-              : go(score_rows_exact<uint16_t, 128, U, false>, 128);
+      if (wide) by_xf(score_rows_exact<uint16_t, 256, U, 0>, score_rows_exact<uint16_t, 256, U, 1>,
+                      score_rows_exact<uint16_t, 256, U, 2>, 256);
+      else by_xf(score_rows_exact<uint16_t, 128, U, 0>, score_rows_exact<uint16_t, 128, U, 1>,
+                 score_rows_exact<uint16_t, 128, U, 2>, 128);
     } else {
-      if (wide) xf ? go(score_rows_exact<float, 256, U, true>, 256)
-                   : go(score_rows_exact<float, 256, U, false>, 256);
-      else xf ? go(score_rows_exact<float, 128, U, true>, 128)
-              : go(score_rows_exact<float, 128, U, false>, 128);
+      if (wide) by_xf(score_rows_exact<float, 256, U, 0>, score_rows_exact<float, 256, U, 1>,
+                      score_rows_exact<float, 256, U, 2>, 256);
+      else by_xf(score_rows_exact<float, 128, U, 0>, score_rows_exact<float, 128, U, 1>,
+                 score_rows_exact<float, 128, U, 2>, 128);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
