@@ -45,8 +45,9 @@ template <> struct Elem<uint16_t> {  // bf16 bit patterns
 // v (SCALE: the value, TEMPERATURE: its reciprocal) or, for SOFTCAP, x -> v * tanh(x * inv)
 // with inv = 1 / v.
 //
-// The same chain folded into one step for the log-sum-exp terms of the streaming kernel
-// and for the gradient (dlogits) (kind != 0): z = fa + fb * g(x), with
+// The same chain folded into one step for the log-sum-exp terms of the scoring kernels
+// (tree and exact reductions) and for the gradient (dlogits) (kind != 0): z = fa + fb g(x),
+// with
 //   kind 1 (multiplying steps only): g(x) = x, fa = 0, fb = the product of the factors;
 //   kind 2 (one SOFTCAP step of value c, factor p before it and q after it):
 //     g(x) = 1 / (1 + 2^(fc * x)), fc = 2 log2(e) p / c, fa = q c, fb = -2 q c,
