@@ -37,6 +37,10 @@ CHAINS = {
     "none": (None, None),
     "softcap_temp": ([("softcap", 20.0), ("temperature", 0.8)], [("temperature", 1.25)]),
     "scale_neg": ([("scale", -1.5)], None),
+    # chains the folded form does not take (two soft-caps; a cap above 40): step by step,
+    # and a folded side beside a step-by-step one
+    "softcap_twice": ([("softcap", 30.0), ("softcap", 12.0)], [("softcap", 50.0)]),
+    "mixed_forms": ([("softcap", 25.0)], [("softcap", 30.0), ("softcap", 20.0)]),
 }
 
 
