@@ -50,7 +50,10 @@ MUTATIONS = [
      "if boundaries[s] <= y <= boundaries[s + 1]:"),                              # owner
     ("sharding.py", "return M + math.log(", "return math.log("),                  # max term
     ("lmhead.py", "z[i, int(ids[r])]", "z[i, int(ids[i])]"),
-    ("lmhead.py", "z = h @ weight_f64", "z = (h[:, ::-1] @ weight_f64)"),        # reversed K
+    ("lmhead.py", "z = apply_transforms(h @ weight_f64, transforms)",
+     "z = apply_transforms(h[:, ::-1] @ weight_f64, transforms)"),               # reversed K
+    ("lmhead.py", "z = apply_transforms(h @ weight_f64, transforms)",
+     "z = h @ weight_f64"),                                                      # chain dropped
 ]
 
 
