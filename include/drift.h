@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define DRIFT_ABI_VERSION 8
+#define DRIFT_ABI_VERSION 9
 
 /* ---- status codes ---------------------------------------------------------------- */
 #define DRIFT_OK          0
@@ -407,6 +407,28 @@ int drift_lmhead_logprob(const void* hidden, const void* weight, int64_t T, int6
 int drift_lmhead_logprob_vh(const void* hidden, const void* weight_vh, int64_t T, int64_t H,
                             int64_t V, const int32_t* target_ids, const uint8_t* active,
                             float* logp, void* ws, size_t ws_bytes, void* stream);
+
+/* The fused LM-head with a transform chain on the head's logits before the softmax
+ * ("[WS2] Framework for ablation experiment", LogProb knobs row 7, temperature /
+ * logit_scale / soft_cap, applied to the logits that rows 9-10 form and reduce in one
+ * pass): logp[t] = chain(z)[t, y_t] - LSE(chain(z)[t]). The logits stay on chip, so a
+ * model whose final logits are soft-capped needs the cap here.
+ *   weight_layout  DRIFT_WEIGHT_HV (weight bf16 [H, V], as drift_lmhead_logprob) or
+ *                  DRIFT_WEIGHT_VH (bf16 [V, H], as drift_lmhead_logprob_vh); the
+ *                  workspace is that entry point's
+ *   transform      the chain (nullable or count 0: the entry point without a chain, bit
+ *                  for bit). It must fold (see the transform arithmetic above: at most one
+ *                  SOFTCAP step, |cap x later factors| <= 40), else DRIFT_EINVAL. The
+ *                  log-sum-exp terms take the folded form, the selected logit the steps one
+ *                  by one; the tile and merge order are those of the entry point without a
+ *                  chain, so a row's result is bitwise the same in any batch.
+ * Other arguments, limits and statuses as drift_lmhead_logprob. */
+#define DRIFT_WEIGHT_HV 0
+#define DRIFT_WEIGHT_VH 1
+int drift_lmhead_logprob_chain(const void* hidden, const void* weight, int weight_layout,
+                               int64_t T, int64_t H, int64_t V, const int32_t* target_ids,
+                               const uint8_t* active, const drift_transform* transform,
+                               float* logp, void* ws, size_t ws_bytes, void* stream);
 
 /* Gradient of the selected-token logprob of one side with respect to its stored logits
  * ("[WS2] Framework for ablation experiment", LogProb knobs row 11: dlogits), for the

@@ -24,7 +24,7 @@ def test_header_declares_the_boundary():
                             "drift_shard_partials", "drift_merge_shards",
                             "drift_active_rows", "drift_backend_descriptor",
                             "drift_strerror", "drift_diagnostics_noalloc",
-                            "drift_lmhead_logprob_vh"])
+                            "drift_lmhead_logprob_vh", "drift_lmhead_logprob_chain"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -51,7 +51,7 @@ def test_struct_layouts_match_header():
 def test_descriptor_and_strerror():
     from train_rollout_logprob_amd import binding as B
     d = B.drift_backend_descriptor()
-    assert d["abi_version"] == 8 and d["archs"] == "gfx950"
+    assert d["abi_version"] == 9 and d["archs"] == "gfx950"
     assert "batch composition" in d["determinism"]
     assert d["lse_domain"] == "natural log"
     assert d["build_fingerprint"].startswith("src:")
@@ -134,6 +134,24 @@ def test_host_checks_fail_closed_without_launching():
                   None) == B.DRIFT_EWORKSPACE
         assert fn(big, big, 3530753, 4096, 151936, big, None, big, big, 1 << 40,
                   None) == B.DRIFT_EINVAL
+    # the chain entry point: layout and chain checked before the workspace; chains that
+    # do not fold (two soft-caps, a cap above 40) are refused
+    fc = lambda layout, chain, ws_bytes: lib.drift_lmhead_logprob_chain(
+        big, big, layout, 4, 64, 16, big, None,
+        ctypes.byref(chain) if chain is not None else None, big, big, ws_bytes, None)
+    for chain, want in (([("softcap", 30.0)], B.DRIFT_EWORKSPACE),
+                        ([("temperature", 0.7), ("scale", -2.0)], B.DRIFT_EWORKSPACE),
+                        ([], B.DRIFT_EWORKSPACE),
+                        ([("softcap", 30.0), ("softcap", 20.0)], B.DRIFT_EINVAL),
+                        ([("softcap", 60.0)], B.DRIFT_EINVAL),
+                        ([("softcap", 30.0), ("scale", 2.0)], B.DRIFT_EINVAL),
+                        ([("temperature", 0.0)], B.DRIFT_EINVAL)):
+        t = B.drift_transform()
+        B.set_chain(t, chain)
+        for layout in (B.DRIFT_WEIGHT_HV, B.DRIFT_WEIGHT_VH):
+            assert fc(layout, t, 64) == want, (chain, layout)
+    assert fc(2, None, 1 << 40) == B.DRIFT_EINVAL                      # unknown layout
+    assert fc(B.DRIFT_WEIGHT_HV, None, 64) == B.DRIFT_EWORKSPACE       # no chain
     for op in (B.DRIFT_OP_LMHEAD, B.DRIFT_OP_LMHEAD_VH):
         assert B.drift_workspace_size(op, 3530752, 151936, 4096, B.DRIFT_BF16) > 0
         assert B.drift_workspace_size(op, 3530753, 151936, 4096, B.DRIFT_BF16) == 0

@@ -22,9 +22,10 @@ def _bits(t):
     return t.cpu().view(torch.int16).numpy().view(np.uint16)
 
 
-def _oracle(case, rows):
+def _oracle(case, rows, transforms=None):
     w64 = oracle.widen(_bits(case.weight), "bf16").reshape(case.H, case.V)
-    return oracle.lmhead_logprob(_bits(case.hidden), w64, case.ids, rows=rows)
+    return oracle.lmhead_logprob(_bits(case.hidden), w64, case.ids, rows=rows,
+                                 transforms=transforms)
 
 
 # The last two shapes span hundreds of tiles (more than one per compute unit) with ragged
@@ -130,3 +131,101 @@ def test_full_size_sampled_rows_and_invariance():
                                       check=True)
             g = np.float32(got[slot].item())
             assert g.view(np.uint32) == full[pr].view(np.uint32), (bs, pr)
+
+
+# chains on the head's logits (all fold: at most one soft-cap, |cap x later factors| <= 40)
+HEAD_CHAINS = {
+    "softcap30": [("softcap", 30.0)],
+    "temp_softcap": [("temperature", 0.7), ("softcap", 15.0)],
+    "scale_neg_softcap": [("scale", -1.5), ("softcap", 10.0), ("scale", 2.0)],
+    # a multiplying chain only (on these scaled weights, a temperature above 1 keeps the
+    # logits at a few units; the fp32 GEMM's own error grows with their size)
+    "temperature": [("temperature", 2.0)],
+}
+
+
+@pytest.mark.parametrize("chain", list(HEAD_CHAINS))
+@pytest.mark.parametrize("T,H,V", [(300, 264, 1000), (77, 520, 4104), (2000, 256, 20008)])
+def test_chain_parity_ragged_shapes(T, H, V, chain):
+    """drift_lmhead_logprob_chain against the oracle's head with the same chain, for both
+    weight layouts (bitwise the same results), with ragged token and vocabulary edges."""
+    from train_rollout_logprob_amd import binding as B
+    print(f"[case] lmhead chain={chain} T={T} H={H} V={V}", flush=True)
+    case = synth.make_lmhead_case(device="cuda", T=T, H=H, V=V)
+    # logits of a few units, so that the caps bite
+    case.weight.mul_(20.0)
+    ids = torch.as_tensor(case.ids, device="cuda")
+    tr = HEAD_CHAINS[chain]
+    logp, ws = B.lmhead_logprob(case.hidden, case.weight, ids, check=True, transforms=tr)
+    want = _oracle(case, None, tr)
+    err = np.abs(logp.cpu().numpy().astype(np.float64) - want)
+    print(f"[case] max err {err.max():.3e}", flush=True)
+    assert err.max() <= LOGP_TOL
+    w_vh = case.weight.t().contiguous()
+    logp_vh, _ = B.lmhead_logprob(case.hidden, w_vh, ids, check=True, weight_layout="vh",
+                                  transforms=tr)
+    assert torch.equal(logp_vh.view(torch.int32), logp.view(torch.int32))
+
+
+def test_identity_chain_is_bitwise_the_plain_head():
+    from train_rollout_logprob_amd import binding as B
+    case = synth.make_lmhead_case(device="cuda", T=300, H=264, V=1000)
+    ids = torch.as_tensor(case.ids, device="cuda")
+    plain, _ = B.lmhead_logprob(case.hidden, case.weight, ids, check=True)
+    for tr in ([("scale", 1.0)], [("temperature", 1.0)]):
+        got, _ = B.lmhead_logprob(case.hidden, case.weight, ids, check=True, transforms=tr)
+        assert torch.equal(got.view(torch.int32), plain.view(torch.int32)), tr
+
+
+def test_chain_refused_when_it_does_not_fold():
+    from train_rollout_logprob_amd import binding as B
+    case = synth.make_lmhead_case(device="cuda", T=16, H=64, V=256)
+    ids = torch.as_tensor(case.ids, device="cuda")
+    for tr in ([("softcap", 30.0), ("softcap", 20.0)], [("softcap", 50.0)]):
+        with pytest.raises(B.DriftError):
+            B.lmhead_logprob(case.hidden, case.weight, ids, transforms=tr)
+
+
+def test_chain_batch_composition_control_is_bitwise_zero():
+    """With a soft-cap on the logits, rows re-scored in batches of 1, 7 and 64 at other
+    positions are bitwise equal to the full batch."""
+    from train_rollout_logprob_amd import binding as B
+    T, H, V = 2048, 1024, 16384
+    case = synth.make_lmhead_case(device="cuda", T=T, H=H, V=V)
+    case.weight.mul_(20.0)
+    ids = torch.as_tensor(case.ids, device="cuda")
+    tr = [("softcap", 30.0)]
+    full, _ = B.lmhead_logprob(case.hidden, case.weight, ids, check=True, transforms=tr)
+    full = full.cpu().numpy()
+    rng = np.random.default_rng(13)
+    for bs in (1, 7, 64):
+        for pr in (0, 5, 1000, T - 1):
+            rows = rng.integers(0, T, bs)
+            slot = int(rng.integers(0, bs))
+            rows[slot] = pr
+            idx = torch.as_tensor(rows, device="cuda")
+            got, _ = B.lmhead_logprob(case.hidden.index_select(0, idx).contiguous(),
+                                      case.weight, ids.index_select(0, idx).contiguous(),
+                                      check=True, transforms=tr)
+            g = np.float32(got[slot].item())
+            assert g.view(np.uint32) == full[pr].view(np.uint32), (bs, pr)
+
+
+@pytest.mark.slow
+def test_full_size_chain_sampled_rows():
+    """The timed head shape with a soft-cap of 10 on logits scaled to a few units (std 6.4):
+    256 rows (the first, the last and 254 drawn) against the oracle."""
+    from train_rollout_logprob_amd import binding as B
+    case = synth.make_lmhead_case(device="cuda")
+    case.weight.mul_(5.0)
+    ids = torch.as_tensor(case.ids, device="cuda")
+    tr = [("softcap", 10.0)]
+    logp, ws = B.lmhead_logprob(case.hidden, case.weight, ids, check=True, transforms=tr)
+    full = logp.cpu().numpy()
+    rng = np.random.default_rng(14)
+    drawn = rng.choice(np.arange(1, case.T - 1), 254, replace=False)
+    rows = np.unique(np.concatenate([[0, case.T - 1], drawn]))
+    want = _oracle(case, rows, tr)
+    err = np.abs(full[rows].astype(np.float64) - want)
+    print(f"[case] lmhead chain full max err {err.max():.3e} over {len(rows)} rows", flush=True)
+    assert err.max() <= LOGP_TOL

@@ -33,6 +33,7 @@ DRIFT_PAD_RIGHT, DRIFT_PAD_LEFT, DRIFT_PACKED = 0, 1, 2
 LAYOUTS = {"right": DRIFT_PAD_RIGHT, "left": DRIFT_PAD_LEFT, "packed": DRIFT_PACKED}
 DRIFT_OP_SELECTED_LOGPROB, DRIFT_OP_DIAGNOSTICS, DRIFT_OP_LMHEAD, DRIFT_OP_ACTIVE_ROWS = 0, 1, 2, 3
 DRIFT_OP_LMHEAD_VH = 4
+DRIFT_WEIGHT_HV, DRIFT_WEIGHT_VH = 0, 1
 DRIFT_XF_SCALE, DRIFT_XF_TEMPERATURE, DRIFT_XF_SOFTCAP = 1, 2, 3
 DRIFT_MAX_TRANSFORMS = 4
 DRIFT_REDUCE_TREE, DRIFT_REDUCE_EXACT = 0, 1
@@ -46,7 +47,7 @@ EXPORTS = ("drift_workspace_size", "drift_selected_logprob", "drift_get_status",
            "drift_diagnostics", "drift_segment_diagnostics", "drift_lmhead_logprob",
            "drift_dlogits", "drift_shard_partials", "drift_merge_shards",
            "drift_active_rows", "drift_backend_descriptor", "drift_strerror",
-           "drift_diagnostics_noalloc", "drift_lmhead_logprob_vh")
+           "drift_diagnostics_noalloc", "drift_lmhead_logprob_vh", "drift_lmhead_logprob_chain")
 DRIFT_NOALLOC_MAX_ROWS = 1 << 22
 
 
@@ -123,6 +124,9 @@ def _load():
     lib.drift_lmhead_logprob.restype = ctypes.c_int
     lib.drift_lmhead_logprob_vh.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]
     lib.drift_lmhead_logprob_vh.restype = ctypes.c_int
+    lib.drift_lmhead_logprob_chain.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, vp, vp,
+                                               ctypes.POINTER(drift_transform), vp, vp, sz, vp]
+    lib.drift_lmhead_logprob_chain.restype = ctypes.c_int
     lib.drift_dlogits.argtypes = [ctypes.POINTER(drift_logprob_args), ctypes.c_int, vp, vp, vp,
                                   ctypes.c_int, vp, i64, vp]
     lib.drift_dlogits.restype = ctypes.c_int
@@ -204,6 +208,16 @@ def drift_lmhead_logprob_vh(hidden, weight_vh, T: int, H: int, V: int, target_id
     return int(lib.drift_lmhead_logprob_vh(_ptr(hidden), _ptr(weight_vh), T, H, V,
                                            _ptr(target_ids), _ptr(active), _ptr(logp), _ptr(ws),
                                            ws_bytes, _stream(stream)))
+
+
+def drift_lmhead_logprob_chain(hidden, weight, weight_layout: int, T: int, H: int, V: int,
+                               target_ids, active, transform, logp, ws, ws_bytes: int,
+                               stream=None) -> int:
+    """`transform`: a drift_transform, or None."""
+    return int(lib.drift_lmhead_logprob_chain(
+        _ptr(hidden), _ptr(weight), weight_layout, T, H, V, _ptr(target_ids), _ptr(active),
+        ctypes.byref(transform) if transform is not None else None, _ptr(logp), _ptr(ws),
+        ws_bytes, _stream(stream)))
 
 
 def drift_dlogits(args: drift_logprob_args, side: int, lse, active, grad_logp, out_dtype: int,
@@ -579,10 +593,11 @@ class ScoringStep:
 
 
 def lmhead_logprob(hidden, weight, ids, active=None, ws=None, out=None, stream=None,
-                   check=False, weight_layout="hv"):
+                   check=False, weight_layout="hv", transforms=None):
     """Call drift_lmhead_logprob on torch tensors: hidden bf16 [T, H], weight bf16 [H, V]
     (weight_layout "hv") or [V, H] ("vh": drift_lmhead_logprob_vh, read in place), ids
-    int32 [T], active uint8 [T] or None. Returns (logp, ws)."""
+    int32 [T], active uint8 [T] or None; `transforms`: an optional chain [(kind, value),
+    ...] on the head's logits (drift_lmhead_logprob_chain). Returns (logp, ws)."""
     T, H = hidden.shape
     if weight_layout == "hv":
         H2, V = weight.shape
@@ -602,7 +617,15 @@ def lmhead_logprob(hidden, weight, ids, active=None, ws=None, out=None, stream=N
         ws = workspace(op, T, V, DRIFT_BF16, hidden.device, hidden_dim=H)
     if out is None:
         out = torch.empty(T, dtype=torch.float32, device=hidden.device)
-    st = fn(hidden, weight, T, H, V, ids, active, out, ws, ws.numel(), stream)
+    if transforms:
+        t = drift_transform()
+        set_chain(t, transforms)
+        layout = DRIFT_WEIGHT_VH if weight_layout == "vh" else DRIFT_WEIGHT_HV
+        name = "drift_lmhead_logprob_chain"
+        st = drift_lmhead_logprob_chain(hidden, weight, layout, T, H, V, ids, active, t, out,
+                                        ws, ws.numel(), stream)
+    else:
+        st = fn(hidden, weight, T, H, V, ids, active, out, ws, ws.numel(), stream)
     if st != DRIFT_OK:
         raise DriftError(st, name)
     if check:

@@ -386,7 +386,7 @@ namespace {
 
 int lmhead_call(const void* hidden, const void* weight, bool w_vh, int64_t T, int64_t H,
                 int64_t V, const int32_t* target_ids, const uint8_t* active, float* logp,
-                void* ws, size_t ws_bytes, void* stream) {
+                void* ws, size_t ws_bytes, void* stream, const drift_transform* chain) {
   if (T < 0 || T > INT32_MAX || H < 1 || V < 1 || V > INT32_MAX) return DRIFT_EINVAL;
   if (H % 8 != 0 || V % 8 != 0 || H > (int64_t{1} << 22)) return DRIFT_EINVAL;
   if (!lmhead_shape_ok(T, V)) return DRIFT_EINVAL;
@@ -394,9 +394,15 @@ int lmhead_call(const void* hidden, const void* weight, bool w_vh, int64_t T, in
   if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(target_ids, 4) ||
       !aligned(logp, 4))
     return DRIFT_EINVAL;
+  LmheadParams lp;
+  lp.xf = Chain{};
+  if (chain && chain->count > 0) {  // the head takes folded chains only (rowio.h)
+    if (!chain_ok(*chain)) return DRIFT_EINVAL;
+    lp.xf = make_chain(*chain);
+    if (lp.xf.kind == 0) return DRIFT_EINVAL;
+  }
   if (!ws || !aligned(ws, 256) || ws_bytes < lmhead_ws_bytes(T, H, V, w_vh))
     return DRIFT_EWORKSPACE;
-  LmheadParams lp;
   lp.T = T;
   lp.H = H;
   lp.V = V;
@@ -419,14 +425,23 @@ int drift_lmhead_logprob(const void* hidden, const void* weight, int64_t T, int6
                          const int32_t* target_ids, const uint8_t* active, float* logp,
                          void* ws, size_t ws_bytes, void* stream) {
   return lmhead_call(hidden, weight, false, T, H, V, target_ids, active, logp, ws, ws_bytes,
-                     stream);
+                     stream, nullptr);
 }
 
 int drift_lmhead_logprob_vh(const void* hidden, const void* weight_vh, int64_t T, int64_t H,
                             int64_t V, const int32_t* target_ids, const uint8_t* active,
                             float* logp, void* ws, size_t ws_bytes, void* stream) {
   return lmhead_call(hidden, weight_vh, true, T, H, V, target_ids, active, logp, ws, ws_bytes,
-                     stream);
+                     stream, nullptr);
+}
+
+int drift_lmhead_logprob_chain(const void* hidden, const void* weight, int weight_layout,
+                               int64_t T, int64_t H, int64_t V, const int32_t* target_ids,
+                               const uint8_t* active, const drift_transform* transform,
+                               float* logp, void* ws, size_t ws_bytes, void* stream) {
+  if (weight_layout != DRIFT_WEIGHT_HV && weight_layout != DRIFT_WEIGHT_VH) return DRIFT_EINVAL;
+  return lmhead_call(hidden, weight, weight_layout == DRIFT_WEIGHT_VH, T, H, V, target_ids,
+                     active, logp, ws, ws_bytes, stream, transform);
 }
 
 int drift_dlogits(const drift_logprob_args* a, int side, const double* lse,

@@ -114,6 +114,7 @@ hipError_t launch_diagnostics(const DiagParams& p, hipStream_t s);
 struct LmheadParams {
   int64_t T, H, V;
   bool w_vh;  // weight stored [V, H] (K contiguous) instead of [H, V]
+  Chain xf;   // transform chain of the head's logits (n = 0: none)
   const void* hidden;
   const void* weight;
   const int32_t* ids;

@@ -187,6 +187,7 @@ struct GemmArgs {
   const int32_t* ids;
   Partial* part;        // [nVt, Tp]
   float* zsel;          // [Tp]
+  Chain xf;             // transform chain of the logits (used by the XF kernel only)
 };
 
 // Epilogue of the GEMM kernels: each token's logits of this block become one (k, s)
@@ -199,7 +200,7 @@ struct GemmArgs {
 // out of its 64 values with a select tree on the offset's bits and stores it once. The two
 // vocab waves of a token merge through LDS (wave wv = 1 writes the partials of all its
 // tokens, one barrier, wave wv = 0 merges and stores).
-template <int TM, int TN, int WV, int WT, bool FULL>
+template <int TM, int TN, int WV, int WT, bool FULL, bool XF>
 __device__ __forceinline__ void lse_epilogue(const f32x16 (&acc)[TM][TN], const GemmArgs& a,
                                              int64_t vt, int64_t v0, int64_t t0, int wv, int wt,
                                              int lr, int lh, float (*s_k)[WT],
@@ -221,7 +222,7 @@ __device__ __forceinline__ void lse_epilogue(const f32x16 (&acc)[TM][TN], const 
 #pragma unroll
     for (int i = 0; i < NZ; ++i) {
       const int off = 32 * (i >> 4) + 8 * ((i & 15) >> 2) + (i & 3);
-      z[i] = (FULL || off < vlim) ? acc[i >> 4][in][i & 15] : -INFINITY;
+      z[i] = (XF || FULL || off < vlim) ? acc[i >> 4][in][i & 15] : -INFINITY;
     }
     if (yrel >= 0 && (yrel & 4) == 0) {
       // the owner: i = 16 (bits 5-6) + 4 (bits 3-4) + (bits 0-1) of the offset, picked by a
@@ -238,7 +239,32 @@ __device__ __forceinline__ void lse_epilogue(const f32x16 (&acc)[TM][TN], const 
 #pragma unroll
         for (int q = 0; q < n; ++q) u[q] = (mb & u[2 * q + 1]) | (~mb & u[2 * q]);
       }
-      a.zsel[t] = __uint_as_float(u[0]);
+      float zs = __uint_as_float(u[0]);
+      if constexpr (XF) {  // the selected logit takes the chain step by step
+        float one[1] = {zs};
+        apply_chain<1>(one, a.xf);
+        zs = one[0];
+      }
+      a.zsel[t] = zs;
+    }
+    if constexpr (XF) {
+      // the logits through the chain: folded (rowio.h) or step by step; rows past V are
+      // -inf after it
+      if (a.xf.kind == 2) {
+        fold_values<NZ>(z, a.xf);
+#pragma unroll
+        for (int i = 0; i < NZ; ++i) z[i] = fmaf(a.xf.fb, z[i], a.xf.fa);
+      } else {  // kind 1 (the entry point takes folded chains only)
+#pragma unroll
+        for (int i = 0; i < NZ; ++i) z[i] = z[i] * a.xf.fb;
+      }
+      if constexpr (!FULL) {
+#pragma unroll
+        for (int i = 0; i < NZ; ++i) {
+          const int off = 32 * (i >> 4) + 8 * ((i & 15) >> 2) + (i & 3);
+          if (off >= vlim) z[i] = -INFINITY;
+        }
+      }
     }
     float m = -INFINITY;
 #pragma unroll
@@ -298,6 +324,7 @@ __device__ __forceinline__ void lse_epilogue(const f32x16 (&acc)[TM][TN], const 
 // the fragment reads (16 lanes = 16 consecutive rows at one logical chunk) hit 16 distinct
 // 4-bank groups. The four buffers (A and B, two stages) are separate LDS arrays and the
 // stage loop is unrolled by two, so every access names its buffer at compile time.
+template <bool XF>
 __global__ void __launch_bounds__(kPThreads, 1) lm_gemm_lse(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[kBV * kBK];
   __shared__ __attribute__((aligned(1024))) uint16_t sA1[kBV * kBK];
@@ -467,9 +494,9 @@ __global__ void __launch_bounds__(kPThreads, 1) lm_gemm_lse(GemmArgs a) {
   __syncthreads();
 
   if (v0 + kBV <= a.V)  // block-uniform
-    lse_epilogue<kPT, kPU, kPW, kPN, true>(acc, a, vt, v0, t0, wv, wt, lr, lh, s_k, s_s);
+    lse_epilogue<kPT, kPU, kPW, kPN, true, XF>(acc, a, vt, v0, t0, wv, wt, lr, lh, s_k, s_s);
   else
-    lse_epilogue<kPT, kPU, kPW, kPN, false>(acc, a, vt, v0, t0, wv, wt, lr, lh, s_k, s_s);
+    lse_epilogue<kPT, kPU, kPW, kPN, false, XF>(acc, a, vt, v0, t0, wv, wt, lr, lh, s_k, s_s);
 }
 
 // Four lanes per token: lane q folds the vocab tiles [q*c, (q+1)*c) in ascending order
@@ -604,7 +631,11 @@ hipError_t launch_lmhead(const LmheadParams& p, hipStream_t s) {
   g.part = (Partial*)(p.ws + l.part_off);
   g.zsel = (float*)(p.ws + l.zsel_off);
   const int64_t nblocks = g.nVt_pad * g.nTt_pad;
-  hipLaunchKernelGGL(lm_gemm_lse, dim3((unsigned)nblocks), dim3(kPThreads), 0, s, g);
+  g.xf = p.xf;
+  if (p.xf.n > 0)
+    hipLaunchKernelGGL(lm_gemm_lse<true>, dim3((unsigned)nblocks), dim3(kPThreads), 0, s, g);
+  else
+    hipLaunchKernelGGL(lm_gemm_lse<false>, dim3((unsigned)nblocks), dim3(kPThreads), 0, s, g);
   hipLaunchKernelGGL(lm_merge, dim3((unsigned)((p.T * kMergeSplit + 255) / 256)), dim3(256), 0, s,
                      g.part,
                      g.zsel, p.ids, p.active, p.logp, p.T, l.Tp, p.V, l.nVt, p.ws);
