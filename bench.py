@@ -198,8 +198,9 @@ def cpu_baseline(pool, sample, budget_s):
 
 def lmhead_leg(steps=5, warmup=2):
     """Fused LM-head workload (hidden [16384, 4096] x W [4096, 151936], bf16): the whole
-    drift_lmhead_logprob call timed with events on the launch stream; beside it, for
-    context, the vendor library's plain GEMM of the same shape (logits written out)."""
+    drift_lmhead_logprob call timed with events on the launch stream, the [V, H] weight
+    layout with and without a soft-cap on the logits; beside it, for context, the vendor
+    library's plain GEMM of the same shape (logits written out)."""
     import torch
 
     from train_rollout_logprob_amd import binding as B
@@ -250,6 +251,26 @@ def lmhead_leg(steps=5, warmup=2):
                         "frac": flop / (vh_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                         "bitwise_equal_to_hv": bool(torch.equal(out_vh.view(torch.int32),
                                                                 lp.view(torch.int32)))}
+    # the same [V, H] call with a soft-cap of 30 on the head's logits
+    # (drift_lmhead_logprob_chain; the cap is folded into the epilogue)
+    chain = [("softcap", 30.0)]
+    for _ in range(warmup):
+        B.lmhead_logprob(case.hidden, w_vh, ids, ws=ws, out=out_vh, weight_layout="vh",
+                         transforms=chain)
+    e0.record()
+    for _ in range(steps):
+        B.lmhead_logprob(case.hidden, w_vh, ids, ws=ws, out=out_vh, weight_layout="vh",
+                         transforms=chain)
+    e1.record()
+    torch.cuda.synchronize()
+    st, _ = B.drift_get_status(ws)
+    if st != B.DRIFT_OK:
+        raise RuntimeError(f"lmhead with a soft-cap: status {B.STATUS_NAMES[st]}")
+    cap_ms = e0.elapsed_time(e1) / steps
+    out["weight_vh_softcap"] = {"what": "drift_lmhead_logprob_chain, W as [V, H], soft-cap 30 "
+                                        "on the logits", "ms_per_call": cap_ms,
+                                "tflops": flop / (cap_ms * 1e-3) / 1e12,
+                                "frac": flop / (cap_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
     del ws, w_vh
     torch.cuda.empty_cache()
     # context, not the product path: the plain bf16 GEMM of the same shape through the
