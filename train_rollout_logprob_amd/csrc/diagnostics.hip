@@ -8,11 +8,12 @@
 //                  non-finite counts and the largest key with its first row, written as
 //                  one partial per tile;
 //   diag_select    one block of kSelThreads: folds the tile partials in a fixed order (lane
-//                  j of wave 0 takes tiles j, j + 64, ..., then the 64 lane results in lane
-//                  order) into the statistics, derives the nearest ranks and runs the
-//                  three-digit radix select over all keys with LDS histograms, one per
-//                  quantile; the first 16 keys of each thread are read once into
-//                  registers, any further keys are re-read per digit (they stay in L2).
+//                  j of wave 0 takes tiles j, j + 64, ... in ascending order, then the 64
+//                  lane results by the lane butterfly) into the statistics, derives the
+//                  nearest ranks and runs the three-digit radix select over all keys with
+//                  LDS histograms, one per quantile; the first 16 keys of each thread are
+//                  read once into registers (the later digits count only those whose first
+//                  digit matches), any further keys are re-read per digit (they stay in L2).
 // diag_segments (drift_segment_diagnostics) computes the same statistics per segment of
 // rows (per sequence, per batch row or per rank) in one launch, one block per segment.
 // Every statistics record also carries mismatch_kl = -mean(d), the k1 estimator of
@@ -113,13 +114,24 @@ __device__ __forceinline__ unsigned long long wave_max(unsigned long long v) {
 // a second wave scan finds the bin. Counts are 32-bit (a total never exceeds the number
 // of rows, below 2^31). The caller separates this from the histogram writes and from the
 // next reads of s_prefix / s_rank with block barriers.
+// Inclusive prefix sum over the 64 lanes of a fully active wave: Hillis-Steele steps of
+// 1, 2, 4 and 8 lanes inside each row of 16 lanes (DPP row_shr; a lane with no source lane
+// adds 0), then each row adds the totals of the rows before it (lanes 15, 31, 47, read as
+// wave-uniform values). All ALU and no LDS round trip.
+template <int kCtrl>
+__device__ __forceinline__ unsigned int row_shr_or_zero(unsigned int v) {
+  return (unsigned int)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, 0xf, 0xf, false);
+}
 __device__ __forceinline__ unsigned int wave_incl_scan(unsigned int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const unsigned int t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
-  return v;
+  v += row_shr_or_zero<0x111>(v);  // row_shr:1
+  v += row_shr_or_zero<0x112>(v);  // row_shr:2
+  v += row_shr_or_zero<0x114>(v);  // row_shr:4
+  v += row_shr_or_zero<0x118>(v);  // row_shr:8
+  const unsigned int t0 = (unsigned int)__builtin_amdgcn_readlane((int)v, 15);
+  const unsigned int t1 = (unsigned int)__builtin_amdgcn_readlane((int)v, 31);
+  const unsigned int t2 = (unsigned int)__builtin_amdgcn_readlane((int)v, 47);
+  const int row = lane >> 4;
+  return v + (row > 0 ? t0 : 0u) + (row > 1 ? t1 : 0u) + (row > 2 ? t2 : 0u);
 }
 
 __device__ void pick_digits(const unsigned int* h0, const unsigned int* h1, int shift,
@@ -146,7 +158,7 @@ __device__ void pick_digits(const unsigned int* h0, const unsigned int* h1, int 
     const unsigned int ex = inc[q] - mine[q];
     const unsigned long long own = __ballot(ex < rk && rk <= inc[q]);  // exactly one lane
     blk[q] = own ? (unsigned int)(__ffsll((long long)own) - 1) : 0u;
-    rank[q] = rk - (unsigned int)__shfl((int)ex, (int)blk[q]);
+    rank[q] = rk - (unsigned int)__builtin_amdgcn_readlane((int)ex, (int)blk[q]);
     cnt[q] = lane < PER ? h[q][blk[q] * PER + lane] : 0u;
   }
 #pragma unroll
@@ -179,8 +191,10 @@ __device__ __forceinline__ void add_row(RowStats& a, float df, int64_t r, double
   a.s_exp += e;
   a.s_kl += expm1(v) - v;
   a.s_d += v;
-  if (e < lo_edge) ++a.lo;
-  else if (e > hi_edge) ++a.hi;
+  // lo_edge <= hi_edge, so at most one of the two holds (NaN: neither); counted without a
+  // branch, which keeps both counters in registers
+  a.lo += e < lo_edge ? 1 : 0;
+  a.hi += e > hi_edge ? 1 : 0;
   if (!isfinite(df)) ++a.nf;
   const unsigned long long cand = ((unsigned long long)key_of(df) << 32) |
                                   (unsigned long long)(0xffffffffu - (unsigned int)r);
@@ -199,10 +213,9 @@ __device__ __forceinline__ void add_stats(RowStats& a, const RowStats& b) {
   a.best = b.best > a.best ? b.best : a.best;
 }
 
-// Block-cooperative; the total is returned in thread 0.
-__device__ RowStats block_reduce(RowStats a) {
-  __shared__ RowStats s_w[kDiagThreads / 64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Lane butterfly (xor 32, 16, ..., 1) over a fully active wave; every lane ends with the
+// total, the fp64 sums in an order fixed by the lane count.
+__device__ __forceinline__ RowStats wave_reduce(RowStats a) {
   a.s_abs = wave_sum(a.s_abs);
   a.s_exp = wave_sum(a.s_exp);
   a.s_kl = wave_sum(a.s_kl);
@@ -212,6 +225,14 @@ __device__ RowStats block_reduce(RowStats a) {
   a.hi = wave_sum(a.hi);
   a.nf = wave_sum(a.nf);
   a.best = wave_max(a.best);
+  return a;
+}
+
+// Block-cooperative; the total is returned in thread 0.
+__device__ RowStats block_reduce(RowStats a) {
+  __shared__ RowStats s_w[kDiagThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  a = wave_reduce(a);
   if (lane == 0) s_w[wave] = a;
   __syncthreads();
   RowStats t = {};
@@ -336,14 +357,14 @@ __device__ __forceinline__ void keys4(const float* d, const uint8_t* active, int
 // pass issues a quarter of the load instructions. Digit h of a
 // quantile counts, in LDS, the keys whose upper digits match the ones chosen so far; the
 // first digit's histogram is shared by both quantiles.
+// select_keys issues the loads of the cached keys (a caller may overlap them with other
+// work) and returns whether the vector path applies; radix_select then runs the digits.
 template <int NT, int KC>
-__device__ void radix_select(const float* d, const uint8_t* active, int64_t lo, int64_t hi,
-                             unsigned int (*s_hist)[kBins], long long* s_rank,
-                             unsigned int* s_prefix) {
+__device__ __forceinline__ bool select_keys(const float* d, const uint8_t* active, int64_t lo,
+                                            int64_t hi, unsigned int (&ck)[KC]) {
   static_assert(KC % 4 == 0, "the vector path caches groups of four rows");
   const int tid = threadIdx.x;
   const bool vec = lo == 0 && ((uintptr_t)d & 15) == 0 && ((uintptr_t)active & 3) == 0;
-  unsigned int ck[KC];
   if (vec) {  // block-uniform
 #pragma unroll
     for (int k = 0; k < KC / 4; ++k) {
@@ -364,6 +385,23 @@ __device__ void radix_select(const float* d, const uint8_t* active, int64_t lo, 
 #pragma unroll
     for (int k = 0; k < KC; ++k) ck[k] = a[k] ? key_of(x[k]) : kNoKey;
   }
+  return vec;
+}
+
+//
+// With `s_list` (64 KC keys per wave in LDS), after the first digit each wave packs the
+// cached keys whose first digit matches either quantile's into its own list (ballot and
+// lane count, in lane order), and the later digits count that list instead of every cached
+// key: far fewer LDS atomics when few keys share the selected bins. The counts, and so the
+// result, are the same.
+template <int NT, int KC>
+__device__ void radix_select(const float* d, const uint8_t* active, int64_t lo, int64_t hi,
+                             const unsigned int (&ck)[KC], bool vec,
+                             unsigned int (*s_hist)[kBins], long long* s_rank,
+                             unsigned int* s_prefix, unsigned int* s_list) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  unsigned int* wl = s_list ? s_list + (tid >> 6) * (64 * KC) : nullptr;
+  unsigned int nl = 0;  // wave-uniform length of wl
   const int64_t rest = lo + (int64_t)KC * NT;
   for (int pass = 0; pass < 3; ++pass) {
     for (int b = tid; b < kNumQ * kBins; b += NT) (&s_hist[0][0])[b] = 0;
@@ -381,8 +419,12 @@ __device__ void radix_select(const float* d, const uint8_t* active, int64_t lo, 
         if ((key >> hi_shift) == pre1) atomicAdd(&s_hist[1][(key >> shift) & mask], 1u);
       }
     };
+    if (pass == 0 || !wl) {
 #pragma unroll
-    for (int k = 0; k < KC; ++k) count(ck[k]);
+      for (int k = 0; k < KC; ++k) count(ck[k]);
+    } else {
+      for (unsigned int i = lane; i < nl; i += 64) count(wl[i]);
+    }
     if (vec) {
       for (int64_t base = rest; base < hi; base += (int64_t)NT * kSelBatch) {
         unsigned int kk[kSelBatch / 4][4];
@@ -409,21 +451,52 @@ __device__ void radix_select(const float* d, const uint8_t* active, int64_t lo, 
     __syncthreads();
     pick_digits(s_hist[0], s_hist[pass == 0 ? 0 : 1], shift, s_rank, s_prefix);
     __syncthreads();
+    if (pass == 0 && wl) {  // wl is block-uniform; the next pass's barrier orders the list
+      const unsigned int q0 = s_prefix[0] >> kShift[0], q1 = s_prefix[1] >> kShift[0];
+#pragma unroll
+      for (int k = 0; k < KC; ++k) {
+        const unsigned int key = ck[k];
+        const bool m = key != kNoKey && ((key >> kShift[0]) == q0 || (key >> kShift[0]) == q1);
+        const unsigned long long bm = __ballot(m);
+        const unsigned int below = __builtin_amdgcn_mbcnt_hi(
+            (unsigned int)(bm >> 32), __builtin_amdgcn_mbcnt_lo((unsigned int)bm, 0u));
+        if (m) wl[nl + below] = key;
+        nl += (unsigned int)__popcll(bm);
+      }
+    }
   }
 }
 
 // The whole batch after diag_tile: folds the tile partials, finishes the statistics and
-// selects p95 / p99.
+// selects p95 / p99 (MULTI: from the digit histograms of the multi-block launches, taken
+// above kSelSingleMax rows; else from the keys themselves).
+template <bool MULTI>
 __global__ void __launch_bounds__(kSelThreads) diag_select(DiagParams p) {
   __shared__ unsigned int s_hist[kNumQ][kBins];
   __shared__ long long s_rank[kNumQ];
   __shared__ unsigned int s_prefix[kNumQ];
-  __shared__ RowStats s_lane[64];
   __shared__ long long s_n;
+  __shared__ unsigned int s_list[MULTI ? 1 : kSelThreads * 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const DiagLayout lay = DiagLayout::make(p.N);
   const TilePartial* tp = (const TilePartial*)(p.ws + lay.partial_off);
   drift_stats& S = p.out ? *p.out : ((SelState*)p.ws)->stats;
+  // The selection's inputs are loaded first, so that their latency overlaps the fold: the
+  // digit histograms of the multi-block launches, or the keys this block selects from.
+  constexpr int kHistPer = kNumQ * kBins / kSelThreads;
+  unsigned int hreg[MULTI ? 3 : 1][kHistPer];
+  unsigned int ck[MULTI ? 4 : 16];
+  bool vec = false;
+  if constexpr (MULTI) {
+    const unsigned int* gh = (const unsigned int*)(p.ws + lay.hist_off);
+#pragma unroll
+    for (int pass = 0; pass < 3; ++pass)
+#pragma unroll
+      for (int i = 0; i < kHistPer; ++i)
+        hreg[pass][i] = gh[(pass * kNumQ) * kBins + tid + i * kSelThreads];
+  } else {
+    vec = select_keys<kSelThreads, 16>(p.d, p.active, 0, p.N, ck);
+  }
   if (wave == 0) {
     RowStats a = {};
     // lane j folds tiles j, j + 64, ... in ascending order, loading four at a time
@@ -441,35 +514,31 @@ __global__ void __launch_bounds__(kSelThreads) diag_select(DiagParams p) {
       for (int u = 0; u < 4; ++u)
         if (g0 + 64 * u < lay.G) add_stats(a, bs[u]);
     }
-    s_lane[lane] = a;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    RowStats a = {};
-    for (int g = 0; g < 64; ++g) add_stats(a, s_lane[g]);
-    finish_stats(S, a, p.lp);
-    for (int q = 0; q < kNumQ; ++q) {
-      s_rank[q] = quantile_rank(q, a.n);
-      s_prefix[q] = 0;
+    // then the 64 lane results by the lane butterfly
+    a = wave_reduce(a);
+    if (lane == 0) {
+      finish_stats(S, a, p.lp);
+      for (int q = 0; q < kNumQ; ++q) {
+        s_rank[q] = quantile_rank(q, a.n);
+        s_prefix[q] = 0;
+      }
+      s_n = a.n;
     }
-    s_n = a.n;
   }
   __syncthreads();
   if (s_n == 0) return;  // block-uniform
-  if (p.N > kSelSingleMax) {
-    const unsigned int* gh = (const unsigned int*)(p.ws + lay.hist_off);
+  if constexpr (MULTI) {
+#pragma unroll
     for (int pass = 0; pass < 3; ++pass) {
 #pragma unroll
-      for (int i = 0; i < kNumQ * kBins / kSelThreads; ++i) {
-        const int b = tid + i * kSelThreads;
-        (&s_hist[0][0])[b] = gh[(pass * kNumQ) * kBins + b];
-      }
+      for (int i = 0; i < kHistPer; ++i) (&s_hist[0][0])[tid + i * kSelThreads] = hreg[pass][i];
       __syncthreads();
       pick_digits(s_hist[0], s_hist[pass == 0 ? 0 : 1], kShift[pass], s_rank, s_prefix);
       __syncthreads();
     }
   } else {
-    radix_select<kSelThreads, 16>(p.d, p.active, 0, p.N, s_hist, s_rank, s_prefix);
+    radix_select<kSelThreads, 16>(p.d, p.active, 0, p.N, ck, vec, s_hist, s_rank, s_prefix,
+                                  s_list);
   }
   if (tid == 0) {
     S.p95_abs_dlogp = __uint_as_float(s_prefix[0]);
@@ -501,8 +570,7 @@ __global__ void __launch_bounds__(kPassThreads) diag_pass(DiagParams p) {
     unsigned int c = 0;
 #pragma unroll
     for (int i = 0; i < kBins / kPassThreads; ++i) c += s_hist[0][tid + i * kPassThreads];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) c += (unsigned int)__shfl_xor((int)c, o);
+    c = (unsigned int)__builtin_amdgcn_readlane((int)wave_incl_scan(c, lane), 63);
     if (lane == 0) s_w[wave] = c;
     __syncthreads();
     if (tid < kNumQ) {
@@ -615,7 +683,10 @@ __global__ void __launch_bounds__(kDiagThreads) diag_segments(SegParams p) {
     if (tid == 0) *out = s;
     return;
   }
-  radix_select<kDiagThreads, 8>(p.d, p.active, lo, hi, s_hist, s_rank, s_prefix);
+  unsigned int ck[8];
+  const bool vec = select_keys<kDiagThreads, 8>(p.d, p.active, lo, hi, ck);
+  radix_select<kDiagThreads, 8>(p.d, p.active, lo, hi, ck, vec, s_hist, s_rank, s_prefix,
+                                nullptr);
   if (tid == 0) {
     s.p95_abs_dlogp = __uint_as_float(s_prefix[0]);
     s.p99_abs_dlogp = __uint_as_float(s_prefix[1]);
@@ -670,7 +741,10 @@ hipError_t launch_diagnostics(const DiagParams& p, hipStream_t s) {
     hipLaunchKernelGGL(diag_pass<1>, dim3(nb), dim3(kPassThreads), 0, s, p);
     hipLaunchKernelGGL(diag_pass<2>, dim3(nb), dim3(kPassThreads), 0, s, p);
   }
-  hipLaunchKernelGGL(diag_select, dim3(1), dim3(kSelThreads), 0, s, p);
+  if (p.N > kSelSingleMax)
+    hipLaunchKernelGGL(diag_select<true>, dim3(1), dim3(kSelThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(diag_select<false>, dim3(1), dim3(kSelThreads), 0, s, p);
   return hipGetLastError();
 }
 
