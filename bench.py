@@ -419,6 +419,53 @@ def exact_leg(case, ids, att, act, cu, shards=8, steps=10, warmup=2):
     }
 
 
+def copy_ceiling(src, dst, active, reps=10, warmup=2):
+    """Plain-copy rate (GB/s) of the gradient pass's traffic on the same tensors: every row of
+    `dst` written, the rows of `src` whose `active` byte is set read, one block per row,
+    16-byte nontemporal loads and stores (libdrift_ceiling.so, measurement only); the faster
+    of 4 and 8 loads in flight per lane. HIP events on the launch stream, median."""
+    import torch
+
+    from train_rollout_logprob_amd import build as Bd
+
+    if not os.path.exists(Bd.CEILING_LIB):
+        raise RuntimeError(f"{Bd.CEILING_LIB} is missing: run __graft_entry__.build()")
+    lib = ctypes.CDLL(Bd.CEILING_LIB)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.drift_copy_ceiling.argtypes = [vp, vp, i64, i64, i64, i64, vp, ctypes.c_int, vp]
+    lib.drift_copy_ceiling.restype = ctypes.c_int
+    rows = dst.shape[0]
+    row_bytes = dst.shape[1] * dst.element_size()
+    if src.shape[1] * src.element_size() != row_bytes:
+        raise ValueError("copy ceiling: source and destination rows must have the same size")
+    n_read = int(active.to(torch.bool).sum().item())
+    stream = torch.cuda.current_stream()
+    best = None
+    for unroll in (4, 8):
+        def call():
+            st = lib.drift_copy_ceiling(src.data_ptr(), dst.data_ptr(), rows, row_bytes,
+                                        src.stride(0) * src.element_size(),
+                                        dst.stride(0) * dst.element_size(), active.data_ptr(),
+                                        unroll, stream.cuda_stream)
+            if st != 0:
+                raise RuntimeError(f"drift_copy_ceiling: status {st}")
+
+        for _ in range(warmup):
+            call()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            call()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[reps // 2]
+        gbs = (n_read + rows) * row_bytes / (ms * 1e-3) / 1e9
+        if best is None or gbs > best[0]:
+            best = (gbs, ms, unroll)
+    return best
+
+
 def training_leg(case, ids, att, act, cu, steps=10, warmup=2):
     """Training-only state on the same batch: the scoring kernel with per-row entropy and
     LSE written for both sides (kernel time from events on the launch stream), then
@@ -467,6 +514,11 @@ def training_leg(case, ids, att, act, cu, steps=10, warmup=2):
     torch.cuda.synchronize()
     dl_ms = e0.elapsed_time(e1) / steps
     dl_bytes = n_active * V * esz + N * V * 2
+    dl_gbs = dl_bytes / (dl_ms * 1e-3) / 1e9
+    ceiling = copy_ceiling(case.train, grad, active) if esz == 2 else None
+    if ceiling:
+        log(f"[bench] dlogits {dl_gbs:.0f} GB/s; plain copy of the same rows {ceiling[0]:.0f} GB/s "
+            f"({ceiling[1]:.3f} ms, {ceiling[2]} loads in flight): {dl_gbs / ceiling[0]:.3f} of it")
     del grad
     return {
         "workload": "same batch; entropy + LSE of both sides from the scoring pass, then "
@@ -478,8 +530,13 @@ def training_leg(case, ids, att, act, cu, steps=10, warmup=2):
                                "frac": ent_bytes / (ent_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "dlogits": {"kernel": f"dlogits_rows<{case.dtype}, bf16>", "kernel_ms": dl_ms,
                     "bytes_per_launch": dl_bytes,
-                    "achieved_gbs": dl_bytes / (dl_ms * 1e-3) / 1e9,
-                    "frac": dl_bytes / (dl_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "achieved_gbs": dl_gbs,
+                    "frac": dl_gbs / HBM_PEAK_GBS,
+                    "ceiling_gbs": ceiling[0] if ceiling else None,
+                    "frac_of_ceiling": dl_gbs / ceiling[0] if ceiling else None,
+                    "ceiling_kernel": "copy_rows: the same rows of the train logits copied into "
+                                      "the gradient buffer, inactive rows written as zeros, "
+                                      "16-byte nontemporal loads and stores" if ceiling else None,
                     "traffic": recorded_traffic(DLOGITS_PROFILE, DLOGITS_SOURCES)
                     if case.name == "qwen8b" else None},
     }

@@ -1,11 +1,12 @@
-/* Pure-read bandwidth of the scoring kernels' access pattern, for measurement only.
+/* Plain-transfer bandwidth of the drift kernels' access patterns, for measurement only.
  *
  * The paired scoring pass reads each active row's logits once and is bound by HBM
  * bandwidth; its rate is compared with the GPU's nominal peak. No kernel reaches that
  * figure, so a benchmark also reports the share of what a plain read of the same bytes,
- * with the same access pattern, reaches on the same GPU. This library holds that read and
- * nothing of the method (no operation of the pages is computed here); it is not part of
- * the drift library.
+ * with the same access pattern, reaches on the same GPU; likewise for the gradient pass
+ * (dlogits), which reads active rows and writes every row, against a plain copy of the
+ * same rows. This library holds those transfers and nothing of the method (no operation
+ * of the pages is computed here); it is not part of the drift library.
  *
  * Built as libdrift_ceiling.so beside libdrift.so. Same conventions as drift.h: device
  * pointers, caller-owned memory, stream-ordered, no allocation, no state.
@@ -42,6 +43,23 @@ extern "C" {
  * when the launch fails. Does not synchronize. */
 int drift_read_ceiling(const void* a, const void* b, int64_t rows, int64_t row_bytes,
                        int64_t stride_bytes, uint32_t* sink, void* stream);
+
+/* Copies rows [0, rows) of `src` to `dst` (device memory) as the gradient pass moves them:
+ * one block of 256 threads per row; a row whose `active` byte is non-zero (every row when
+ * `active` is null) is read with 16-byte nontemporal loads, `unroll` loads in flight per
+ * lane, and written with 16-byte nontemporal stores; any other row is written as zeros.
+ *   src, dst      device pointers, 16-byte aligned (may be null when rows == 0)
+ *   rows          0 <= rows < 2^31
+ *   row_bytes     bytes per row: > 0 and a multiple of 16
+ *   src_stride, dst_stride   distances between rows: >= row_bytes, multiples of 16
+ *   active        device uint8 [rows], or null
+ *   unroll        4 or 8
+ *   stream        hipStream_t (null = the default stream)
+ * Returns DRIFT_CEILING_OK, or an error before anything is launched (EINVAL), or EHIP
+ * when the launch fails. Does not synchronize. */
+int drift_copy_ceiling(const void* src, void* dst, int64_t rows, int64_t row_bytes,
+                       int64_t src_stride, int64_t dst_stride, const uint8_t* active,
+                       int unroll, void* stream);
 
 #ifdef __cplusplus
 }

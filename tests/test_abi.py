@@ -246,13 +246,15 @@ def _ceiling_lib():
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.drift_read_ceiling.argtypes = [vp, vp, i64, i64, i64, vp, vp]
     lib.drift_read_ceiling.restype = ctypes.c_int
+    lib.drift_copy_ceiling.argtypes = [vp, vp, i64, i64, i64, i64, vp, ctypes.c_int, vp]
+    lib.drift_copy_ceiling.restype = ctypes.c_int
     return lib
 
 
-def test_ceiling_library_exports_its_declared_symbol():
+def test_ceiling_library_exports_its_declared_symbols():
     src = re.sub(r"/\*.*?\*/", "", open(CEILING_HEADER).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(drift_[a-z_]+)\s*\(", src)))
-    assert names == ["drift_read_ceiling"]
+    assert names == ["drift_copy_ceiling", "drift_read_ceiling"]
     lib = _ceiling_lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -277,6 +279,24 @@ def test_ceiling_host_checks_fail_before_launch():
     ]
     for a, b, rows, rb, st, sink in cases:
         assert lib.drift_read_ceiling(a, b, rows, rb, st, sink, None) == EINVAL, (rows, rb, st)
+    assert lib.drift_copy_ceiling(None, None, 0, 16, 16, 16, None, 8, None) == 0  # no rows
+    copy_cases = [
+        (good, good, -1, 16, 16, 16, 8),               # negative rows
+        (good, good, 1 << 31, 16, 16, 16, 8),          # rows beyond a grid
+        (good, good, 1, 0, 16, 16, 8),                 # empty rows
+        (good, good, 1, 24, 32, 32, 8),                # row bytes not a multiple of 16
+        (good, good, 1, 32, 16, 32, 8),                # source stride below the row
+        (good, good, 1, 32, 32, 16, 8),                # destination stride below the row
+        (good, good, 1, 16, 24, 16, 8),                # stride not a multiple of 16
+        (good, good, 1, 16, 16, 16, 2),                # unsupported unroll
+        (None, good, 1, 16, 16, 16, 8),                # null source
+        (good, None, 1, 16, 16, 16, 4),                # null destination
+        (good + 8, good, 1, 16, 16, 16, 8),            # misaligned source
+        (good, good + 4, 1, 16, 16, 16, 8),            # misaligned destination
+    ]
+    for src, dst, rows, rb, ss, ds, u in copy_cases:
+        assert lib.drift_copy_ceiling(src, dst, rows, rb, ss, ds, None, u, None) == EINVAL, \
+            (rows, rb, ss, ds, u)
 
 
 def test_build_fingerprint_covers_every_source():
