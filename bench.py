@@ -544,8 +544,11 @@ def training_leg(case, ids, att, act, cu, steps=10, warmup=2):
 
 def time_steps(runner, steps, warmup, name):
     """Runs `warmup` untimed and `steps` timed steps of a ScoringStep (scoring kernel
-    bracketed by events on its launch stream, diagnostics, one host sync each). Returns the
-    sorted kernel times (ms) and the wall time of the timed steps (s)."""
+    bracketed by events on its launch stream, then drift_diagnostics_async), pipelined two
+    deep: step i + 1 is launched before the host waits for step i and checks its
+    statistics (status and active count), so the GPU does not idle while the host reads
+    them; the last step is collected before the clock stops. Returns the sorted kernel
+    times (ms), the wall time of the timed steps (s) and the last step's statistics."""
     import torch
 
     from train_rollout_logprob_amd import binding as B
@@ -559,21 +562,36 @@ def time_steps(runner, steps, warmup, name):
     torch.cuda.synchronize()
     handles = [(e0.cuda_event, e1.cuda_event) for e0, e1 in evs]
 
-    def step(i):
-        runner.set_events(*handles[i])
-        st = runner.run()
+    n_active = []
+
+    def check(slot):
+        st = runner.collect(slot)
         if st != B.DRIFT_OK:
             raise RuntimeError(f"{name}: status {B.STATUS_NAMES[st]}")
+        n_active.append(runner.stats_of(slot).n_active)
 
-    for i in range(warmup):
-        step(i)
+    def run(lo, hi):
+        prev = None
+        for i in range(lo, hi):
+            runner.set_events(*handles[i])
+            cur = runner.submit()
+            if prev is not None:
+                check(prev)
+            prev = cur
+        if prev is not None:
+            check(prev)
+        return prev
+
+    run(0, warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(warmup, n_ev):
-        step(i)
+    last = run(warmup, n_ev)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    return sorted(evs[i][0].elapsed_time(evs[i][1]) for i in range(warmup, n_ev)), elapsed
+    if len(set(n_active)) != 1:
+        raise RuntimeError(f"{name}: the steps disagree on the active count: {set(n_active)}")
+    return (sorted(evs[i][0].elapsed_time(evs[i][1]) for i in range(warmup, n_ev)), elapsed,
+            runner.stats_of(last))
 
 
 def transforms_leg(case, ids, att, act, cu, steps=20, warmup=3):
@@ -589,7 +607,7 @@ def transforms_leg(case, ids, att, act, cu, steps=20, warmup=3):
         runner = B.ScoringStep(case.train, case.rollout, ids, att, act, case.layout, case.B,
                                case.L, cu, case.eps_low, case.eps_high,
                                transforms=(chain, chain))
-        kern, _ = time_steps(runner, steps, warmup, f"{case.name} {xf}")
+        kern, _, _ = time_steps(runner, steps, warmup, f"{case.name} {xf}")
         avg = sum(kern) / len(kern)
         out[xf] = {"chain": chain, "kernel": f"score_rows<{case.dtype}, folded chain>",
                    "kernel_ms": avg, "kernel_ms_median": kern[len(kern) // 2],
@@ -604,7 +622,7 @@ def transforms_leg(case, ids, att, act, cu, steps=20, warmup=3):
 
 def score_leg(name, steps, warmup, xf="none", ceiling=True):
     """Generates one scoring workload on cuda:0 and times `steps` steps (scoring +
-    diagnostics, one host sync each) after `warmup` untimed ones. Returns the measurement
+    diagnostics, pipelined two deep) after `warmup` untimed ones. Returns the measurement
     and what later legs reuse (the case, its device inputs and the step runner)."""
     import torch
 
@@ -624,10 +642,10 @@ def score_leg(name, steps, warmup, xf="none", ceiling=True):
     runner = B.ScoringStep(case.train, case.rollout, ids, att, act, case.layout, case.B,
                            case.L, cu, case.eps_low, case.eps_high, transforms=(chain, chain))
     log(f"[bench] {name}: timing {steps} steps")
-    kern, elapsed = time_steps(runner, steps, warmup, name)
+    kern, elapsed, stats = time_steps(runner, steps, warmup, name)
     kern_avg = sum(kern) / len(kern)
-    if runner.stats.n_active != n_active:
-        raise RuntimeError(f"{name}: {runner.stats.n_active} active rows, expected {n_active}")
+    if stats.n_active != n_active:
+        raise RuntimeError(f"{name}: {stats.n_active} active rows, expected {n_active}")
     alg_bytes = n_active * case.V * case.elem_bytes * 2
     achieved = alg_bytes / (kern_avg * 1e-3) / 1e9
     ms_per_step = elapsed * 1e3 / steps
@@ -643,7 +661,7 @@ def score_leg(name, steps, warmup, xf="none", ceiling=True):
                      "kernel": f"score_rows<{case.dtype}>", "kernel_ms": kern_avg,
                      "kernel_ms_median": kern[len(kern) // 2], "kernel_ms_min": kern[0],
                      "bytes_per_launch": alg_bytes},
-        "diagnostics": {k: getattr(runner.stats, k) for k in (
+        "diagnostics": {k: getattr(stats, k) for k in (
             "ratio0", "clipfrac0", "approx_kl0", "mismatch_kl", "mean_abs_dlogp",
             "p95_abs_dlogp", "p99_abs_dlogp", "max_abs_dlogp", "argmax_row")},
     }

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define DRIFT_ABI_VERSION 9
+#define DRIFT_ABI_VERSION 10
 
 /* ---- status codes ---------------------------------------------------------------- */
 #define DRIFT_OK          0
@@ -321,6 +321,24 @@ int drift_get_status(const void* ws, void* stream, int64_t* first_bad_row);
 int drift_diagnostics(const float* dlogp, const uint8_t* active, int64_t num_rows,
                       double eps_low, double eps_high, const void* logprob_ws,
                       drift_stats* out_host, void* ws, size_t ws_bytes, void* stream);
+
+/* drift_diagnostics without the synchronization, for loops that read a step's statistics
+ * while later work runs (a training loop checks step i while step i + 1 is on the GPU).
+ *   out   drift_stats [1], caller-owned, writable by the device: device memory, or pinned
+ *         host memory (hipHostMalloc) that the host reads once the stream has passed this
+ *         call (an event, or a synchronization); its `status` field holds what
+ *         drift_diagnostics would return (DRIFT_OK, DRIFT_ENOACTIVE, DRIFT_ENONFINITE, or
+ *         the logprob_ws status)
+ *   other arguments as drift_diagnostics; ws and out stay in use until the stream has
+ *   passed the call
+ * The statistics are bitwise those of drift_diagnostics on the same inputs (the same
+ * kernels). Returns DRIFT_OK after launching, or EINVAL / EWORKSPACE before any launch,
+ * or EHIP when a launch fails. ("Diagnostics" table; the Kernel Integration Contract of
+ * "WS2 Cross-Config Logprob Drift Contract": the device status travels with the
+ * statistics, nothing is decided or dropped on the host.) */
+int drift_diagnostics_async(const float* dlogp, const uint8_t* active, int64_t num_rows,
+                            double eps_low, double eps_high, const void* logprob_ws,
+                            drift_stats* out, void* ws, size_t ws_bytes, void* stream);
 
 /* Largest batch of drift_diagnostics_noalloc. */
 #define DRIFT_NOALLOC_MAX_ROWS (1 << 22)

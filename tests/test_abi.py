@@ -24,7 +24,8 @@ def test_header_declares_the_boundary():
                             "drift_shard_partials", "drift_merge_shards",
                             "drift_active_rows", "drift_backend_descriptor",
                             "drift_strerror", "drift_diagnostics_noalloc",
-                            "drift_lmhead_logprob_vh", "drift_lmhead_logprob_chain"])
+                            "drift_lmhead_logprob_vh", "drift_lmhead_logprob_chain",
+                            "drift_diagnostics_async"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -51,7 +52,7 @@ def test_struct_layouts_match_header():
 def test_descriptor_and_strerror():
     from train_rollout_logprob_amd import binding as B
     d = B.drift_backend_descriptor()
-    assert d["abi_version"] == 9 and d["archs"] == "gfx950"
+    assert d["abi_version"] == 10 and d["archs"] == "gfx950"
     assert "batch composition" in d["determinism"]
     assert d["lse_domain"] == "natural log"
     assert d["build_fingerprint"].startswith("src:")
@@ -320,6 +321,26 @@ def test_active_rows_host_checks():
     assert f(ok, 5000, ctypes.c_void_p((1 << 20) + 2), ok, ws, need, None) == B.DRIFT_EINVAL
     assert f(ok, 5000, ok, ok, ws, need - 1, None) == B.DRIFT_EWORKSPACE
     assert f(ok, 5000, ok, ok, ws + 8, need, None) == B.DRIFT_EWORKSPACE
+
+
+def test_diagnostics_async_host_checks():
+    """Null or misaligned outputs, bad sizes and eps, and short or misaligned workspaces
+    fail before any launch (fake device pointers are never dereferenced)."""
+    from train_rollout_logprob_amd import binding as B
+    lib = B.lib
+    d, a, out, ws = 4096, 8192, 16384, 1 << 20
+    need = lib.drift_workspace_size(B.DRIFT_OP_DIAGNOSTICS, 100000, 1, 0, B.DRIFT_F32)
+    f = lib.drift_diagnostics_async
+    assert f(d, a, 100000, 0.2, 0.2, None, None, ws, need, None) == B.DRIFT_EINVAL
+    assert f(d, a, 100000, 0.2, 0.2, None, out + 4, ws, need, None) == B.DRIFT_EINVAL
+    assert f(d, a, -1, 0.2, 0.2, None, out, ws, need, None) == B.DRIFT_EINVAL
+    assert f(d, a, 1 << 31, 0.2, 0.2, None, out, ws, need, None) == B.DRIFT_EINVAL
+    assert f(d, a, 100000, 0.2, 1.0, None, out, ws, need, None) == B.DRIFT_EINVAL
+    assert f(None, a, 100000, 0.2, 0.2, None, out, ws, need, None) == B.DRIFT_EINVAL
+    assert f(d + 2, a, 100000, 0.2, 0.2, None, out, ws, need, None) == B.DRIFT_EINVAL
+    assert f(d, a, 100000, 0.2, 0.2, None, out, ws, need - 1, None) == B.DRIFT_EWORKSPACE
+    assert f(d, a, 100000, 0.2, 0.2, None, out, ws + 8, need, None) == B.DRIFT_EWORKSPACE
+    assert f(d, a, 100000, 0.2, 0.2, None, out, None, need, None) == B.DRIFT_EWORKSPACE
 
 
 def test_diagnostics_noalloc_host_checks():

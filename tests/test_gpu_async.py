@@ -1,0 +1,107 @@
+"""drift_diagnostics_async (no synchronization; statistics written by the device to device
+memory or pinned host memory) against drift_diagnostics on the same inputs, through the C
+ABI: bitwise the same statistics on both selection paths, for both kinds of output memory,
+with a logprob status folded in; and the pipelined ScoringStep (submit / collect) against
+its synchronizing run()."""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+
+
+def _same(got, want):
+    assert set(got) == set(want)
+    for k, w in want.items():
+        g = got[k]
+        if isinstance(w, float):
+            assert np.float64(g).tobytes() == np.float64(w).tobytes(), (k, g, w)
+        else:
+            assert g == w, (k, g, w)
+
+
+def _batch(n, seed, tail):
+    rng = np.random.default_rng(seed)
+    d = rng.standard_t(2, n) * tail if tail else rng.normal(0.0, 1e-3, n)
+    a = (rng.random(n) < 0.8).astype(np.uint8)
+    return (torch.as_tensor(d.astype(np.float32), device="cuda"),
+            torch.as_tensor(a, device="cuda"))
+
+
+@pytest.mark.parametrize("where", ["device", "pinned"])
+def test_async_matches_diagnostics(where):
+    from train_rollout_logprob_amd import binding as B
+    import ctypes
+    sz = ctypes.sizeof(B.drift_stats)
+    if where == "device":
+        out = torch.empty(sz, dtype=torch.uint8, device="cuda")
+    else:
+        out = torch.empty(sz, dtype=torch.uint8, pin_memory=True)
+    # 300001 and 70001 rows take the multi-block digit path, 4099 the single-block one
+    for n, seed, tail in ((300001, 1, 0.05), (4099, 2, 0.0), (70001, 3, 0.3), (1, 5, 0.0)):
+        print(f"[case] async {where} n={n} seed={seed}", flush=True)
+        d, a = _batch(n, seed, tail)
+        a[0] = 1
+        st, want = B.diagnostics(d, a, 0.2, 0.2)
+        assert st == want["status"]
+        out.fill_(0xAB)
+        B.diagnostics_async(d, a, out, 0.2, 0.2)
+        torch.cuda.synchronize()
+        _same(B.stats_from(out), want)
+
+
+def test_async_empty_and_status_cases():
+    from train_rollout_logprob_amd import binding as B
+    import ctypes
+    out = torch.empty(ctypes.sizeof(B.drift_stats), dtype=torch.uint8, pin_memory=True)
+    d, a = _batch(1000, 4, 0.0)
+    a.zero_()
+    st, want = B.diagnostics(d, a, 0.2, 0.2)
+    assert st == B.DRIFT_ENOACTIVE
+    B.diagnostics_async(d, a, out, 0.2, 0.2)
+    torch.cuda.synchronize()
+    _same(B.stats_from(out), want)
+    e = torch.empty(0, dtype=torch.float32, device="cuda")
+    eb = torch.empty(0, dtype=torch.uint8, device="cuda")
+    st, want = B.diagnostics(e, eb, 0.2, 0.2)
+    B.diagnostics_async(e, eb, out, 0.2, 0.2)
+    torch.cuda.synchronize()
+    _same(B.stats_from(out), want)
+    # a scoring call whose action mask marks a padded row: its status outranks the stats'
+    x = torch.randn((8, 64), device="cuda")
+    ids = torch.zeros(8, dtype=torch.int32, device="cuda")
+    att = torch.tensor([1, 1, 1, 0, 1, 1, 1, 1], dtype=torch.uint8, device="cuda")
+    act = torch.tensor([0, 1, 1, 1, 0, 1, 1, 1], dtype=torch.uint8, device="cuda")
+    t, r, dd, aa, ws = B.selected_logprob(x, x, ids, att, act, "right", 2, 4)
+    st, want = B.diagnostics(dd, aa, 0.2, 0.2, logprob_ws=ws)
+    assert st == B.DRIFT_EMASK
+    B.diagnostics_async(dd, aa, out, 0.2, 0.2, logprob_ws=ws)
+    torch.cuda.synchronize()
+    _same(B.stats_from(out), want)
+
+
+def test_pipelined_steps_match_run():
+    """Three steps submitted two deep (each collected after the next is launched) give the
+    statistics of the synchronizing run(), bitwise, in every slot."""
+    from helpers import make_small, device_inputs
+    from train_rollout_logprob_amd import binding as B
+    case = make_small(dict(name="large", B=4, L=64))
+    ids, att, act, cu = device_inputs(case)
+    step = B.ScoringStep(case.train, case.rollout, ids, att, act, case.layout, case.B, case.L,
+                         cu, case.eps_low, case.eps_high, depth=2)
+    assert step.run() == B.DRIFT_OK
+    want = step.stats.as_dict()
+    prev = step.submit()
+    for _ in range(3):
+        cur = step.submit()
+        assert step.collect(prev) == B.DRIFT_OK
+        _same(step.stats_of(prev).as_dict(), want)
+        prev = cur
+    assert step.collect(prev) == B.DRIFT_OK
+    _same(step.stats_of(prev).as_dict(), want)

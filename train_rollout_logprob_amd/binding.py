@@ -47,7 +47,8 @@ EXPORTS = ("drift_workspace_size", "drift_selected_logprob", "drift_get_status",
            "drift_diagnostics", "drift_segment_diagnostics", "drift_lmhead_logprob",
            "drift_dlogits", "drift_shard_partials", "drift_merge_shards",
            "drift_active_rows", "drift_backend_descriptor", "drift_strerror",
-           "drift_diagnostics_noalloc", "drift_lmhead_logprob_vh", "drift_lmhead_logprob_chain")
+           "drift_diagnostics_noalloc", "drift_lmhead_logprob_vh", "drift_lmhead_logprob_chain",
+           "drift_diagnostics_async")
 DRIFT_NOALLOC_MAX_ROWS = 1 << 22
 
 
@@ -112,6 +113,9 @@ def _load():
     lib.drift_diagnostics.argtypes = [vp, vp, i64, ctypes.c_double, ctypes.c_double, vp,
                                       ctypes.POINTER(drift_stats), vp, sz, vp]
     lib.drift_diagnostics.restype = ctypes.c_int
+    lib.drift_diagnostics_async.argtypes = [vp, vp, i64, ctypes.c_double, ctypes.c_double, vp,
+                                            vp, vp, sz, vp]
+    lib.drift_diagnostics_async.restype = ctypes.c_int
     lib.drift_diagnostics_noalloc.argtypes = [vp, vp, i64, ctypes.c_double, ctypes.c_double,
                                               vp, vp, vp]
     lib.drift_diagnostics_noalloc.restype = ctypes.c_int
@@ -181,6 +185,13 @@ def drift_segment_diagnostics(dlogp, active, num_rows: int, seg_offsets, num_seg
                                              _ptr(seg_offsets), num_segments, eps_low,
                                              eps_high, _ptr(logprob_ws), _ptr(out_dev),
                                              _stream(stream)))
+
+
+def drift_diagnostics_async(dlogp, active, num_rows: int, eps_low: float, eps_high: float,
+                            logprob_ws, out, ws, ws_bytes: int, stream=None) -> int:
+    return int(lib.drift_diagnostics_async(_ptr(dlogp), _ptr(active), num_rows, eps_low,
+                                           eps_high, _ptr(logprob_ws), _ptr(out), _ptr(ws),
+                                           ws_bytes, _stream(stream)))
 
 
 def drift_diagnostics_noalloc(dlogp, active, num_rows: int, eps_low: float, eps_high: float,
@@ -525,6 +536,34 @@ def diagnostics_noalloc(dlogp, active, eps_low=0.2, eps_high=0.2, logprob_ws=Non
     return drift_stats.from_buffer(host).as_dict(), out
 
 
+def diagnostics_async(dlogp, active, out, eps_low=0.2, eps_high=0.2, logprob_ws=None,
+                      ws=None, stream=None):
+    """Call drift_diagnostics_async: the statistics go to `out`, a uint8 tensor of
+    sizeof(drift_stats) bytes in device memory or pinned host memory, once the stream
+    passes the call; nothing is synchronized here. Returns the workspace, which stays in
+    use until then."""
+    N = dlogp.shape[0]
+    if out.numel() < ctypes.sizeof(drift_stats) or out.dtype != torch.uint8:
+        raise ValueError("out must be a uint8 tensor of at least sizeof(drift_stats) bytes")
+    if not out.is_cuda and not out.is_pinned():
+        raise ValueError("out must be device memory or pinned host memory")
+    if ws is None:
+        ws = workspace(DRIFT_OP_DIAGNOSTICS, N, 1, DRIFT_F32, dlogp.device)
+    st = drift_diagnostics_async(dlogp, active, N, eps_low, eps_high, logprob_ws, out, ws,
+                                 ws.numel(), stream)
+    if st != DRIFT_OK:
+        raise DriftError(st, "drift_diagnostics_async")
+    return ws
+
+
+def stats_from(buf) -> dict:
+    """The statistics held in a uint8 tensor written by drift_diagnostics_async or
+    drift_diagnostics_noalloc (copied to the host first if it is device memory; the caller
+    has already waited for the call)."""
+    host = bytearray(buf[:ctypes.sizeof(drift_stats)].cpu().numpy().tobytes())
+    return drift_stats.from_buffer(host).as_dict()
+
+
 def report(stats: dict, segments=None, **metadata) -> dict:
     """One JSON-ready report of a comparison ("Diagnostics" table, report layout): the
     statistics, optional per-segment versions, and metadata (the backend descriptor plus
@@ -550,12 +589,20 @@ def report(stats: dict, segments=None, **metadata) -> dict:
 class ScoringStep:
     """Repeated drift_selected_logprob + drift_diagnostics on fixed tensors.
 
-    All marshalling (argument struct, output tensors, workspaces, a pinned host buffer for
-    the statistics) is done once here, so a call to `run` is two C calls."""
+    All marshalling (argument struct, output tensors, workspaces, pinned host buffers for
+    the statistics) is done once here, so a call to `run` is two C calls.
+
+    `run` waits for each step's statistics. `submit` / `collect` pipeline the steps instead:
+    `submit` launches a step with drift_diagnostics_async, whose statistics land in one of
+    `depth` pinned host slots, and returns the slot; `collect(slot)` waits for that step
+    and returns its status, the statistics then in `stats_of(slot)`. A loop that submits
+    step i + 1 before collecting step i keeps the GPU busy while the host reads and checks
+    the previous step. The per-row outputs are shared by all steps (each step overwrites
+    them); the statistics are per slot."""
 
     def __init__(self, train, rollout, ids, attention=None, action=None, layout="right",
                  batch=0, seq_len=0, cu_seqlens=None, eps_low=0.2, eps_high=0.2,
-                 stream=None, vocab_real=None, transforms=(None, None)):
+                 stream=None, vocab_real=None, transforms=(None, None), depth=2):
         dev = train.device
         self.args = make_args(train, rollout, ids, attention, action, layout, batch, seq_len,
                               cu_seqlens, vocab_real=vocab_real, transforms=transforms)
@@ -568,10 +615,15 @@ class ScoringStep:
                     torch.empty(self.N, dtype=torch.float32, device=dev),
                     torch.empty(self.N, dtype=torch.float32, device=dev),
                     torch.empty(self.N, dtype=torch.uint8, device=dev))
-        self._pinned = torch.empty(ctypes.sizeof(drift_stats), dtype=torch.uint8,
-                                   pin_memory=True)
+        sz = ctypes.sizeof(drift_stats)
+        self._pinned = torch.empty(sz * (1 + depth), dtype=torch.uint8, pin_memory=True)
         self.stats = drift_stats.from_address(self._pinned.data_ptr())
+        self._slot_ptr = [self._pinned.data_ptr() + sz * (1 + k) for k in range(depth)]
+        self._slots = [drift_stats.from_address(q) for q in self._slot_ptr]
+        self._stream_obj = stream
         self._stream = _stream(stream)
+        self._done = [torch.cuda.Event() for _ in range(depth)]
+        self._next = 0
         self._args_ref = ctypes.byref(self.args)
         self._stats_ref = ctypes.byref(self.stats)
         t, r, d, a = (x.data_ptr() for x in self.out)
@@ -590,6 +642,39 @@ class ScoringStep:
         if st != DRIFT_OK:
             raise DriftError(st, "drift_selected_logprob")
         return lib.drift_diagnostics(*self._dg_args)
+
+    def _torch_stream(self):
+        s = self._stream_obj
+        if s is None:
+            return torch.cuda.current_stream()
+        if isinstance(s, int):
+            return torch.cuda.ExternalStream(s)
+        return s
+
+    def submit(self) -> int:
+        """Launches one step; returns the slot its statistics go to. The slot must have
+        been collected (or never used) before it comes round again."""
+        k = self._next
+        self._next = (k + 1) % len(self._slots)
+        st = lib.drift_selected_logprob(*self._lp_args)
+        if st != DRIFT_OK:
+            raise DriftError(st, "drift_selected_logprob")
+        d, a = self._dg_args[0], self._dg_args[1]
+        st = lib.drift_diagnostics_async(d, a, self.N, self.eps[0], self.eps[1],
+                                         self.ws.data_ptr(), self._slot_ptr[k],
+                                         self.dws.data_ptr(), self.dws.numel(), self._stream)
+        if st != DRIFT_OK:
+            raise DriftError(st, "drift_diagnostics_async")
+        self._done[k].record(self._torch_stream())
+        return k
+
+    def collect(self, slot) -> int:
+        """Waits for the step whose statistics go to `slot`; returns their status."""
+        self._done[slot].synchronize()
+        return self._slots[slot].status
+
+    def stats_of(self, slot):
+        return self._slots[slot]
 
 
 def lmhead_logprob(hidden, weight, ids, active=None, ws=None, out=None, stream=None,

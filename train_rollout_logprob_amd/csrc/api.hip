@@ -317,6 +317,26 @@ int drift_diagnostics(const float* dlogp, const uint8_t* active, int64_t num_row
   return out_host->status;
 }
 
+int drift_diagnostics_async(const float* dlogp, const uint8_t* active, int64_t num_rows,
+                            double eps_low, double eps_high, const void* logprob_ws,
+                            drift_stats* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!out || !aligned(out, 8) || num_rows < 0 || num_rows > INT32_MAX) return DRIFT_EINVAL;
+  if (num_rows > 0 && (!dlogp || !active || !aligned(dlogp, 4))) return DRIFT_EINVAL;
+  if (!(eps_low >= 0.0 && eps_low < 1.0 && eps_high >= 0.0 && eps_high < 1.0))
+    return DRIFT_EINVAL;
+  if (!ws || !aligned(ws, 256) || ws_bytes < diag_ws_bytes(num_rows)) return DRIFT_EWORKSPACE;
+  DiagParams dp{};
+  dp.N = num_rows;
+  dp.eps_low = eps_low;
+  dp.eps_high = eps_high;
+  dp.d = dlogp;
+  dp.active = active;
+  dp.lp = (const WsHeader*)logprob_ws;
+  dp.ws = (char*)ws;
+  dp.out = out;
+  return launch_diagnostics(dp, (hipStream_t)stream) == hipSuccess ? DRIFT_OK : DRIFT_EHIP;
+}
+
 int drift_diagnostics_noalloc(const float* dlogp, const uint8_t* active, int64_t num_rows,
                               double eps_low, double eps_high, const void* logprob_ws,
                               drift_stats* out_dev, void* stream) {
