@@ -677,6 +677,58 @@ class ScoringStep:
         return self._slots[slot]
 
 
+class ScoringGraph:
+    """One step of a ScoringStep (drift_selected_logprob + drift_diagnostics_async) captured
+    once as a HIP graph (torch.cuda.CUDAGraph) and replayed as a single launch, for batches
+    small enough that launching the step's kernels one by one costs more than running them.
+
+    The graph keeps the step's pointers: every replay reads the step's input tensors as they
+    are then (overwrite them in place to score new data) and writes the step's outputs
+    (`step.out`) and this graph's pinned statistics record (`stats()` once the replay has
+    completed). The capture launches kernels only: neither entry point copies, sets memory
+    or synchronizes. Profiling events are off inside the graph."""
+
+    def __init__(self, step):
+        self.step = step
+        self._pinned = torch.empty(ctypes.sizeof(drift_stats), dtype=torch.uint8,
+                                   pin_memory=True)
+        self._stats = drift_stats.from_address(self._pinned.data_ptr())
+        self.graph = torch.cuda.CUDAGraph()
+        ev = (step.args.prof_events[0], step.args.prof_events[1])
+        step.set_events(0, 0)
+        try:
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):  # one uncaptured step first, as torch asks
+                self._launch(side.cuda_stream)
+            torch.cuda.current_stream().wait_stream(side)
+            with torch.cuda.graph(self.graph):
+                self._launch(torch.cuda.current_stream().cuda_stream)
+        finally:
+            step.set_events(*ev)
+
+    def _launch(self, stream):
+        st = self.step
+        t, r, d, a = st._lp_args[1:5]
+        rc = lib.drift_selected_logprob(st._args_ref, t, r, d, a, st.ws.data_ptr(),
+                                        st.ws.numel(), stream)
+        if rc != DRIFT_OK:
+            raise DriftError(rc, "drift_selected_logprob")
+        rc = lib.drift_diagnostics_async(d, a, st.N, st.eps[0], st.eps[1], st.ws.data_ptr(),
+                                         self._pinned.data_ptr(), st.dws.data_ptr(),
+                                         st.dws.numel(), stream)
+        if rc != DRIFT_OK:
+            raise DriftError(rc, "drift_diagnostics_async")
+
+    def replay(self):
+        """Launches the captured step on the current stream (asynchronous)."""
+        self.graph.replay()
+
+    def stats(self):
+        """The statistics of the last completed replay (the caller has waited for it)."""
+        return self._stats
+
+
 def lmhead_logprob(hidden, weight, ids, active=None, ws=None, out=None, stream=None,
                    check=False, weight_layout="hv", transforms=None):
     """Call drift_lmhead_logprob on torch tensors: hidden bf16 [T, H], weight bf16 [H, V]
