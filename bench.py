@@ -1,8 +1,10 @@
 """Throughput of the paired selected-token logprob + drift path on one MI355X.
 
 One step = drift_selected_logprob (classification, paired one-pass log-softmax gather of
-both sides, drift) + drift_diagnostics (sums, counts, exact nearest-rank select, one host
-sync) over one batch, inputs resident in HBM before timing starts.
+both sides, drift) + drift_diagnostics_async (sums, counts, exact nearest-rank select; the
+statistics written into pinned host memory) over one batch, inputs resident in HBM before
+timing starts. Steps run two deep: the host waits for step i and checks its statistics
+while step i + 1 runs; the last step is collected before the clock stops.
 
 The main line is the large-batch workload, the largest that fits one GPU: bf16 logits,
 V=151936, B=32, L=4096 (prompt 1024 + response U[1024,3072]), right padding, about 40 GB
