@@ -1,9 +1,13 @@
-"""Runs the oracle's per-row scoring over many rows in a pool of CPU worker processes.
+"""Runs the oracle's per-row functions over many rows in a pool of CPU worker processes.
 
 Test infrastructure only (see the package docstring): the full-size parity tests and the
 CPU-baseline leg of the benchmark use it. It adds no arithmetic of its own: every row is
-scored by `score_rows` of this package (textbook two-pass log-sum-exp in float64), one
-call per contiguous range of rows, and the results are put back in row order.
+scored by `score_rows` of this package (textbook two-pass log-sum-exp in float64), its
+entropy by `entropy_rows` and its log-sum-exp by `logsumexp_row`, its gradient by
+`dlogits_rows`, one call per contiguous range of rows, and the results are put back in row
+order. For the gradient the workers also compare it with a given array (so that no
+[rows, V] float64 array travels back): per row, the largest |got - want| - c |want| over
+the other columns, and the same quantity at the selected column.
 
 Rows reach the workers through a shared host buffer: the caller writes a chunk of rows of
 both sides into a memory-mapped file (in /dev/shm when it has room, else the temporary
@@ -44,6 +48,46 @@ def _score_range(task):
     t, r, d = score_rows(mm[0, lo:hi], mm[1, lo:hi], dtype, ids, vocab_real, transforms)
     del mm
     return lo, t, r, d, time.perf_counter() - t0
+
+
+def _entropy_range(task):
+    """Worker body: entropy and natural-log log-sum-exp of rows [lo, hi) of both sides."""
+    from .logprob import apply_transforms, logsumexp_row, widen
+    from .training import entropy_rows
+
+    path, rows, cols, dtype, lo, hi, vocab_real, transforms = task
+    mm = np.memmap(path, dtype=_NP[dtype], mode="r", shape=(2, rows, cols))
+    V = cols if vocab_real is None else int(vocab_real)
+    ent, lse = [], []
+    for s in (0, 1):
+        part = mm[s, lo:hi]
+        ent.append(entropy_rows(part, dtype, vocab_real, transforms[s]))
+        lse.append(np.array([logsumexp_row(apply_transforms(widen(r[:V], dtype), transforms[s]))
+                             for r in part]))
+    del mm
+    return lo, ent + lse  # entropy train, rollout; lse train, rollout
+
+
+def _dlogits_range(task):
+    """Worker body: the oracle's gradient of rows [lo, hi) (side 0 of the buffer holds the
+    logits, side 1 the gradient to compare, both in the stored type), and per row the
+    largest |got - want| - c |want| over the columns other than the selected one, and that
+    quantity at the selected column."""
+    from .logprob import widen
+    from .training import dlogits_rows
+
+    path, rows, cols, dtype, out_dtype, lo, hi, ids, c, vocab_real, transform = task
+    mm = np.memmap(path, dtype=_NP[dtype], mode="r", shape=(2, rows, cols))
+    want = dlogits_rows(mm[0, lo:hi], dtype, ids, np.ones(hi - lo, np.uint8), vocab_real,
+                        transform)
+    got = widen(mm[1, lo:hi], out_dtype).reshape(want.shape)
+    del mm
+    ex = np.abs(got - want) - c * np.abs(want)
+    k = np.arange(hi - lo)
+    y = np.asarray(ids, dtype=np.int64)
+    at_y = ex[k, y].copy()
+    ex[k, y] = -np.inf
+    return lo, ex.max(axis=1), at_y
 
 
 class OraclePool:
@@ -111,6 +155,46 @@ class OraclePool:
             r[lo:lo + len(a)] = b
             d[lo:lo + len(a)] = c
         return t, r, d, wall
+
+    def _ranges(self, rows):
+        # about four ranges per worker, so that uneven row costs even out
+        step = max(1, -(-rows // (4 * self.workers)))
+        return [(lo, min(rows, lo + step)) for lo in range(0, rows, step)]
+
+    def entropy(self, rows: int, cols: int, dtype: str, vocab_real=None,
+                transforms=(None, None)):
+        """Entropy (nats) and natural-log log-sum-exp of rows [0, rows) of both sides of the
+        buffer, float64: (entropy_train, entropy_rollout, lse_train, lse_rollout)."""
+        assert self._shape is not None and self._shape[0][1] >= rows
+        self._mm.flush()
+        total = self._shape[0][1]
+        tasks = [(self._path, total, cols, dtype, lo, hi, vocab_real, transforms)
+                 for lo, hi in self._ranges(rows)]
+        out = np.empty((4, rows))
+        for lo, parts in self._pool.map(_entropy_range, tasks, chunksize=1):
+            for k in range(4):
+                out[k, lo:lo + len(parts[k])] = parts[k]
+        return tuple(out)
+
+    def dlogits_excess(self, rows: int, cols: int, dtype: str, out_dtype: str, ids, c: float,
+                       vocab_real=None, transform=None):
+        """Rows [0, rows) of side 0 are logits, of side 1 a gradient of them to check (both
+        stored as `dtype`, which `out_dtype` must share, e.g. bf16 logits and a bf16
+        gradient). Returns, per row, the largest |got - want| - c |want| over the other
+        columns and its value at the selected column, against the oracle's gradient of the
+        selected logprob (upstream gradient 1)."""
+        assert self._shape is not None and self._shape[0][1] >= rows
+        assert _NP[dtype] == _NP[out_dtype]
+        self._mm.flush()
+        total = self._shape[0][1]
+        ids = np.asarray(ids, dtype=np.int64)
+        tasks = [(self._path, total, cols, dtype, out_dtype, lo, hi, ids[lo:hi], c, vocab_real,
+                  transform) for lo, hi in self._ranges(rows)]
+        other, at_y = np.empty(rows), np.empty(rows)
+        for lo, ex, ey in self._pool.map(_dlogits_range, tasks, chunksize=1):
+            other[lo:lo + len(ex)] = ex
+            at_y[lo:lo + len(ey)] = ey
+        return other, at_y
 
     def _release(self):
         self._mm = None

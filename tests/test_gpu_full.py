@@ -5,7 +5,8 @@ Every active row of each scoring workload is compared with the fp64 oracle (the 
 runs in a pool of host worker processes started before this process touched the GPU):
 per-token logp of both sides and dlogp within 2e-5. The diagnostics are checked twice:
 Gate A, the library's statistics of its own dlogp array against the oracle's statistics
-of the same array (counts, order statistics and argmax bit-exact, means to 1e-5); and
+of the same array (counts, order statistics, argmax and clipfrac0 bit-exact, means to
+1e-12 relative); and
 Gate B, the library's statistics against the oracle's statistics of the oracle's own fp64
 dlogp (means to 1e-5 relative; counts and order statistics as far as the per-token
 tolerance decides them)."""
