@@ -181,3 +181,33 @@ def assert_gate_b(got, want, d_oracle_active, eps_low=0.2, eps_high=0.2, tol=LOG
     a = np.sort(np.abs(d))
     if len(a) > 1 and a[-1] - a[-2] > 2 * tol:
         assert got["argmax_row"] == want["argmax_row"]
+
+
+FULL_CHUNK_BYTES = 2 << 30  # rows of both sides copied to the host per round (full sizes)
+
+
+def copy_rows(dst, src, idx):
+    """Rows `idx` of a device tensor into a host array of the stored type (bf16 as bits)."""
+    sub = src.index_select(0, idx)
+    if sub.dtype == torch.bfloat16:
+        torch.from_numpy(dst.view(np.int16)).copy_(sub.view(torch.int16))
+    else:
+        torch.from_numpy(dst).copy_(sub)
+
+
+def oracle_all_rows(pool, case, rows, transforms=(None, None)):
+    """Oracle logps and dlogp (float64, [3, len(rows)]) of the given rows of a case whose
+    logits are on the GPU, scored in the worker pool chunk by chunk."""
+    per = max(1, FULL_CHUNK_BYTES // (2 * case.V * case.elem_bytes))
+    per = min(per, len(rows))
+    out = np.empty((3, len(rows)))
+    for a in range(0, len(rows), per):
+        sel = rows[a:a + per]
+        bt, br = pool.buffers(per, case.V, case.dtype)
+        idx = torch.as_tensor(sel, device=case.train.device)
+        copy_rows(bt[:len(sel)], case.train, idx)
+        copy_rows(br[:len(sel)], case.rollout, idx)
+        t, r, d, _ = pool.score(len(sel), case.V, case.dtype, case.ids[sel],
+                                transforms=transforms)
+        out[:, a:a + len(sel)] = (t, r, d)
+    return out

@@ -15,45 +15,16 @@ import pytest
 import torch
 
 import oracle
-from helpers import (LOGP_TOL, assert_gate_b, assert_stats_exact, device_inputs, oracle_pool,
-                     status_name)
+from helpers import (LOGP_TOL, assert_gate_b, assert_stats_exact, device_inputs,
+                     oracle_all_rows, oracle_pool, status_name)
 from train_rollout_logprob_amd import synth
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
-
-CHUNK_BYTES = 2 << 30  # rows of both sides copied to the host per round
-
 
 @pytest.fixture(scope="module", autouse=True)
 def _need_gpu():
     if not torch.cuda.is_available():
         pytest.skip("needs a GPU")
-
-
-def _copy_rows(dst, src, idx):
-    """Rows `idx` of a device logits tensor into a host array of the stored type."""
-    sub = src.index_select(0, idx)
-    if sub.dtype == torch.bfloat16:
-        torch.from_numpy(dst.view(np.int16)).copy_(sub.view(torch.int16))
-    else:
-        torch.from_numpy(dst).copy_(sub)
-
-
-def _oracle_all_rows(pool, case, rows, transforms=(None, None)):
-    """Oracle logps and dlogp (float64) of the given rows, scored chunk by chunk."""
-    per = max(1, CHUNK_BYTES // (2 * case.V * case.elem_bytes))
-    per = min(per, len(rows))
-    out = np.empty((3, len(rows)))
-    for a in range(0, len(rows), per):
-        sel = rows[a:a + per]
-        bt, br = pool.buffers(per, case.V, case.dtype)
-        idx = torch.as_tensor(sel, device=case.train.device)
-        _copy_rows(bt[:len(sel)], case.train, idx)
-        _copy_rows(br[:len(sel)], case.rollout, idx)
-        t, r, d, _ = pool.score(len(sel), case.V, case.dtype, case.ids[sel],
-                                transforms=transforms)
-        out[:, a:a + len(sel)] = (t, r, d)
-    return out
 
 
 # soft-cap 30 on both sides: the folded log-sum-exp terms of the scoring kernel at full size
@@ -88,7 +59,7 @@ def test_full_size_every_active_row(name):
     assert np.all(th[a_h == 0] == 0) and np.all(rh[a_h == 0] == 0) and np.all(dh[a_h == 0] == 0)
     print(f"[case] full {name}: oracle over {len(rows)} rows in {pool.workers} workers",
           flush=True)
-    ot, orr, od = _oracle_all_rows(pool, case, rows, tr)
+    ot, orr, od = oracle_all_rows(pool, case, rows, tr)
     for name_, g, w in (("train", th, ot), ("rollout", rh, orr), ("dlogp", dh, od)):
         err = np.abs(g[rows].astype(np.float64) - w)
         print(f"[case] {name} {name_}: max err {err.max():.3e} (row {rows[int(err.argmax())]}) "

@@ -14,8 +14,8 @@ import pytest
 import torch
 
 import oracle
-from helpers import (LOGP_TOL, device_inputs, host_logits, make_small, oracle_pool, run_library,
-                     status_name)
+from helpers import (FULL_CHUNK_BYTES, LOGP_TOL, copy_rows, device_inputs, host_logits,
+                     make_small, oracle_pool, run_library, status_name)
 from train_rollout_logprob_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -209,15 +209,6 @@ def test_dlogits_unaligned_rows_take_the_scalar_path():
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
 
 
-def _copy_rows(dst, src, idx):
-    """Rows `idx` of a device tensor into a host array of the stored type (bf16 as bits)."""
-    sub = src.index_select(0, idx)
-    if sub.dtype == torch.bfloat16:
-        torch.from_numpy(dst.view(np.int16)).copy_(sub.view(torch.int16))
-    else:
-        torch.from_numpy(dst).copy_(sub)
-
-
 @pytest.mark.slow
 def test_full_size_entropy_and_dlogits_every_row():
     """The full bf16 scoring workload (B=8, L=2048, V=151936) with entropy and LSE exported,
@@ -243,20 +234,20 @@ def test_full_size_entropy_and_dlogits_every_row():
     ent_h = [e.cpu().numpy().astype(np.float64) for e in ent]
     lse_h = [x.cpu().numpy() for x in lse]
     rows = np.nonzero(a_h)[0]
-    per = max(1, (2 << 30) // (2 * V * case.elem_bytes))
+    per = max(1, FULL_CHUNK_BYTES // (2 * V * case.elem_bytes))
     worst = {"entropy": 0.0, "lse": 0.0, "dlogits": -np.inf}
     for a0 in range(0, len(rows), per):
         sel = rows[a0:a0 + per]
         idx = torch.as_tensor(sel, device="cuda")
         bt, br = pool.buffers(per, V, case.dtype)
-        _copy_rows(bt[:len(sel)], case.train, idx)
-        _copy_rows(br[:len(sel)], case.rollout, idx)
+        copy_rows(bt[:len(sel)], case.train, idx)
+        copy_rows(br[:len(sel)], case.rollout, idx)
         et, er, lt, lr = pool.entropy(len(sel), V, case.dtype)
         for side, (e, l) in enumerate(((et, lt), (er, lr))):
             worst["entropy"] = max(worst["entropy"], float(np.abs(ent_h[side][sel] - e).max()))
             worst["lse"] = max(worst["lse"], float(np.abs(lse_h[side][sel] - l).max()))
         # side 1 of the buffer now holds the train side's gradient rows from the GPU
-        _copy_rows(br[:len(sel)], out, idx)
+        copy_rows(br[:len(sel)], out, idx)
         # the small-shape bound with g = 1, S = 1: |want| LOGP_TOL + 2e-6, plus LOGP_TOL at
         # the selected column, then (|want| + that) * 2^-8 for the bf16 output
         ex, ey = pool.dlogits_excess(len(sel), V, case.dtype, "bf16", case.ids[sel],
