@@ -620,8 +620,15 @@ class ScoringStep:
         self.stats = drift_stats.from_address(self._pinned.data_ptr())
         self._slot_ptr = [self._pinned.data_ptr() + sz * (1 + k) for k in range(depth)]
         self._slots = [drift_stats.from_address(q) for q in self._slot_ptr]
-        self._stream_obj = stream
-        self._stream = _stream(stream)
+        # the stream every call of this step launches into, fixed here (None = the stream
+        # current now), and the same stream object for the completion events of `submit`
+        if stream is None:
+            self._stream_obj = torch.cuda.current_stream()
+        elif isinstance(stream, int):
+            self._stream_obj = torch.cuda.ExternalStream(stream)
+        else:
+            self._stream_obj = stream
+        self._stream = self._stream_obj.cuda_stream
         self._done = [torch.cuda.Event() for _ in range(depth)]
         self._next = 0
         self._args_ref = ctypes.byref(self.args)
@@ -643,14 +650,6 @@ class ScoringStep:
             raise DriftError(st, "drift_selected_logprob")
         return lib.drift_diagnostics(*self._dg_args)
 
-    def _torch_stream(self):
-        s = self._stream_obj
-        if s is None:
-            return torch.cuda.current_stream()
-        if isinstance(s, int):
-            return torch.cuda.ExternalStream(s)
-        return s
-
     def submit(self) -> int:
         """Launches one step; returns the slot its statistics go to. The slot must have
         been collected (or never used) before it comes round again."""
@@ -665,7 +664,7 @@ class ScoringStep:
                                          self.dws.data_ptr(), self.dws.numel(), self._stream)
         if st != DRIFT_OK:
             raise DriftError(st, "drift_diagnostics_async")
-        self._done[k].record(self._torch_stream())
+        self._done[k].record(self._stream_obj)
         return k
 
     def collect(self, slot) -> int:
