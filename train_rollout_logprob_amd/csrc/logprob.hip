@@ -581,6 +581,94 @@ __global__ void __launch_bounds__(NT) score_rows_exact(ScoreParams p) {
   }
 }
 
+// The exact pass for short rows (vocabulary shards, small V): one wave per row, four rows
+// per block, with no block barrier. Lane 0 classifies the row and finishes it, the wave
+// streams it and merges its lanes. The bins make the sum independent of how a row is
+// split among lanes, so the results are bitwise those of score_rows_exact.
+template <typename T, int U, int XF>
+__global__ void __launch_bounds__(256) score_rows_exact_w(ScoreParams p) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t r = p.row0 + (int64_t)blockIdx.x * 4 + wave;
+  if (r >= p.N) return;  // wave-uniform: the last block's rows past the batch
+  WsHeader* h = (WsHeader*)p.ws;
+  const bool shard = p.part[0] != nullptr;
+  int64_t y = -1;
+  if (lane == 0) {
+    int64_t end = p.N;
+    if (p.layout == DRIFT_PACKED) {
+      end = (int64_t)p.cu[p.nseq];
+      end = end < 0 ? 0 : (end > p.N ? p.N : end);
+    }
+    const RowClass c = classify_row(p, r, end);
+    if (p.active) p.active[r] = c.active ? 1 : 0;
+    if (c.err & (1u << kErrMask)) record_error(h, kErrMask, r);
+    if (c.err & (1u << kErrToken)) record_error(h, kErrToken, r);
+    if (!c.score) {
+      if (shard) {
+        for (int side = 0; side < 2; ++side) {
+          drift_lse_partial& q = p.part[side][r];
+          q.bin[0] = q.bin[1] = q.bin[2] = 0;
+          q.top = kEmptyTop;
+          q.flags = 0;
+          q.x_sel = 0.0f;
+          q.reserved = 0.0f;
+        }
+      } else {
+        unscored_outputs(p, r, c.active);
+      }
+    }
+    y = c.score ? c.y : -1;
+  }
+  // lane 0's value to the whole wave (lane 0 is its first active lane here)
+  const uint32_t ylo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)y);
+  const uint32_t yhi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)y >> 32));
+  y = (int64_t)(((uint64_t)yhi << 32) | ylo);
+  if (y < 0) return;  // wave-uniform
+
+  const size_t off = (size_t)r * (size_t)p.stride * sizeof(T);
+  const char* rt = (const char*)p.train + off;
+  const char* rr = (const char*)p.rollout + off;
+  AccX at = accx_empty(), ar = accx_empty();
+  if ((((uintptr_t)rt | (uintptr_t)rr) & 15) == 0) {
+    stream_row<T, 64, U, true, XF>(rt, rr, p.V, lane, at, ar, p);
+  } else {
+    stream_row<T, 64, U, false, XF>(rt, rr, p.V, lane, at, ar, p);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    at = merge(at, shfl_xor_acc(at, o));
+    ar = merge(ar, shfl_xor_acc(ar, o));
+  }
+  if (lane == 0) {
+    const bool owner = y >= p.vstart && y < p.vstart + p.V;
+    float xty = 0.0f, xry = 0.0f;
+    if (owner) {  // single owner: the selected logit goes through the same chain
+      float one[1] = {Elem<T>::load1(rt, y - p.vstart)};
+      if constexpr (XF) apply_chain<1>(one, p.xf[0]);
+      xty = one[0];
+      one[0] = Elem<T>::load1(rr, y - p.vstart);
+      if constexpr (XF) apply_chain<1>(one, p.xf[1]);
+      xry = one[0];
+    }
+    if (shard) {
+      auto put = [&](drift_lse_partial& q, const AccX& a, float xs) {
+        q.bin[0] = a.b2;
+        q.bin[1] = a.b1;
+        q.bin[2] = a.b0;
+        q.top = a.top;
+        q.flags = DRIFT_PART_SCORED | (owner ? DRIFT_PART_OWNER : 0u) |
+                  (a.bad ? DRIFT_PART_BAD : 0u);
+        q.x_sel = xs;
+        q.reserved = 0.0f;
+      };
+      put(p.part[0][r], at, xty);
+      put(p.part[1][r], ar, xry);
+    } else {
+      finish_row_exact(p, h, r, at, ar, xty, xry);
+    }
+  }
+}
+
 // Shard merge: one thread per row classifies it, folds the S partials of each side in
 // shard order and takes the selected logit from the owner shard.
 __global__ void __launch_bounds__(256) merge_shards(MergeParams m) {
@@ -657,6 +745,19 @@ void launch_over_rows(K kernel, ScoreParams p, int nt, hipStream_t s) {
   }
 }
 
+// Launches a four-rows-per-block kernel (one wave per row) over rows [0, p.N) in
+// consecutive launches over row ranges whose lengths are multiples of 4, so that only the
+// last block of the last launch has rows past the batch (it skips them).
+template <typename K>
+void launch_over_rows_w(K kernel, ScoreParams p, hipStream_t s) {
+  const int64_t per = (int64_t)(0xffffffffu / 256u) * 4;
+  for (int64_t r0 = 0; r0 < p.N; r0 += per) {
+    p.row0 = r0;
+    const int64_t n = p.N - r0 < per ? p.N - r0 : per;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, s, p);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_score(const ScoreParams& p, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
@@ -701,10 +802,10 @@ hipError_t launch_score_exact(const ScoreParams& p, hipStream_t s, hipEvent_t ev
   if (e != hipSuccess) return e;
   if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
   if (p.N > 0) {
-    // The exact sum does not depend on how a row is split among lanes, so the block width
-    // follows the row length: 256 threads for rows of 4096 or more 16-byte groups, 128 for
-    // shorter ones (vocabulary shards), which keep more rows in flight per CU (measured on
-    // MI355X: 8 fp32 shards of 4000 columns 9.6 -> 7.6 ms, full rows unchanged).
+    // The exact sum does not depend on how a row is split among lanes, so the layout
+    // follows the row length: a block of 256 threads per row for rows of 4096 or more
+    // 16-byte groups, one wave per row (four rows per block) for shorter ones (vocabulary
+    // shards), which keeps more rows in flight per CU without block barriers.
     // chains as in launch_score: none (0), step by step (1), both folded (2)
     const int xf = !(p.xf[0].n > 0 || p.xf[1].n > 0) ? 0
                    : (p.xf[0].kind != 0 && p.xf[1].kind != 0) ? 2 : 1;
@@ -717,16 +818,21 @@ hipError_t launch_score_exact(const ScoreParams& p, hipStream_t s, hipEvent_t ev
       else if (xf == 1) go(k1, nt);
       else go(k0, nt);
     };
+    auto by_xf_w = [&](auto k0, auto k1, auto k2) {
+      if (xf == 2) launch_over_rows_w(k2, p, s);
+      else if (xf == 1) launch_over_rows_w(k1, p, s);
+      else launch_over_rows_w(k0, p, s);
+    };
     if (p.dtype == DRIFT_BF16) {
       if (wide) by_xf(score_rows_exact<uint16_t, 256, U, 0>, score_rows_exact<uint16_t, 256, U, 1>,
                       score_rows_exact<uint16_t, 256, U, 2>, 256);
-      else by_xf(score_rows_exact<uint16_t, 128, U, 0>, score_rows_exact<uint16_t, 128, U, 1>,
-                 score_rows_exact<uint16_t, 128, U, 2>, 128);
+      else by_xf_w(score_rows_exact_w<uint16_t, U, 0>, score_rows_exact_w<uint16_t, U, 1>,
+                   score_rows_exact_w<uint16_t, U, 2>);
     } else {
       if (wide) by_xf(score_rows_exact<float, 256, U, 0>, score_rows_exact<float, 256, U, 1>,
                       score_rows_exact<float, 256, U, 2>, 256);
-      else by_xf(score_rows_exact<float, 128, U, 0>, score_rows_exact<float, 128, U, 1>,
-                 score_rows_exact<float, 128, U, 2>, 128);
+      else by_xf_w(score_rows_exact_w<float, U, 0>, score_rows_exact_w<float, U, 1>,
+                   score_rows_exact_w<float, U, 2>);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
