@@ -178,3 +178,44 @@ def test_batch_beyond_one_dispatch():
     got = g.index_select(0, idx).cpu().numpy().astype(np.float64)
     assert np.abs(got - want).max() <= 2e-5
     torch.cuda.empty_cache()
+
+
+def test_exact_batch_beyond_one_dispatch():
+    """The exact reduction on short rows runs one wave per row, four rows per block, so one
+    dispatch covers 67108860 rows; a larger batch takes consecutive launches. Sampled rows
+    and the rows on both sides of the boundary against the oracle, and the boundary rows,
+    the last rows and a few random rows bitwise equal to the same rows scored as a batch of
+    their own (the exact result does not depend on the batch or the launch a row falls in)."""
+    B = B_()
+    split = 67108860
+    N, V = split + 37, 8
+    print(f"[case] exact fp32 N={N} V={V}: launches split at {split}", flush=True)
+    rng = np.random.default_rng(43)
+    ids = rng.integers(0, V, N).astype(np.int32)
+    act = (rng.random(N) < 0.9).astype(np.uint8)
+    gen = torch.Generator(device="cuda").manual_seed(43)
+    ro = torch.randn((N, V), generator=gen, device="cuda") * 2.0
+    tr = ro + torch.randn((N, V), generator=gen, device="cuda") * 1e-3
+    ids_d = torch.as_tensor(ids, device="cuda")
+    act_d = torch.as_tensor(act, device="cuda")
+    t, r, d, a, _ = B.selected_logprob(tr, ro, ids_d, None, act_d, "right", N, 1, check=True,
+                                       reduction="exact")
+    assert torch.equal(a, act_d)
+    near = np.concatenate([np.arange(split - 5, split + 5), np.arange(N - 4, N)])
+    rows = np.unique(np.concatenate([near, rng.integers(0, N, 300)]))
+    rows = rows[act[rows] == 1]
+    idx = torch.as_tensor(rows, device="cuda")
+    ot, orr, od = oracle.score_rows(tr.index_select(0, idx).cpu().numpy(),
+                                    ro.index_select(0, idx).cpu().numpy(), "f32", ids[rows])
+    for g, w in ((t, ot), (r, orr), (d, od)):
+        err = np.abs(g.index_select(0, idx).cpu().numpy().astype(np.float64) - w)
+        assert float(err.max()) <= LOGP_TOL
+    n = len(rows)
+    t2, r2, d2, a2, _ = B.selected_logprob(tr.index_select(0, idx), ro.index_select(0, idx),
+                                           ids_d.index_select(0, idx), None,
+                                           act_d.index_select(0, idx), "right", n, 1,
+                                           check=True, reduction="exact")
+    for g, w in ((t, t2), (r, r2), (d, d2)):
+        assert torch.equal(g.index_select(0, idx).view(torch.int32), w.view(torch.int32))
+    del tr, ro
+    torch.cuda.empty_cache()
