@@ -105,3 +105,11 @@ def test_pipelined_steps_match_run():
         prev = cur
     assert step.collect(prev) == B.DRIFT_OK
     _same(step.stats_of(prev).as_dict(), want)
+    with pytest.raises(RuntimeError):   # collected already
+        step.collect(prev)
+    a, b = step.submit(), step.submit()
+    with pytest.raises(RuntimeError):   # a third outstanding step in two slots
+        step.submit()
+    for k in (a, b):
+        assert step.collect(k) == B.DRIFT_OK
+        _same(step.stats_of(k).as_dict(), want)

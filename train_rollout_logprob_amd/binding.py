@@ -598,7 +598,9 @@ class ScoringStep:
     and returns its status, the statistics then in `stats_of(slot)`. A loop that submits
     step i + 1 before collecting step i keeps the GPU busy while the host reads and checks
     the previous step. The per-row outputs are shared by all steps (each step overwrites
-    them); the statistics are per slot."""
+    them); the statistics are per slot. At most `depth` steps are outstanding: `submit`
+    raises when the next slot has not been collected, and `collect` raises for a slot with
+    no outstanding step."""
 
     def __init__(self, train, rollout, ids, attention=None, action=None, layout="right",
                  batch=0, seq_len=0, cu_seqlens=None, eps_low=0.2, eps_high=0.2,
@@ -630,6 +632,7 @@ class ScoringStep:
             self._stream_obj = stream
         self._stream = self._stream_obj.cuda_stream
         self._done = [torch.cuda.Event() for _ in range(depth)]
+        self._pending = [False] * depth
         self._next = 0
         self._args_ref = ctypes.byref(self.args)
         self._stats_ref = ctypes.byref(self.stats)
@@ -654,6 +657,9 @@ class ScoringStep:
         """Launches one step; returns the slot its statistics go to. The slot must have
         been collected (or never used) before it comes round again."""
         k = self._next
+        if self._pending[k]:
+            raise RuntimeError(f"slot {k} still holds an uncollected step (depth "
+                               f"{len(self._slots)})")
         self._next = (k + 1) % len(self._slots)
         st = lib.drift_selected_logprob(*self._lp_args)
         if st != DRIFT_OK:
@@ -665,11 +671,15 @@ class ScoringStep:
         if st != DRIFT_OK:
             raise DriftError(st, "drift_diagnostics_async")
         self._done[k].record(self._stream_obj)
+        self._pending[k] = True
         return k
 
     def collect(self, slot) -> int:
         """Waits for the step whose statistics go to `slot`; returns their status."""
+        if not self._pending[slot]:
+            raise RuntimeError(f"slot {slot} has no outstanding step")
         self._done[slot].synchronize()
+        self._pending[slot] = False
         return self._slots[slot].status
 
     def stats_of(self, slot):
