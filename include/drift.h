@@ -390,7 +390,8 @@ int drift_segment_diagnostics(const float* dlogp, const uint8_t* active, int64_t
  *               active[r] != 0 in ascending order; entries from n on are not written
  *   n_dev       int64 [1] device: receives n
  *   ws          drift_workspace_size(DRIFT_OP_ACTIVE_ROWS, N, 1, 0, DRIFT_F32) bytes
- *               (per-tile counts), 256-byte aligned
+ *               (per-tile counts of 4096 rows, and above 1024 tiles the tiles' offsets),
+ *               256-byte aligned
  * Integer work only: the result is exact and independent of scheduling. Asynchronous;
  * returns EINVAL / EWORKSPACE for bad arguments before any launch, EHIP if a launch
  * fails. */

@@ -1,6 +1,8 @@
 """GPU parity of drift_active_rows (the ascending active-row list) against the oracle's
 list, bit-exact: ragged and tile-multiple sizes, empty and full masks, non-0/1 bytes, the
-entries past n left untouched, and the list of a scored batch's `active` output."""
+entries past n left untouched, batches on both sides of 1024 tiles of 4096 rows (where the
+tiles' offsets move from the scatter blocks to a scan launch), and the list of a scored
+batch's `active` output."""
 import numpy as np
 import pytest
 import torch
@@ -18,7 +20,8 @@ def _need_gpu():
         pytest.skip("needs a GPU")
 
 
-@pytest.mark.parametrize("N", [0, 1, 4095, 4096, 4097, 100003, 270336])
+@pytest.mark.parametrize("N", [0, 1, 4095, 4096, 4097, 100003, 270336,
+                               4096 * 1024, 4096 * 1024 + 1, 16777216 + 4099])
 @pytest.mark.parametrize("p", [0.0, 0.01, 0.5, 1.0])
 def test_active_rows_match_the_oracle(N, p):
     from train_rollout_logprob_amd import binding as B

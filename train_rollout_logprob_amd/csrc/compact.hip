@@ -3,13 +3,16 @@
 // active response/action tokens enter the comparison). Callers use the list to gather or
 // scatter per-token results of the active rows only.
 //
-// Two launches over tiles of kCompactTile rows:
+// Launches over tiles of kCompactTile rows:
 //   compact_count    one block per tile: the tile's active count;
-//   compact_scatter  one block per tile: adds the counts of the tiles before it (integer,
-//                    exact), then walks its tile in 16 rounds of 256 consecutive rows; a
-//                    round ranks its active rows with wave ballots and a 4-entry LDS
-//                    prefix, so rows are written in ascending order. The last tile also
-//                    writes n.
+//   compact_scan     above kCompactDirectTiles tiles only: one block forms every tile's
+//                    offset (the exclusive prefix of the counts, int64);
+//   compact_scatter  one block per tile: takes its offset from compact_scan, or with
+//                    fewer tiles adds the counts of the tiles before it itself (at most
+//                    4 loads per thread; integer, exact), then walks its tile in 16 rounds
+//                    of 256 consecutive rows; a round ranks its active rows with wave
+//                    ballots and a 4-entry LDS prefix, so rows are written in ascending
+//                    order. The last tile also writes n.
 #include "common.h"
 
 namespace drift {
@@ -19,6 +22,8 @@ constexpr int kCompactThreads = 256;
 constexpr int kCompactRounds = 16;
 constexpr int kCompactTile = kCompactThreads * kCompactRounds;
 constexpr int kCompactWaves = kCompactThreads / 64;
+constexpr int64_t kCompactDirectTiles = 1024;  // in-block prefix up to this many tiles
+constexpr int kScanThreads = 1024;
 
 __global__ void __launch_bounds__(kCompactThreads) compact_count(const uint8_t* __restrict__ active,
                                                                  int64_t N,
@@ -44,9 +49,39 @@ __global__ void __launch_bounds__(kCompactThreads) compact_count(const uint8_t* 
   }
 }
 
+// One block: offs[g] = counts[0] + ... + counts[g - 1]. Thread t owns the contiguous run
+// of tiles [t·per, (t+1)·per): it sums the run, a block scan of the run sums gives the
+// run's first offset, and the thread walks the run again writing offsets.
+__global__ void __launch_bounds__(kScanThreads) compact_scan(const int32_t* __restrict__ counts,
+                                                             int64_t G,
+                                                             long long* __restrict__ offs) {
+  __shared__ long long s_w[kScanThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t per = (G + kScanThreads - 1) / kScanThreads;
+  const int64_t lo = (int64_t)tid * per < G ? (int64_t)tid * per : G;
+  const int64_t hi = lo + per < G ? lo + per : G;
+  long long sum = 0;
+  for (int64_t g = lo; g < hi; ++g) sum += counts[g];
+  long long x = sum;  // inclusive scan over the wave's lanes
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const long long y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_w[wave] = x;
+  __syncthreads();
+  long long run = x - sum;
+  for (int w = 0; w < wave; ++w) run += s_w[w];
+  for (int64_t g = lo; g < hi; ++g) {
+    offs[g] = run;
+    run += counts[g];
+  }
+}
+
 __global__ void __launch_bounds__(kCompactThreads) compact_scatter(
     const uint8_t* __restrict__ active, int64_t N, const int32_t* __restrict__ counts,
-    int32_t* __restrict__ rows, int64_t* __restrict__ n_out) {
+    const long long* __restrict__ offs, int32_t* __restrict__ rows,
+    int64_t* __restrict__ n_out) {
   __shared__ long long s_part[kCompactWaves];
   __shared__ int s_w[kCompactWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -58,14 +93,18 @@ __global__ void __launch_bounds__(kCompactThreads) compact_scatter(
     f[j] = r < N ? active[r] : (uint8_t)0;
   }
   // rows of the tiles before this one
-  long long part = 0;
-  for (int g = tid; g < (int)blockIdx.x; g += kCompactThreads) part += counts[g];
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
-  if (lane == 0) s_part[wave] = part;
-  __syncthreads();
   long long off = 0;
-  for (int w = 0; w < kCompactWaves; ++w) off += s_part[w];
+  if (offs) {
+    off = offs[blockIdx.x];
+  } else {
+    long long part = 0;
+    for (int g = tid; g < (int)blockIdx.x; g += kCompactThreads) part += counts[g];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
+    if (lane == 0) s_part[wave] = part;
+    __syncthreads();
+    for (int w = 0; w < kCompactWaves; ++w) off += s_part[w];
+  }
   const unsigned long long below = (1ull << lane) - 1ull;
 #pragma unroll
   for (int j = 0; j < kCompactRounds; ++j) {
@@ -93,16 +132,27 @@ int64_t compact_tiles(int64_t N) {
   return g > 0 ? g : 1;
 }
 
-size_t compact_ws_bytes(int64_t N) { return align_up((size_t)compact_tiles(N) * 4, 256); }
+// per-tile counts (int32), then above kCompactDirectTiles tiles the offsets (int64)
+size_t compact_ws_bytes(int64_t N) {
+  const int64_t G = compact_tiles(N);
+  return align_up((size_t)G * 4, 256) + (G > kCompactDirectTiles ? align_up((size_t)G * 8, 256)
+                                                                  : 0);
+}
 
 hipError_t launch_compact(const uint8_t* active, int64_t N, int32_t* rows, int64_t* n_out,
                           char* ws, hipStream_t s) {
   const int64_t G = compact_tiles(N);
   int32_t* counts = (int32_t*)ws;
+  long long* offs = nullptr;
   hipLaunchKernelGGL(compact_count, dim3((unsigned)G), dim3(kCompactThreads), 0, s, active, N,
                      counts);
+  if (G > kCompactDirectTiles) {
+    offs = (long long*)(ws + align_up((size_t)G * 4, 256));
+    hipLaunchKernelGGL(compact_scan, dim3(1), dim3(kScanThreads), 0, s, (const int32_t*)counts,
+                       G, offs);
+  }
   hipLaunchKernelGGL(compact_scatter, dim3((unsigned)G), dim3(kCompactThreads), 0, s, active, N,
-                     (const int32_t*)counts, rows, n_out);
+                     (const int32_t*)counts, (const long long*)offs, rows, n_out);
   return hipGetLastError();
 }
 
