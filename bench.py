@@ -3,8 +3,9 @@
 One step = drift_selected_logprob (classification, paired one-pass log-softmax gather of
 both sides, drift) + drift_diagnostics_async (sums, counts, exact nearest-rank select; the
 statistics written into pinned host memory) over one batch, inputs resident in HBM before
-timing starts. Steps run two deep: the host waits for step i and checks its statistics
-while step i + 1 runs; the last step is collected before the clock stops.
+timing starts. Steps run two deep: a step's diagnostics run on a second stream beside the
+next step's scoring pass, and the host waits for step i and checks its statistics while
+step i + 1 runs; the last step is collected before the clock stops.
 
 The main line is the large-batch workload, the largest that fits one GPU: bf16 logits,
 V=151936, B=32, L=4096 (prompt 1024 + response U[1024,3072]), right padding, about 40 GB
@@ -551,11 +552,13 @@ def training_leg(case, ids, att, act, cu, steps=10, warmup=2):
 
 def time_steps(runner, steps, warmup, name):
     """Runs `warmup` untimed and `steps` timed steps of a ScoringStep (scoring kernel
-    bracketed by events on its launch stream, then drift_diagnostics_async), pipelined two
-    deep: step i + 1 is launched before the host waits for step i and checks its
-    statistics (status and active count), so the GPU does not idle while the host reads
-    them; the last step is collected before the clock stops. Returns the sorted kernel
-    times (ms), the wall time of the timed steps (s) and the last step's statistics."""
+    bracketed by events on its launch stream, then drift_diagnostics_async on the step's
+    diagnostics stream), pipelined two deep: step i + 1 is launched before the host waits
+    for step i and checks its statistics (status and active count), so the GPU does not
+    idle while the host reads them and step i's diagnostics overlap step i + 1's scoring;
+    the last step is collected and the device synchronized before the clock stops.
+    Returns the sorted kernel times (ms), the wall time of the timed steps (s) and the
+    last step's statistics."""
     import torch
 
     from train_rollout_logprob_amd import binding as B

@@ -1,8 +1,8 @@
 """drift_diagnostics_async (no synchronization; statistics written by the device to device
 memory or pinned host memory) against drift_diagnostics on the same inputs, through the C
 ABI: bitwise the same statistics on both selection paths, for both kinds of output memory,
-with a logprob status folded in; and the pipelined ScoringStep (submit / collect) against
-its synchronizing run()."""
+with a logprob status folded in; and the pipelined ScoringStep (submit / collect, the
+diagnostics on a stream of their own) against its synchronizing run()."""
 import numpy as np
 import pytest
 import torch
@@ -24,6 +24,10 @@ def _same(got, want):
             assert np.float64(g).tobytes() == np.float64(w).tobytes(), (k, g, w)
         else:
             assert g == w, (k, g, w)
+
+
+def _bits(t):
+    return t.view(torch.int32) if t.dtype == torch.float32 else t
 
 
 def _batch(n, seed, tail):
@@ -113,3 +117,45 @@ def test_pipelined_steps_match_run():
     for k in (a, b):
         assert step.collect(k) == B.DRIFT_OK
         _same(step.stats_of(k).as_dict(), want)
+
+
+@pytest.mark.parametrize("spec", [dict(name="qwen8b", B=3, L=96),
+                                  dict(name="large", B=4, L=20000, V=8, prompt=4)],
+                         ids=["qwen8b_small", "large_V8_80000_rows"])
+def test_pipelined_steps_on_changing_inputs(spec):
+    """Each step scores new logits (written in place on the step's stream after the previous
+    submit) while the previous step's diagnostics run on the diagnostics stream: every
+    slot's statistics and per-row outputs are bitwise those of a synchronizing run() on the
+    same logits; once with the single-block selection and once above 65536 rows."""
+    from helpers import make_small, device_inputs
+    from train_rollout_logprob_amd import binding as B
+    print(f"[case] pipelined changing inputs {spec}", flush=True)
+    case = make_small(spec)
+    ids, att, act, cu = device_inputs(case)
+    train = case.train.clone()
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    variants = [(case.train.float() + torch.randn(train.shape, generator=gen, device="cuda")
+                 * (0.02 * k)).to(train.dtype) for k in range(5)]
+    mk = lambda: B.ScoringStep(train, case.rollout, ids, att, act, case.layout, case.B, case.L,
+                               cu, case.eps_low, case.eps_high)
+    ref, step = mk(), mk()
+    want = []
+    for v in variants:
+        train.copy_(v)
+        assert ref.run() == B.DRIFT_OK
+        want.append((ref.stats.as_dict(), [x.clone() for x in ref.out]))
+    assert len({w[0]["max_abs_dlogp"] for w in want}) == len(variants)  # the steps differ
+    prev = None
+    for k, v in enumerate(variants):
+        train.copy_(v)          # ordered after the previous step's scoring on this stream
+        cur = step.submit()
+        if prev is not None:
+            assert step.collect(prev[0]) == B.DRIFT_OK
+            _same(step.stats_of(prev[0]).as_dict(), want[prev[1]][0])
+            for g, w in zip(step.out_of(prev[0]), want[prev[1]][1]):
+                assert torch.equal(_bits(g), _bits(w))
+        prev = (cur, k)
+    assert step.collect(prev[0]) == B.DRIFT_OK
+    _same(step.stats_of(prev[0]).as_dict(), want[prev[1]][0])
+    if case.N > 65536:
+        assert step.N > 65536

@@ -593,37 +593,46 @@ class ScoringStep:
     the statistics) is done once here, so a call to `run` is two C calls.
 
     `run` waits for each step's statistics. `submit` / `collect` pipeline the steps instead:
-    `submit` launches a step with drift_diagnostics_async, whose statistics land in one of
-    `depth` pinned host slots, and returns the slot; `collect(slot)` waits for that step
-    and returns its status, the statistics then in `stats_of(slot)`. A loop that submits
-    step i + 1 before collecting step i keeps the GPU busy while the host reads and checks
-    the previous step. The per-row outputs are shared by all steps (each step overwrites
-    them); the statistics are per slot. At most `depth` steps are outstanding: `submit`
-    raises when the next slot has not been collected, and `collect` raises for a slot with
-    no outstanding step."""
+    `submit` scores a step into one of `depth` slots (per-row outputs and a logprob
+    workspace per slot) on the step's stream, then launches drift_diagnostics_async on a
+    second stream once the scoring is done, with the statistics landing in the slot's
+    pinned host record, and returns the slot. `collect(slot)` waits for that step's
+    diagnostics and returns its status, the statistics then in `stats_of(slot)` and the
+    per-row outputs in `out_of(slot)`. A loop that submits step i + 1 before collecting
+    step i keeps the GPU busy while the host reads and checks the previous step, and the
+    diagnostics of step i run beside the scoring of step i + 1 instead of between the two
+    scoring passes. At most `depth` steps are outstanding: `submit` raises when the next
+    slot has not been collected (collecting waits for the slot's diagnostics, so the slot's
+    buffers are free again), and `collect` raises for a slot with no outstanding step.
+    `run` uses slot 0 and raises while steps are outstanding; `out` and `ws` are slot 0's
+    buffers."""
 
     def __init__(self, train, rollout, ids, attention=None, action=None, layout="right",
                  batch=0, seq_len=0, cu_seqlens=None, eps_low=0.2, eps_high=0.2,
                  stream=None, vocab_real=None, transforms=(None, None), depth=2):
+        if depth < 1:
+            raise ValueError("depth >= 1")
         dev = train.device
         self.args = make_args(train, rollout, ids, attention, action, layout, batch, seq_len,
                               cu_seqlens, vocab_real=vocab_real, transforms=transforms)
         self.N = int(self.args.num_rows)
         self.eps = (float(eps_low), float(eps_high))
-        self.ws = workspace(DRIFT_OP_SELECTED_LOGPROB, self.N, self.args.vocab,
-                            self.args.logits_dtype, dev)
+        self._ws = [workspace(DRIFT_OP_SELECTED_LOGPROB, self.N, self.args.vocab,
+                              self.args.logits_dtype, dev) for _ in range(depth)]
         self.dws = workspace(DRIFT_OP_DIAGNOSTICS, self.N, 1, DRIFT_F32, dev)
-        self.out = (torch.empty(self.N, dtype=torch.float32, device=dev),
-                    torch.empty(self.N, dtype=torch.float32, device=dev),
-                    torch.empty(self.N, dtype=torch.float32, device=dev),
-                    torch.empty(self.N, dtype=torch.uint8, device=dev))
+        self._out = [(torch.empty(self.N, dtype=torch.float32, device=dev),
+                      torch.empty(self.N, dtype=torch.float32, device=dev),
+                      torch.empty(self.N, dtype=torch.float32, device=dev),
+                      torch.empty(self.N, dtype=torch.uint8, device=dev))
+                     for _ in range(depth)]
+        self.ws, self.out = self._ws[0], self._out[0]
         sz = ctypes.sizeof(drift_stats)
         self._pinned = torch.empty(sz * (1 + depth), dtype=torch.uint8, pin_memory=True)
         self.stats = drift_stats.from_address(self._pinned.data_ptr())
         self._slot_ptr = [self._pinned.data_ptr() + sz * (1 + k) for k in range(depth)]
         self._slots = [drift_stats.from_address(q) for q in self._slot_ptr]
-        # the stream every call of this step launches into, fixed here (None = the stream
-        # current now), and the same stream object for the completion events of `submit`
+        # the stream every scoring call of this step launches into, fixed here (None = the
+        # stream current now); submitted steps' diagnostics go to a stream of their own
         if stream is None:
             self._stream_obj = torch.cuda.current_stream()
         elif isinstance(stream, int):
@@ -631,14 +640,21 @@ class ScoringStep:
         else:
             self._stream_obj = stream
         self._stream = self._stream_obj.cuda_stream
+        self._diag_obj = torch.cuda.Stream(device=dev)
+        self._diag = self._diag_obj.cuda_stream
+        self._scored = [torch.cuda.Event() for _ in range(depth)]
         self._done = [torch.cuda.Event() for _ in range(depth)]
         self._pending = [False] * depth
         self._next = 0
         self._args_ref = ctypes.byref(self.args)
         self._stats_ref = ctypes.byref(self.stats)
-        t, r, d, a = (x.data_ptr() for x in self.out)
-        self._lp_args = (self._args_ref, t, r, d, a, self.ws.data_ptr(), self.ws.numel(),
-                         self._stream)
+        self._lp = []
+        for k in range(depth):
+            t, r, d, a = (x.data_ptr() for x in self._out[k])
+            self._lp.append((self._args_ref, t, r, d, a, self._ws[k].data_ptr(),
+                             self._ws[k].numel(), self._stream))
+        self._lp_args = self._lp[0]
+        d, a = self._lp[0][3], self._lp[0][4]
         self._dg_args = (d, a, self.N, self.eps[0], self.eps[1], self.ws.data_ptr(),
                          self._stats_ref, self.dws.data_ptr(), self.dws.numel(), self._stream)
 
@@ -648,34 +664,37 @@ class ScoringStep:
         self.args.prof_events[1] = ev1
 
     def run(self) -> int:
+        if any(self._pending):
+            raise RuntimeError("run() with submitted steps not yet collected")
         st = lib.drift_selected_logprob(*self._lp_args)
         if st != DRIFT_OK:
             raise DriftError(st, "drift_selected_logprob")
         return lib.drift_diagnostics(*self._dg_args)
 
     def submit(self) -> int:
-        """Launches one step; returns the slot its statistics go to. The slot must have
-        been collected (or never used) before it comes round again."""
+        """Launches one step; returns its slot."""
         k = self._next
         if self._pending[k]:
             raise RuntimeError(f"slot {k} still holds an uncollected step (depth "
                                f"{len(self._slots)})")
         self._next = (k + 1) % len(self._slots)
-        st = lib.drift_selected_logprob(*self._lp_args)
+        lp = self._lp[k]
+        st = lib.drift_selected_logprob(*lp)
         if st != DRIFT_OK:
             raise DriftError(st, "drift_selected_logprob")
-        d, a = self._dg_args[0], self._dg_args[1]
-        st = lib.drift_diagnostics_async(d, a, self.N, self.eps[0], self.eps[1],
-                                         self.ws.data_ptr(), self._slot_ptr[k],
-                                         self.dws.data_ptr(), self.dws.numel(), self._stream)
+        self._scored[k].record(self._stream_obj)
+        self._diag_obj.wait_event(self._scored[k])
+        st = lib.drift_diagnostics_async(lp[3], lp[4], self.N, self.eps[0], self.eps[1],
+                                         lp[5], self._slot_ptr[k], self.dws.data_ptr(),
+                                         self.dws.numel(), self._diag)
         if st != DRIFT_OK:
             raise DriftError(st, "drift_diagnostics_async")
-        self._done[k].record(self._stream_obj)
+        self._done[k].record(self._diag_obj)
         self._pending[k] = True
         return k
 
     def collect(self, slot) -> int:
-        """Waits for the step whose statistics go to `slot`; returns their status."""
+        """Waits for the step of `slot` (its diagnostics included); returns their status."""
         if not self._pending[slot]:
             raise RuntimeError(f"slot {slot} has no outstanding step")
         self._done[slot].synchronize()
@@ -684,6 +703,14 @@ class ScoringStep:
 
     def stats_of(self, slot):
         return self._slots[slot]
+
+    def out_of(self, slot):
+        """(train_logp, rollout_logp, dlogp, active) of the step last submitted to `slot`."""
+        return self._out[slot]
+
+    def ws_of(self, slot):
+        """The logprob workspace (device status) of the step last submitted to `slot`."""
+        return self._ws[slot]
 
 
 class ScoringGraph:
