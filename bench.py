@@ -25,6 +25,7 @@ and `transforms` (temperature and soft-cap chains) on the Qwen3-8B-shaped batch;
 the fused LM-head selected logprob.
 """
 import argparse
+import collections
 import ctypes
 import json
 import os
@@ -580,17 +581,20 @@ def time_steps(runner, steps, warmup, name):
             raise RuntimeError(f"{name}: status {B.STATUS_NAMES[st]}")
         n_active.append(runner.stats_of(slot).n_active)
 
+    depth = runner.depth
+
     def run(lo, hi):
-        prev = None
+        q = collections.deque()
+        last = None
         for i in range(lo, hi):
+            if len(q) == depth:  # every slot holds a step: wait for the oldest
+                check(q.popleft())
             runner.set_events(*handles[i])
-            cur = runner.submit()
-            if prev is not None:
-                check(prev)
-            prev = cur
-        if prev is not None:
-            check(prev)
-        return prev
+            last = runner.submit()
+            q.append(last)
+        while q:
+            check(q.popleft())
+        return last
 
     run(0, warmup)
     torch.cuda.synchronize()

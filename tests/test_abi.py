@@ -321,6 +321,15 @@ def test_active_rows_host_checks():
     assert f(ok, 5000, ctypes.c_void_p((1 << 20) + 2), ok, ws, need, None) == B.DRIFT_EINVAL
     assert f(ok, 5000, ok, ok, ws, need - 1, None) == B.DRIFT_EWORKSPACE
     assert f(ok, 5000, ok, ok, ws + 8, need, None) == B.DRIFT_EWORKSPACE
+    # up to 1024 tiles: counts only; beyond, int64 offsets per tile after the counts
+    size = lambda n: B.drift_workspace_size(B.DRIFT_OP_ACTIVE_ROWS, n, 1, 0, B.DRIFT_F32)
+    assert size(4096 * 1024) == 4096
+    assert size(4096 * 1024 + 1) == 4352 + 8448  # 1025 counts, then 1025 offsets
+    big = 2 ** 31 - 1
+    tiles = -(-big // 4096)
+    assert size(big) == -(-4 * tiles // 256) * 256 + -(-8 * tiles // 256) * 256
+    assert f(ok, 4096 * 1024 + 1, ok, ok, ws, size(4096 * 1024 + 1) - 1, None) == \
+        B.DRIFT_EWORKSPACE
 
 
 def test_diagnostics_async_host_checks():

@@ -616,6 +616,7 @@ class ScoringStep:
         self.args = make_args(train, rollout, ids, attention, action, layout, batch, seq_len,
                               cu_seqlens, vocab_real=vocab_real, transforms=transforms)
         self.N = int(self.args.num_rows)
+        self.depth = depth
         self.eps = (float(eps_low), float(eps_high))
         self._ws = [workspace(DRIFT_OP_SELECTED_LOGPROB, self.N, self.args.vocab,
                               self.args.logits_dtype, dev) for _ in range(depth)]
