@@ -119,17 +119,19 @@ def test_pipelined_steps_match_run():
         _same(step.stats_of(k).as_dict(), want)
 
 
+@pytest.mark.parametrize("overlap", [True, False], ids=["two_streams", "one_stream"])
 @pytest.mark.parametrize("spec", [dict(name="qwen8b", B=3, L=96),
                                   dict(name="large", B=4, L=20000, V=8, prompt=4)],
                          ids=["qwen8b_small", "large_V8_80000_rows"])
-def test_pipelined_steps_on_changing_inputs(spec):
+def test_pipelined_steps_on_changing_inputs(spec, overlap):
     """Each step scores new logits (written in place on the step's stream after the previous
-    submit) while the previous step's diagnostics run on the diagnostics stream: every
-    slot's statistics and per-row outputs are bitwise those of a synchronizing run() on the
-    same logits; once with the single-block selection and once above 65536 rows."""
+    submit) while the previous step's diagnostics run on the diagnostics stream (or after
+    it on the step's own stream): every slot's statistics and per-row outputs are bitwise
+    those of a synchronizing run() on the same logits; once with the single-block selection
+    and once above 65536 rows."""
     from helpers import make_small, device_inputs
     from train_rollout_logprob_amd import binding as B
-    print(f"[case] pipelined changing inputs {spec}", flush=True)
+    print(f"[case] pipelined changing inputs {spec} overlap={overlap}", flush=True)
     case = make_small(spec)
     ids, att, act, cu = device_inputs(case)
     train = case.train.clone()
@@ -137,8 +139,9 @@ def test_pipelined_steps_on_changing_inputs(spec):
     variants = [(case.train.float() + torch.randn(train.shape, generator=gen, device="cuda")
                  * (0.02 * k)).to(train.dtype) for k in range(5)]
     mk = lambda: B.ScoringStep(train, case.rollout, ids, att, act, case.layout, case.B, case.L,
-                               cu, case.eps_low, case.eps_high)
+                               cu, case.eps_low, case.eps_high, overlap=overlap)
     ref, step = mk(), mk()
+    assert step.overlap == overlap
     want = []
     for v in variants:
         train.copy_(v)
