@@ -140,10 +140,8 @@ class OraclePool:
         self._mm.flush()
         total = self._shape[0][1]
         ids = np.asarray(ids, dtype=np.int64)
-        # about four ranges per worker, so that uneven row costs even out
-        step = max(1, -(-rows // (4 * self.workers)))
-        tasks = [(self._path, total, cols, dtype, lo, min(rows, lo + step), ids[lo:lo + step],
-                  vocab_real, transforms) for lo in range(0, rows, step)]
+        tasks = [(self._path, total, cols, dtype, lo, hi, ids[lo:hi], vocab_real, transforms)
+                 for lo, hi in self._ranges(rows)]
         t0 = time.perf_counter()
         res = self._pool.map(_score_range, tasks, chunksize=1)
         wall = time.perf_counter() - t0
