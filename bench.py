@@ -721,8 +721,8 @@ def main():
     if not args.legs <= set(LEGS):
         ap.error(f"--legs: unknown leg(s) {sorted(args.legs - set(LEGS))}")
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build has "
-              f"no multi-GPU path; the per-row work shards by rows with no exchange.",
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the library "
+              f"has no multi-GPU path; the per-row work shards by rows with no exchange.",
               file=sys.stderr)
         sys.exit(2)
 
