@@ -50,8 +50,10 @@ extern "C" {
 #define DRIFT_EMASK      -5  /* mask byte not 0/1, action on a padded row, attention not
                                 contiguous on the declared padding side, bad cu_seqlens  */
 #define DRIFT_ENOACTIVE  -6  /* diagnostics over zero active rows                        */
-#define DRIFT_ENONFINITE -7  /* NaN/+inf logit in an active row, selected logit -inf,
-                                |logit| >= 2^127, or a non-finite active dlogp           */
+#define DRIFT_ENONFINITE -7  /* NaN/+inf logit in an active row, selected logit -inf, a
+                                row maximum (after the chain) beyond |z| ~ 7.4e8 (the
+                                exponent range, 2^30 / log2 e; the exact mode: 1.16e7),
+                                or a non-finite active dlogp; such rows' outputs are NaN */
 #define DRIFT_EHIP       -8  /* a HIP runtime call failed                                */
 
 /* ---- element types ---------------------------------------------------------------- */

@@ -219,3 +219,108 @@ def test_exact_batch_beyond_one_dispatch():
         assert torch.equal(g.index_select(0, idx).view(torch.int32), w.view(torch.int32))
     del tr, ro
     torch.cuda.empty_cache()
+
+
+def _bits16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_tree_mode_exponent_range(dtype):
+    """The tree mode's partials keep their exponent reference within |k| < 2^30, i.e. a
+    row maximum below about 7.4e8 in magnitude: rows inside match the oracle (to the fp32
+    rounding of the output), rows beyond fail closed with NaN outputs on either sign, and
+    logits far below the row maximum add nothing wherever they sit in the row (a whole
+    leading wave group of them included)."""
+    B = B_()
+    V = 1024
+    x = torch.zeros((6, V), device="cuda", dtype=torch.float32)
+    x[0, 100] = 5.0e8       # inside: logp of column 0 is about -5e8
+    x[1, 100] = 1.0e9       # beyond: fails closed
+    x[2, :] = -5.0e8        # inside, uniform: -ln V
+    x[3, :] = -1.0e9        # beyond, every logit: fails closed
+    x[4, :600] = -1.0e30    # far below, leading: like absent columns
+    x[5, 600:] = -1.0e30    # far below, trailing
+    x = x.to(dtype)
+    ids_h = np.array([0, 0, 3, 3, 700, 0], np.int32)
+    ids = torch.as_tensor(ids_h, device="cuda")
+    t, r, d, a, ws = B.selected_logprob(x, x, ids, layout="right", batch=6, seq_len=1)
+    st, bad = B.drift_get_status(ws)
+    assert status_name(st) == "ENONFINITE" and bad == 1
+    t_h, d_h = t.cpu().numpy(), d.cpu().numpy()
+    host = x.float().cpu().numpy() if dtype == torch.float32 else _bits16(x)
+    want, _, _ = oracle.score_rows(host, host, "f32" if dtype == torch.float32 else "bf16",
+                                   ids_h)
+    for row in (0, 2, 4, 5):
+        w = np.float32(want[row])
+        assert abs(float(t_h[row]) - float(want[row])) <= float(np.spacing(abs(w))) + 1e-5, row
+        assert d_h[row] == 0.0
+    assert abs(float(t_h[4]) + math.log(V - 600)) <= 1e-5
+    assert abs(float(t_h[5]) + math.log(600)) <= 1e-5
+    for row in (1, 3):
+        assert math.isnan(t_h[row]) and math.isnan(d_h[row]), row
+
+
+def test_lmhead_exponent_range():
+    """The fused head's partials follow the same exponent range: a token whose largest
+    logit is about 6.4e9 fails closed with a NaN logprob, one at about 6.4e8 matches the
+    oracle, the others are unaffected."""
+    B = B_()
+    T, H, V = 8, 64, 512
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    hid = torch.randn((T, H), generator=gen, device="cuda").to(torch.bfloat16)
+    w = (torch.randn((H, V), generator=gen, device="cuda") * 0.1).to(torch.bfloat16)
+    w[:, 5] = 1.0e4
+    hid[0, :] = 1.0e4       # z[0, 5] = 64 x 1e8: beyond
+    hid[1, :] = 1.0e3       # z[1, 5] = 64 x 1e7: inside
+    hid[2, :] = 10.0        # z[2, 5] = 6.4e6, the selected logit: logp about 0, where a
+                            # scale error in the log-sum-exp would show
+    ids_h = np.array([5, 7, 5, 2, 3, 4, 6, 8], np.int32)
+    ids = torch.as_tensor(ids_h, device="cuda")
+    logp, ws = B.lmhead_logprob(hid, w.contiguous(), ids)
+    st, bad = B.drift_get_status(ws)
+    assert status_name(st) == "ENONFINITE" and bad == 0
+    got = logp.cpu().numpy()
+    assert math.isnan(got[0])
+    want = oracle.lmhead_logprob(_bits16(hid), oracle.widen(_bits16(w), "bf16"), ids_h)
+    # the head accumulates each logit in fp32 over H products: allow the classic bound
+    # H 2^-24 sum_k |h_k w_kj| on the largest logit of the row, and the output's rounding
+    habs = np.abs(oracle.widen(_bits16(hid), "bf16")) @ np.abs(oracle.widen(_bits16(w), "bf16"))
+    for t in range(1, T):
+        tol = (float(np.spacing(np.float32(abs(want[t])))) + 2e-5 +
+               2.0 * H * 2.0 ** -24 * float(habs[t].max()))
+        assert abs(float(got[t]) - float(want[t])) <= tol, (t, got[t], want[t])
+    assert abs(float(got[2]) - float(want[2])) <= LOGP_TOL  # its products sum exactly
+
+
+@pytest.mark.parametrize("reduction", ["tree", "exact"])
+def test_large_logits_keep_the_tolerance(reduction):
+    """A constant added to every logit of a row leaves its log-softmax unchanged. The
+    kernels take their exponents with log2(e) rounded to fp32 and convert the log-sum-exp
+    back with that same constant, so rows shifted by up to 1e5 stay within 2e-5 of the
+    oracle, also where the selected logit is the row maximum (logp near 0, where a scale
+    error of the log-sum-exp would show). Under a temperature chain (folded for the
+    log-sum-exp terms, whose way back to natural log undoes the fp32 rounding of the fold's
+    factors) the selected logit takes the chain in fp32, so its rounding, at most
+    2^-23 |z_y| (the reciprocal and the product), adds to the bound."""
+    B = B_()
+    V, N = 4099, 8
+    gen = torch.Generator(device="cuda").manual_seed(9)
+    base = torch.randn((N, V), generator=gen, device="cuda") * 2.0
+    shifts = torch.tensor([1e4, -1e4, 1e5, -1e5, 3e3, -3e3, 5e4, 0.0], device="cuda")
+    x = (base + shifts[:, None]).contiguous()
+    xh = x.cpu().numpy()
+    ids_h = xh.argmax(axis=1).astype(np.int32)
+    ids_h[1::2] = np.random.default_rng(9).integers(0, V, N // 2)
+    ids = torch.as_tensor(ids_h, device="cuda")
+    for chain in (None, [("temperature", 0.7)]):
+        print(f"[case] large logits {reduction} chain={chain}", flush=True)
+        t, r, d, a, ws = B.selected_logprob(x, x, ids, layout="right", batch=N, seq_len=1,
+                                            reduction=reduction, transforms=(chain, chain),
+                                            check=True)
+        want, _, _ = oracle.score_rows(xh, xh, "f32", ids_h, None, (chain, chain))
+        err = np.abs(t.cpu().numpy().astype(np.float64) - want)
+        zy = np.abs(xh[np.arange(N), ids_h].astype(np.float64)) / (0.7 if chain else 1.0)
+        tol = LOGP_TOL + (2.0 ** -23 * zy if chain else 0.0)
+        assert np.all(err <= tol), (chain, err, tol)
+        assert float(d.abs().max()) == 0.0

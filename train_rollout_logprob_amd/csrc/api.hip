@@ -76,6 +76,7 @@ Chain make_chain(const drift_transform& t) {
   c.fald = (double)c.fa * log2e;
   c.fbld = (double)c.fb * log2e;
   c.fdz = nsoft == 1 ? (float)(4.0 * pre * post) : 0.0f;
+  c.lse_scale = c.fbl != 0.0f ? (double)c.fb / (double)c.fbl : 0.693147180559945309417;
   // factors whose folded form leaves the fp32 range keep the step-by-step chain
   const float f[6] = {c.fc, c.fa, c.fb, c.fal, c.fbl, c.fdz};
   for (float x : f)

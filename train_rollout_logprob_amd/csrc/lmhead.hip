@@ -271,16 +271,19 @@ __device__ __forceinline__ void lse_epilogue(const f32x16 (&acc)[TM][TN], const 
     for (int i = 0; i < NZ; ++i) m = fmaxf(m, z[i]);
     Acc p = {-INFINITY, 0.0};
     if (m > -INFINITY) {
-      const float k = ceilf(m * kLog2e);
+      // exponent range as in lse.h: fail closed at or above 2^30, clamp below -2^30
+      const float kn = ceilf(m * kLog2e);
+      const bool big = !(kn < kMaxK);
+      const float k = big ? 0.0f : fmaxf(kn, -kMaxK);
       float s = 0.0f;
-      if (k == INFINITY) {
+      if (big) {
         s = NAN;
       } else {
         const float nk = -k;
 #pragma unroll
         for (int i = 0; i < NZ; ++i) s += __builtin_amdgcn_exp2f(fmaf(z[i], kLog2e, nk));
       }
-      p.k = (k == INFINITY) ? 0.0f : k;
+      p.k = k;
       p.s = (double)s;
     } else if (!(m == -INFINITY)) {
       p.k = 0.0f;
@@ -554,8 +557,9 @@ __global__ void __launch_bounds__(256) lm_merge(const Partial* __restrict__ part
 #pragma unroll
   for (int i = 1; i < kMergeSplit; ++i) R = merge(R, P[i]);
   const float z = zsel[t];
-  logp[t] = (float)((double)z - lse_of(R));
-  if (!lse_ok(R) || !(fabsf(z) < INFINITY)) record_error(h, kErrNonfinite, t);
+  const bool kk = k_ok(R.k);
+  logp[t] = (float)((double)z - (kk ? lse_of(R) : (double)NAN));
+  if (!lse_ok(R) || !kk || !(fabsf(z) < INFINITY)) record_error(h, kErrNonfinite, t);
 }
 
 }  // namespace

@@ -20,9 +20,9 @@
 //     row 5. The element -> lane -> wave mapping depends only on V and the compile-time
 //     block shape, so a row's bits never depend on the batch it is in (the
 //     batch-composition control of the "Attention Debug Matrix" page);
-//   * LSE is exported in the natural-log domain: lse = (k + log2 s) * ln2 in fp64
-//     (Attention knobs row 6, LSE domain); logp and dlogp are formed in fp64 and rounded
-//     once to fp32;
+//   * LSE is exported in the natural-log domain: lse = (k + log2 s) / log2e in fp64, with
+//     the same fp32 log2e the exponents used (lse.h; Attention knobs row 6, LSE domain);
+//     logp and dlogp are formed in fp64 and rounded once to fp32;
 //   * a per-side transform chain (LogProb knobs row 7) with at most one soft-cap step is
 //     folded for the log-sum-exp terms (rowio.h): the exponent is one FMA of the value
 //     g(x), and a soft-capped side, whose logits are bounded by the cap, keeps a fixed k
@@ -65,6 +65,13 @@ template <int VEC> struct Folded {
   __device__ __forceinline__ float base(float nk) const { return ch.fal + nk; }
   __device__ __forceinline__ float expo(int i, float c) const { return fmaf(g[i], ch.fbl, c); }
 };
+
+// Natural-log LSE of a side whose terms 2^(fbl g + fal - k) came from the folded chain c:
+// fa + (log2 of the sum - fal) * fb / fbl (rowio.h).
+template <typename A>
+__device__ __forceinline__ double lse_folded(const A& a, const Chain& c) {
+  return (double)c.fa + (((double)a.k + log2(a.s)) - (double)c.fal) * c.lse_scale;
+}
 
 // exp2 terms of one group in fp32, summed pairwise; with ENT also the first moment of
 // the exponent, sum of 2^a * a over the group (a = x*log2e - k) as a chain of fp32 FMAs in
@@ -121,13 +128,17 @@ __device__ __forceinline__ void push_group(A& a, const G& grp) {
     m = wave_max(m);  // NaN-ignoring; -inf if every logit in the wave's group is -inf/NaN
     const float kn = ceilf(m * kLog2e);
     if (kn > a.k) {
-      if (kn == INFINITY) {
-        a.s = NAN;  // +inf logit, or |x| too large for the fp32 exponent: fail closed
+      if (!(kn < kMaxK)) {
+        a.s = NAN;  // +inf logit, or a maximum beyond the exponent range (lse.h): fail closed
         if constexpr (ENT) a.s2 = NAN;
       } else {
-        if constexpr (ENT) a.s2 = rescale2(a.s2, a.s, a.k, kn);
-        a.s = rescale(a.s, a.k, kn);
-        a.k = kn;
+        // a maximum below -2^30 clamps k (lse.h); the row's final check rejects such a k
+        const float kc = fmaxf(kn, -kMaxK);
+        if (kc > a.k) {
+          if constexpr (ENT) a.s2 = rescale2(a.s2, a.s, a.k, kc);
+          a.s = rescale(a.s, a.k, kc);
+          a.k = kc;
+        }
       }
     }
     if (a.k == -INFINITY) {
@@ -418,18 +429,22 @@ __global__ void __launch_bounds__(NT) score_rows(ScoreParams p) {
       apply_chain<1>(one, p.xf[1]);
       xry = one[0];
     }
-    const double lse_t = lse_of(T_);
-    const double lse_r = lse_of(R_);
+    // a side whose maximum exponent left the range (lse.h) gives NaN outputs; folded
+    // chains take their own way back to natural log (rowio.h)
+    const bool kt = k_ok(T_.k), kr = k_ok(R_.k);
+    const double lse_t = !kt ? (double)NAN : XF == 2 ? lse_folded(T_, p.xf[0]) : lse_of(T_);
+    const double lse_r = !kr ? (double)NAN : XF == 2 ? lse_folded(R_, p.xf[1]) : lse_of(R_);
     p.out_t[r] = (float)((double)xty - lse_t);
     p.out_r[r] = (float)((double)xry - lse_r);
     p.out_d[r] = (float)(((double)xty - (double)xry) - (lse_t - lse_r));
     if (p.lse[0]) p.lse[0][r] = lse_t;
     if (p.lse[1]) p.lse[1][r] = lse_r;
     if constexpr (ENT) {
-      if (p.ent[0]) p.ent[0][r] = (float)entropy_of(T_);
-      if (p.ent[1]) p.ent[1][r] = (float)entropy_of(R_);
+      if (p.ent[0]) p.ent[0][r] = kt ? (float)entropy_of(T_) : NAN;
+      if (p.ent[1]) p.ent[1][r] = kr ? (float)entropy_of(R_) : NAN;
     }
-    const bool ok = lse_ok(T_) && lse_ok(R_) && (xty > -INFINITY) && (xry > -INFINITY);
+    const bool ok = lse_ok(T_) && lse_ok(R_) && kt && kr && (xty > -INFINITY) &&
+                    (xry > -INFINITY);
     if (!ok) record_error(h, kErrNonfinite, r);
   }
 }
@@ -461,8 +476,8 @@ __device__ __forceinline__ AccX from_partial(const drift_lse_partial& q) {
 __device__ __forceinline__ void finish_row_exact(const ScoreParams& p, WsHeader* h, int64_t r,
                                                  const AccX& T_, const AccX& R_, float xty,
                                                  float xry) {
-  const double lse_t = T_.bad ? (double)NAN : accx_log2(T_) * kLn2;
-  const double lse_r = R_.bad ? (double)NAN : accx_log2(R_) * kLn2;
+  const double lse_t = T_.bad ? (double)NAN : accx_log2(T_) * kInvLog2e;
+  const double lse_r = R_.bad ? (double)NAN : accx_log2(R_) * kInvLog2e;
   p.out_t[r] = (float)((double)xty - lse_t);
   p.out_r[r] = (float)((double)xry - lse_r);
   p.out_d[r] = (float)(((double)xty - (double)xry) - (lse_t - lse_r));

@@ -73,6 +73,11 @@ struct Chain {
   // q c tanh(p x / c) is p q (1 - tanh^2) and 1 - tanh^2 = 4 g (1 - g))
   double fald, fbld;
   float fdz;
+  // the log-sum-exp of the folded terms back in natural log: terms 2^(fbl g + fal - k)
+  // sum to 2^L with L = k + log2 s, and LSE(z) = fa + (L - fal) * lse_scale with
+  // lse_scale = fb / fbl in fp64 (ln 2 when fb = 0), which undoes the fp32 rounding of
+  // fbl and fal instead of assuming fbl = fb log2(e) exactly
+  double lse_scale;
 };
 
 // g(x) of the folded chain, in place (kind 1: unchanged). The chain is a kernel argument,
